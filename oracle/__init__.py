@@ -1,0 +1,239 @@
+"""CPU oracle for the 4-bit weight-quantized matmul Y = X·Wᵀ — TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never calls it and shares no code with it: this file has its
+own bf16 decoding, nibble extraction, E2M1/E8M0 decoding and rounding.
+
+Everything here is the plain definition evaluated in fp64 with numpy: weights
+are dequantised exactly (every affine and MXFP4 weight is a dyadic rational with
+few significant bits, so fp64 holds it without rounding) and the contraction is
+a library fp64 matmul.  The GPU reaches the same mathematical result in a
+different summation order and in fp32, which is why parity is a per-element
+tolerance and not bit equality ("优化 kernel 后，要检查请求耗时与数值结果",
+Kapitsa 源码拆解 02：权重、矩阵与 Metal: a different K reduction order is expected
+to change the last bits and is not an error).
+
+Pins (tests/test_oracle.py): the affine worked example, the 36-byte group size,
+the E2M1 value set, exact-rational brute force on tiny shapes, integer-exact
+cases, one-hot columns, row sums and the tolerance checker's self-test.  No
+function here is parity-unpinned.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------
+# Scalar formats
+# ---------------------------------------------------------------------------
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit pattern -> its exact value: the bf16 is the top half of an fp32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(v) -> np.ndarray:
+    """Round fp64 to the nearest bf16 (ties to even), returning bit patterns.
+
+    Used only to state the expected bits of results that are exactly
+    representable (integer-exact cases); the value is rounded directly from
+    fp64 with frexp/ldexp, independent of fp32."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.zeros(v.shape, np.uint16)
+    flat, res = v.reshape(-1), out.reshape(-1)
+    for i, x in enumerate(flat):
+        if x == 0.0:
+            res[i] = 0x8000 if np.signbit(x) else 0
+            continue
+        sign = 0x8000 if x < 0 else 0
+        m, e = np.frexp(abs(x))            # abs(x) = m * 2**e, m in [0.5, 1)
+        q = np.round(np.ldexp(m, 8))       # 8 significant bits, ties to even
+        if q == 256:
+            q, e = 128.0, e + 1
+        exp_field = e - 1 + 127            # value = (q/128) * 2**(e-1)
+        if exp_field >= 255:
+            res[i] = sign | 0x7F80
+        elif exp_field <= 0:                 # subnormal bf16
+            q = np.round(np.ldexp(abs(x), 133))
+            res[i] = sign | int(q)
+        else:
+            res[i] = sign | (exp_field << 7) | (int(q) - 128)
+    return out
+
+
+def e2m1_value(code) -> np.ndarray:
+    """Decode 4-bit E2M1 codes (sign, 2 exponent bits with bias 1, 1 mantissa bit).
+
+    The pages name the format only as "MXFP4: W4, group 32 + E8M0 scale, 4.25
+    bit" (Kimi K3 迁移到 Google TPU 的可行性评估, §2 模型解剖, quantisation row);
+    the element encoding is that of the OCP Microscaling Formats v1.0
+    specification: exponent field 0 is subnormal (value = m/2), otherwise
+    2**(e-1) * (1 + m/2); bit 3 is the sign."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int64)))
+    return sign * mag
+
+
+def e8m0_value(e) -> np.ndarray:
+    """E8M0 shared exponent: 2**(E - 127); E = 255 encodes NaN."""
+    e = np.asarray(e, dtype=np.int64)
+    return np.where(e == 255, np.nan, np.ldexp(1.0, e - 127))
+
+
+# ---------------------------------------------------------------------------
+# Dequantisation
+# ---------------------------------------------------------------------------
+
+
+def affine_codes(codes_u32) -> np.ndarray:
+    """Unsigned 4-bit codes q[N, D] from uint32 words[N, D/8].
+
+    Eight codes share one 32-bit word and are taken out by shift and mask
+    (Kapitsa 源码拆解 02, §"权重怎样存储": wf_extract/wf_codes16); code k of a
+    row is nibble k % 8 of word k // 8, lowest nibble first (reading: the page
+    does not state the nibble order)."""
+    w = np.asarray(codes_u32, dtype=np.uint32)
+    shifts = (4 * np.arange(8, dtype=np.uint32))
+    q = (w[:, :, None] >> shifts[None, None, :]) & np.uint32(0xF)
+    return q.reshape(w.shape[0], w.shape[1] * 8).astype(np.int64)
+
+
+def dequant_affine(codes_u32, scale_bits, bias_bits) -> np.ndarray:
+    """Ŵ[n, k] = scale[n, k//64] * q[n, k] + bias[n, k//64], exactly, in fp64.
+
+    Affine format with groups of 64 codes along D, one bf16 scale and one bf16
+    bias per group (Kapitsa 源码拆解 02, §"权重怎样存储": w ≈ scale×q + bias)."""
+    q = affine_codes(codes_u32).astype(np.float64)
+    n, d = q.shape
+    if d % 64:
+        raise ValueError("D must be a multiple of 64")
+    s = np.repeat(bf16_to_f64(scale_bits).reshape(n, d // 64), 64, axis=1)
+    b = np.repeat(bf16_to_f64(bias_bits).reshape(n, d // 64), 64, axis=1)
+    return s * q + b
+
+
+def mxfp4_codes(codes_u8) -> np.ndarray:
+    """4-bit codes c[N, D] from bytes[N, D/2]: element k is in byte k // 2, low
+    nibble for even k (reading: the checkpoint stores MXFP4 "packed as U8",
+    Kimi K3 迁移到 Google TPU 的可行性评估, §3.1 权重账)."""
+    b = np.asarray(codes_u8, dtype=np.uint8).astype(np.int64)
+    c = np.stack([b & 0xF, b >> 4], axis=-1)
+    return c.reshape(b.shape[0], b.shape[1] * 2)
+
+
+def dequant_mxfp4(codes_u8, e8m0) -> np.ndarray:
+    """Ŵ[n, k] = E2M1(c[n, k]) * 2**(E[n, k//32] - 127), exactly, in fp64.
+
+    Groups of 32 codes along D share one E8M0 exponent (Kimi K3 迁移到 Google TPU
+    的可行性评估, §2 模型解剖: "W4 group 32 + E8M0 scale")."""
+    v = e2m1_value(mxfp4_codes(codes_u8))
+    n, d = v.shape
+    if d % 32:
+        raise ValueError("D must be a multiple of 32")
+    scale = np.repeat(e8m0_value(np.asarray(e8m0).reshape(n, d // 32)), 32, axis=1)
+    return v * scale
+
+
+# ---------------------------------------------------------------------------
+# The contraction
+# ---------------------------------------------------------------------------
+
+
+def matmul(x_bits, w_hat) -> tuple[np.ndarray, np.ndarray]:
+    """Y = X·Ŵᵀ and A = |X|·|Ŵ|ᵀ in fp64.
+
+    Row-vector convention X[T, D], W[N, D] (one output feature per row of W),
+    Y[T, N] (Kapitsa 源码拆解 02, §"矩阵乘法中数据和参数").  A[t, n] = Σ_k
+    |x[t,k]·ŵ[n,k]| is the scale of the tolerance."""
+    x = bf16_to_f64(x_bits)
+    if x.ndim == 1:
+        x = x[None, :]
+    w = np.asarray(w_hat, np.float64)
+    if x.shape[1] != w.shape[1]:
+        raise ValueError("X and W disagree on D")
+    return x @ w.T, np.abs(x) @ np.abs(w).T
+
+
+def gemm_affine(x_bits, codes_u32, scale_bits, bias_bits):
+    """Affine decode GEMV (T = 1) and prefill GEMM: Y = X·Ŵᵀ."""
+    return matmul(x_bits, dequant_affine(codes_u32, scale_bits, bias_bits))
+
+
+def gemm_mxfp4(x_bits, codes_u8, e8m0):
+    """MXFP4 GEMV/GEMM: Y = X·Ŵᵀ."""
+    return matmul(x_bits, dequant_mxfp4(codes_u8, e8m0))
+
+
+def grouped(x_bits, row_index, seg_expert, seg_offsets, expert_weights, segments=None):
+    """Routed-expert grouped matmul, one product per segment.
+
+    Segment s applies expert seg_expert[s] to the activation rows
+    X[row_index[r]] for r in [seg_offsets[s], seg_offsets[s+1]) and writes
+    rows r of the grouped output (the per-expert GEMM of the MoE block,
+    Colibri Kimi K3 Metal 后端实现全解析, Phase 6).  `expert_weights(e)` returns
+    the fp64 Ŵ of expert e.  With `segments` given only those segments are
+    evaluated; the other output rows are NaN."""
+    x_bits = np.asarray(x_bits)
+    row_index = np.asarray(row_index)
+    seg_offsets = np.asarray(seg_offsets)
+    segs = range(len(seg_expert)) if segments is None else segments
+    y = a = None
+    for s in segs:
+        r0, r1 = int(seg_offsets[s]), int(seg_offsets[s + 1])
+        if r1 == r0:
+            continue
+        w = expert_weights(int(seg_expert[s]))
+        if y is None:
+            m_total = int(seg_offsets[-1])
+            y = np.full((m_total, w.shape[0]), np.nan)
+            a = np.full((m_total, w.shape[0]), np.nan)
+        ys, as_ = matmul(x_bits[row_index[r0:r1]], w)
+        y[r0:r1], a[r0:r1] = ys, as_
+    return y, a
+
+
+def sampled(x_bits, w_row, pairs):
+    """y[t, n] and A[t, n] for chosen (t, n) pairs only, each as its own dot
+    product over k: Σ_k x[t,k]·ŵ[n,k].  `w_row(n)` returns row n of Ŵ in fp64."""
+    x = bf16_to_f64(x_bits)
+    if x.ndim == 1:
+        x = x[None, :]
+    y = np.empty(len(pairs))
+    a = np.empty(len(pairs))
+    cache = {}
+    for i, (t, n) in enumerate(pairs):
+        if n not in cache:
+            cache[n] = w_row(n)
+        prod = x[t] * cache[n]
+        y[i] = prod.sum()
+        a[i] = np.abs(prod).sum()
+    return y, a
+
+
+# ---------------------------------------------------------------------------
+# Acceptance
+# ---------------------------------------------------------------------------
+
+REL_TOL = 2e-3
+ABS_TOL = 1e-5
+
+
+def check(y_bits, y_ref, a_ref, rel=REL_TOL, abs_=ABS_TOL) -> dict:
+    """Per-element acceptance |y_gpu - y| <= rel·A + abs_, with the stored bf16
+    output widened exactly.  Reports max(|err|/tol), max |err| and the mean
+    absolute error (the per-op maxAbs/MAE report of Colibri Kimi K3 Metal
+    后端实现全解析, Phase 5)."""
+    y = bf16_to_f64(y_bits).reshape(np.shape(y_ref))
+    y_ref = np.asarray(y_ref, np.float64)
+    tol = rel * np.asarray(a_ref, np.float64) + abs_
+    err = np.abs(y - y_ref)
+    bad = ~(err <= tol)                     # NaN in y counts as a failure
+    return dict(ok=not bool(bad.any()), n_fail=int(bad.sum()), n=int(err.size),
+                max_ratio=float(np.nanmax(err / tol)) if err.size else 0.0,
+                max_abs=float(np.nanmax(err)) if err.size else 0.0,
+                mae=float(np.nanmean(err)) if err.size else 0.0)

@@ -1,0 +1,314 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix (CPU only).
+
+Each pin is independent of the oracle's own code: golden values printed on the
+pages (tests/golden/, each with its citation), exact rational brute force in
+pure Python on tiny shapes, integer-exact cases, one-hot columns, row sums and
+the tolerance checker's self-test.  `test_planted_mistakes` plants plausible
+mistakes in the oracle (on the CPU) and checks that some pin catches each.
+"""
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+RNG_SEED = 20261202
+
+
+# --- independent exact helpers (pure Python, no numpy views, no oracle code) ---
+
+def bf16_exact(bits: int) -> Fraction:
+    return Fraction(struct.unpack(">f", struct.pack(">I", (int(bits) & 0xFFFF) << 16))[0])
+
+
+def row_nibbles_le(words_row) -> list:
+    """Codes of one row, read from the little-endian bytes of its uint32 words:
+    code k lives in byte k // 2, low nibble when k is even."""
+    raw = b"".join(struct.pack("<I", int(w)) for w in words_row)
+    out = []
+    for byte in raw:
+        out.append(byte & 0xF)
+        out.append(byte >> 4)
+    return out
+
+
+def brute_w_affine(codes, scale, bias):
+    """Exact dequantised rows over the rationals."""
+    out = []
+    for j in range(codes.shape[0]):
+        q = row_nibbles_le(codes[j])
+        out.append([bf16_exact(scale[j][k // 64]) * q[k] + bf16_exact(bias[j][k // 64])
+                    for k in range(len(q))])
+    return out
+
+
+def brute_affine(x_bits, codes, scale, bias):
+    """Exact Y and A over the rationals."""
+    t_, d = x_bits.shape
+    n = codes.shape[0]
+    y = [[Fraction(0)] * n for _ in range(t_)]
+    a = [[Fraction(0)] * n for _ in range(t_)]
+    wall = brute_w_affine(codes, scale, bias)
+    for j in range(n):
+        w = wall[j]
+        for i in range(t_):
+            for k in range(d):
+                p = bf16_exact(x_bits[i][k]) * w[k]
+                y[i][j] += p
+                a[i][j] += abs(p)
+    return y, a
+
+
+def brute_mxfp4(x_bits, codes, e8m0, table):
+    t_, d = x_bits.shape
+    n = codes.shape[0]
+    y = [[Fraction(0)] * n for _ in range(t_)]
+    a = [[Fraction(0)] * n for _ in range(t_)]
+    for j in range(n):
+        c = []
+        for byte in bytes(codes[j].tolist()):
+            c += [byte & 0xF, byte >> 4]
+        w = [Fraction(table[c[k]]) * Fraction(2) ** (int(e8m0[j][k // 32]) - 127) for k in range(d)]
+        for i in range(t_):
+            for k in range(d):
+                p = bf16_exact(x_bits[i][k]) * w[k]
+                y[i][j] += p
+                a[i][j] += abs(p)
+    return y, a
+
+
+def rand_affine(rng, n, d):
+    codes = rng.integers(0, 2 ** 32, size=(n, d // 8), dtype=np.uint64).astype(np.uint32)
+    scale = synth.bf16_bits(rng.uniform(0.01, 0.05, size=(n, d // 64)))
+    bias = synth.bf16_bits(rng.uniform(-0.4, 0.0, size=(n, d // 64)))
+    return codes, scale, bias
+
+
+def rand_x(rng, t, d):
+    return synth.bf16_bits(rng.standard_normal((t, d)))
+
+
+# --- pins ------------------------------------------------------------------
+
+def pin_worked_example(golden):
+    g = golden("affine_worked_example.json")
+    q = list(g["q"]) + [0] * (64 - len(g["q"]))
+    word = [sum(q[8 * i + j] << (4 * j) for j in range(8)) for i in range(8)]
+    codes = np.array([word], np.uint32)
+    scale = synth.bf16_bits(np.array([[g["scale"]]]))
+    bias = synth.bf16_bits(np.array([[g["bias"]]]))
+    w = oracle.dequant_affine(codes, scale, bias)
+    assert w[0, :4].tolist() == g["w"], w[0, :4]
+    # the same values reach the output through the contraction (one-hot rows of X)
+    x = np.zeros((4, 64))
+    x[np.arange(4), np.arange(4)] = 1.0
+    y, _ = oracle.gemm_affine(synth.bf16_bits(x), codes, scale, bias)
+    assert y[:, 0].tolist() == g["w"]
+
+
+def pin_nibble_order(golden):
+    g = golden("nibble_order.json")
+    assert oracle.affine_codes(np.array([g["affine_words"]], np.uint32))[0].tolist() == g["affine_codes"]
+    assert oracle.mxfp4_codes(np.array([g["mxfp4_bytes"]], np.uint8))[0].tolist() == g["mxfp4_codes"]
+
+
+def pin_e2m1(golden):
+    g = golden("e2m1_ocp_mx.json")
+    v = oracle.e2m1_value(np.arange(16))
+    assert v.tolist() == g["values_by_code"]
+    assert np.signbit(v[8]) and not np.signbit(v[0])
+    e = oracle.e8m0_value(np.array(g["e8m0"]["E"]))
+    assert e.tolist() == [2.0 ** p for p in g["e8m0"]["log2_scale"]]
+    assert np.isnan(oracle.e8m0_value(255))
+
+
+def pin_brute_affine(shapes=((1, 1, 64), (2, 2, 128), (3, 7, 192), (5, 33, 64))):
+    rng = np.random.default_rng(RNG_SEED)
+    for t, n, d in shapes:
+        codes, scale, bias = rand_affine(rng, n, d)
+        x = rand_x(rng, t, d)
+        y, a = oracle.gemm_affine(x, codes, scale, bias)
+        ye, ae = brute_affine(x, codes, scale, bias)
+        for i in range(t):
+            for j in range(n):
+                assert abs(y[i, j] - float(ye[i][j])) <= 1e-12 * float(ae[i][j]) + 1e-300, (t, n, d, i, j)
+                assert abs(a[i, j] - float(ae[i][j])) <= 1e-12 * float(ae[i][j])
+
+
+def pin_brute_mxfp4(golden, shapes=((1, 1, 32), (2, 2, 64), (3, 7, 96), (5, 33, 32))):
+    table = golden("e2m1_ocp_mx.json")["values_by_code"]
+    rng = np.random.default_rng(RNG_SEED + 1)
+    for t, n, d in shapes:
+        codes = rng.integers(0, 256, size=(n, d // 2)).astype(np.uint8)
+        e8m0 = rng.integers(100, 140, size=(n, d // 32)).astype(np.uint8)
+        x = rand_x(rng, t, d)
+        y, a = oracle.gemm_mxfp4(x, codes, e8m0)
+        ye, ae = brute_mxfp4(x, codes, e8m0, table)
+        for i in range(t):
+            for j in range(n):
+                assert abs(y[i, j] - float(ye[i][j])) <= 1e-12 * float(ae[i][j]) + 1e-300, (t, n, d, i, j)
+                assert abs(a[i, j] - float(ae[i][j])) <= 1e-12 * float(ae[i][j])
+
+
+def pin_integer_exact():
+    """scale 1, bias 0 and integer x: every result is an exact integer."""
+    rng = np.random.default_rng(RNG_SEED + 2)
+    n, d, t = 9, 192, 3
+    codes = rng.integers(0, 2 ** 32, size=(n, d // 8), dtype=np.uint64).astype(np.uint32)
+    one = synth.bf16_bits(np.ones((n, d // 64)))
+    zero = synth.bf16_bits(np.zeros((n, d // 64)))
+    xi = rng.integers(-3, 4, size=(t, d))
+    y, _ = oracle.gemm_affine(synth.bf16_bits(xi.astype(float)), codes, one, zero)
+    q = np.array([row_nibbles_le(codes[j]) for j in range(n)])
+    assert np.array_equal(y, (xi @ q.T).astype(float))
+
+
+def pin_one_hot_and_row_sums():
+    rng = np.random.default_rng(RNG_SEED + 3)
+    n, d = 5, 128
+    codes, scale, bias = rand_affine(rng, n, d)
+    wref = brute_w_affine(codes, scale, bias)
+    y, _ = oracle.gemm_affine(synth.bf16_bits(np.eye(d)), codes, scale, bias)
+    # one-hot row k of X returns column k of Ŵ, i.e. y[k, j] = ŵ[j, k], exactly
+    assert np.array_equal(y, np.array([[float(wref[j][k]) for j in range(n)] for k in range(d)]))
+    ys, _ = oracle.gemm_affine(synth.bf16_bits(np.ones((1, d))), codes, scale, bias)
+    ye, _ = brute_affine(synth.bf16_bits(np.ones((1, d))), codes, scale, bias)
+    for j in range(n):
+        assert abs(ys[0, j] - float(ye[0][j])) <= 1e-12 * abs(float(ye[0][j])) + 1e-300
+
+
+def pin_checker():
+    rng = np.random.default_rng(RNG_SEED + 4)
+    y = rng.standard_normal(50)
+    a = np.abs(y) + 1.0
+    bits = synth.bf16_bits(y)
+    yb = oracle.bf16_to_f64(bits)
+    assert oracle.check(bits, yb, a)["ok"]
+    bad = yb.copy()
+    bad[7] += 3e-3 * a[7]
+    assert not oracle.check(synth.bf16_bits(bad), yb, a)["ok"]
+    nan = bits.copy()
+    nan[3] = 0x7FC0
+    assert not oracle.check(nan, yb, a)["ok"]
+
+
+def all_pins(golden):
+    pin_worked_example(golden)
+    pin_nibble_order(golden)
+    pin_e2m1(golden)
+    pin_brute_affine(shapes=((1, 3, 128), (2, 5, 192)))
+    pin_brute_mxfp4(golden, shapes=((2, 3, 64), (1, 4, 96)))
+    pin_integer_exact()
+    pin_one_hot_and_row_sums()
+    pin_checker()
+
+
+# --- tests -----------------------------------------------------------------
+
+def test_worked_example(golden):
+    pin_worked_example(golden)
+
+
+def test_nibble_order(golden):
+    pin_nibble_order(golden)
+
+
+def test_e2m1_and_e8m0(golden):
+    pin_e2m1(golden)
+    cfg = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}
+    vals = set(np.abs(oracle.e2m1_value(np.arange(16))).tolist())
+    assert vals == cfg
+
+
+def test_group_sizes(golden):
+    g = golden("format_sizes.json")
+    ga = g["affine_g64"]
+    assert ga["code_bytes"] * 2 == ga["codes_per_group"]
+    assert ga["code_bytes"] + ga["metadata_bytes"] == ga["group_bytes"]
+    assert round(100 * ga["group_bytes"] / ga["bf16_bytes"], 1) == ga["fraction_of_bf16_percent"]
+    w = synth.affine_weights(5, 7, 192)
+    assert w.codes.nbytes + w.scale.nbytes + w.bias.nbytes == ga["group_bytes"] * 7 * 192 // 64
+    m = synth.mxfp4_weights(5, 7, 96, synth.S_GU_CODES, synth.S_GU_E8M0, 0)
+    assert (m.codes.nbytes + m.e8m0.nbytes) * 8 == g["mxfp4_g32"]["bits_per_weight"] * 7 * 96
+    # decode workload: 13824 x 5120 affine weights pack to 39,813,120 bytes
+    assert 13824 * 5120 // 64 * ga["group_bytes"] == 39_813_120
+
+
+def test_bruteforce_affine():
+    pin_brute_affine()
+
+
+def test_bruteforce_mxfp4(golden):
+    pin_brute_mxfp4(golden)
+
+
+def test_integer_exact():
+    pin_integer_exact()
+
+
+def test_one_hot_and_row_sums():
+    pin_one_hot_and_row_sums()
+
+
+def test_checker():
+    pin_checker()
+
+
+def test_bf16_rounding_helper():
+    vals = np.array([0.0, -0.0, 1.0, -3.0, 255.0, 256.0, 257.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8,
+                     2.0 ** -130, 3.0e38, 1e39])
+    got = oracle.f64_to_bf16_bits(vals)
+    # hand-derived patterns: 257 ties to 256; 1+2^-8 ties to 1; 1+3*2^-8 ties up to 1+2^-6;
+    # 2^-130 is the subnormal 8 * 2^-133; 1e39 overflows to inf
+    exp = [0x0000, 0x8000, 0x3F80, 0xC040, 0x437F, 0x4380, 0x4380, 0x3F80, 0x3F82, 0x0008, 0x7F62, 0x7F80]
+    assert got.tolist() == exp
+
+
+def test_grouped_and_sampled(golden):
+    rng = np.random.default_rng(RNG_SEED + 5)
+    e_count, n, d, t = 4, 6, 64, 5
+    ws = {e: rand_affine(rng, n, d) for e in range(e_count)}
+    x = rand_x(rng, t, d)
+    seg_expert = np.array([0, 2, 3], np.int32)
+    seg_offsets = np.array([0, 2, 2, 5], np.int32)     # includes an empty segment
+    row_index = np.array([4, 1, 0, 3, 4], np.int32)
+    y, a = oracle.grouped(x, row_index, seg_expert, seg_offsets,
+                          lambda e: oracle.dequant_affine(*ws[e]))
+    for s in range(3):
+        for r in range(seg_offsets[s], seg_offsets[s + 1]):
+            ye, ae = brute_affine(x[row_index[r]][None, :], *ws[seg_expert[s]])
+            for j in range(n):
+                assert abs(y[r, j] - float(ye[0][j])) <= 1e-12 * float(ae[0][j])
+    pairs = [(0, 1), (4, 5), (2, 0)]
+    ys, as_ = oracle.sampled(x, lambda j: oracle.dequant_affine(*ws[1])[j], pairs)
+    yf, af = oracle.gemm_affine(x, *ws[1])
+    for i, (tt, j) in enumerate(pairs):
+        assert abs(ys[i] - yf[tt, j]) <= 1e-12 * af[tt, j]
+
+
+MUTATIONS = {
+    "drop_bias": ("dequant_affine", lambda orig: (lambda c, s, b: orig(c, s, np.zeros_like(b)))),
+    "nibbles_high_first": ("affine_codes", lambda orig: (lambda w: orig(w).reshape(-1, 8)[:, ::-1].reshape(orig(w).shape))),
+    "group_index_mod": ("dequant_affine", lambda orig: (
+        lambda c, s, b: oracle.affine_codes(c) * np.tile(oracle.bf16_to_f64(s), (1, 64))
+        + np.tile(oracle.bf16_to_f64(b), (1, 64)))),
+    "e8m0_bias_128": ("e8m0_value", lambda orig: (lambda e: orig(e) / 2.0)),
+    "e2m1_no_subnormal": ("e2m1_value", lambda orig: (
+        lambda c: np.where((np.asarray(c) & 7) == 1, np.sign(orig(c)) * 1.0, orig(c)))),
+    "transposed_w": ("matmul", lambda orig: (
+        lambda x, w: orig(x, np.asarray(w)[::-1]) if np.shape(w)[0] > 1 else orig(x, np.asarray(w) * 1.5))),
+    "mxfp4_high_nibble_first": ("mxfp4_codes", lambda orig: (
+        lambda b: orig(b).reshape(-1, 2)[:, ::-1].reshape(orig(b).shape))),
+    "checker_too_loose": ("check", lambda orig: (lambda *a, **k: dict(orig(*a, **k), ok=True))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes(name, golden, monkeypatch):
+    attr, make = MUTATIONS[name]
+    monkeypatch.setattr(oracle, attr, make(getattr(oracle, attr)))
+    with pytest.raises(AssertionError):
+        all_pins(golden)
