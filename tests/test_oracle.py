@@ -183,16 +183,23 @@ def pin_one_hot_and_row_sums():
 def pin_checker():
     rng = np.random.default_rng(RNG_SEED + 4)
     y = rng.standard_normal(50)
-    a = np.abs(y) + 1.0
+    a = 10.0 * np.abs(y) + 10.0              # tolerance well above one bf16 ulp of y
     bits = synth.bf16_bits(y)
     yb = oracle.bf16_to_f64(bits)
     assert oracle.check(bits, yb, a)["ok"]
     bad = yb.copy()
-    bad[7] += 3e-3 * a[7]
+    bad[7] += 1.5 * (2e-3 * a[7] + 1e-5)
     assert not oracle.check(synth.bf16_bits(bad), yb, a)["ok"]
     nan = bits.copy()
     nan[3] = 0x7FC0
     assert not oracle.check(nan, yb, a)["ok"]
+    # the correctly rounded output of an exact value whose products all share a
+    # sign passes even though its rounding error exceeds 2e-3·A; one bf16 step
+    # further does not
+    y_ex, a_ex = 2.054577350616455, 2.785332202911377
+    assert oracle.check(np.array([0x4003], np.uint16), np.array([y_ex]), np.array([a_ex]))["ok"]   # 2.046875
+    assert not oracle.check(np.array([0x4002], np.uint16), np.array([y_ex]), np.array([a_ex]))["ok"]  # 2.03125
+    assert oracle.check(np.array([0x4004], np.uint16), np.array([y_ex]), np.array([a_ex]))["ok"]   # 2.0625
 
 
 def all_pins(golden):
@@ -267,6 +274,18 @@ def test_bf16_rounding_helper():
     assert got.tolist() == exp
 
 
+def test_round_to_bf16_matches_scalar_rounding():
+    rng = np.random.default_rng(RNG_SEED + 6)
+    v = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-40, 39, 2000),
+                        [0.0, -0.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 257.0, 2.0 ** -130,
+                         3 * 2.0 ** -134, 3.0e38, 3.3961e38, 3.4e38, -1e39, 2.0 ** -126 - 2.0 ** -134]])
+    bits = oracle.f64_to_bf16_bits(v)
+    ref = oracle.bf16_to_f64(bits)
+    got = oracle.round_to_bf16(v)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+    assert np.array_equal(got, ref)
+
+
 def test_grouped_and_sampled(golden):
     rng = np.random.default_rng(RNG_SEED + 5)
     e_count, n, d, t = 4, 6, 64, 5
@@ -303,6 +322,7 @@ MUTATIONS = {
     "mxfp4_high_nibble_first": ("mxfp4_codes", lambda orig: (
         lambda b: orig(b).reshape(-1, 2)[:, ::-1].reshape(orig(b).shape))),
     "checker_too_loose": ("check", lambda orig: (lambda *a, **k: dict(orig(*a, **k), ok=True))),
+    "checker_rounds_wrong_way": ("round_to_bf16", lambda orig: (lambda v: orig(v) * (1 + 2.0 ** -6))),
 }
 
 
