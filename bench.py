@@ -1,0 +1,286 @@
+"""Benchmark of the 4-bit weight-quantized matmul hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+One step runs every row of the hot path once, each on inputs already resident
+in HBM:
+  decode    affine GEMV, T=1, D=5120, N=13824 (the headline)
+  prefill   affine GEMM, T=2048, D=5120, N=13824 (bf16 MFMA)
+  moe_dec   MXFP4 grouped GEMV, 16 of 896 experts: gate_up 6144x3584, then
+            down 3584x3072 (a fresh expert draw every step)
+  moe_pre   MXFP4 grouped GEMM, 512 tokens routed top-16 over 896 experts,
+            gate_up only
+Weights of the decode row rotate over enough packed copies (> 2x the 256 MB
+Infinity Cache) that every launch reads HBM, not the cache.
+
+Each kernel launch is bracketed by HIP events on the stream it runs on; its
+average duration gives achieved GB/s (bytes the algorithm must move: packed
+weights + activations + outputs) or TFLOP/s against the chip's peaks.  The
+headline is the decode GEMV's GB/s.  rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
+METRIC = "decode GEMV HBM GB/s (% of peak) + prefill GEMM TFLOP/s (% MFMA peak)"
+
+
+def kernel_sources_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+GEMV_SOURCES = ["bit_weight_quantized_amd/csrc/qmm_gemv.hip", "bit_weight_quantized_amd/csrc/qmm_device.h"]
+
+
+def recorded_traffic(kernel_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the kernel as it is now."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    r = rec.get("decode_gemv")
+    if not r or r.get("kernel_sources_hash") != kernel_hash:
+        return None
+    return r.get("hbm_bytes_per_launch")
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate", type=int, default=24, help="packed copies of the decode weights")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows", default="decode,prefill,moe_dec,moe_pre")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the sharding plan is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import bit_weight_quantized_amd as qmm
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    qmm.load()
+    dev = "cuda"
+    A, M = qmm.QMM_AFFINE4_G64, qmm.QMM_MXFP4_G32
+    rows = [r for r in args.rows.split(",") if r]
+    props = torch.cuda.get_device_properties(0)
+
+    def T(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        elif a.dtype == np.uint32:
+            a = a.view(np.int32)
+        return torch.from_numpy(a).to(dev)
+
+    def log(*a):
+        print("[bench]", *a, file=sys.stderr, flush=True)
+
+    work = {}     # row -> list of (launch fn(step), name, bytes, flops)
+    t_setup = time.time()
+
+    # ---- decode: affine GEMV 13824 x 5120 -------------------------------------------------
+    c1 = synth.CONFIGS[1]
+    n1, d1 = c1["n"], c1["d"]
+    if "decode" in rows:
+        w1 = synth.affine_weights(synth.seed_of(1), n1, d1)
+        p = torch.empty(qmm.qmm_packed_bytes(A, n1, d1), dtype=torch.uint8, device=dev)
+        qmm.qmm_pack(A, n1, d1, T(w1.codes), T(w1.scale), T(w1.bias), p)
+        copies = [p] + [p.clone() for _ in range(args.rotate - 1)]
+        x1 = T(synth.activations(synth.seed_of(1), synth.S_X, 1, d1))
+        y1 = torch.empty(n1, dtype=torch.int16, device=dev)
+        b1 = n1 * d1 * 36 // 64 + 2 * d1 + 2 * n1
+        work["decode"] = [(lambda s: qmm.qmm_gemv(A, copies[s % len(copies)], n1, d1, x1, y1),
+                           "gemv", b1, 2.0 * n1 * d1)]
+        log("decode ready", len(copies), "copies")
+
+    # ---- prefill: affine GEMM 2048 x 5120 x 13824 ------------------------------------------
+    if "prefill" in rows:
+        c2 = synth.CONFIGS[2]
+        t2, n2, d2 = c2["t"], c2["n"], c2["d"]
+        w2 = synth.affine_weights(synth.seed_of(2), n2, d2)
+        p2 = torch.empty(qmm.qmm_packed_bytes(A, n2, d2), dtype=torch.uint8, device=dev)
+        qmm.qmm_pack(A, n2, d2, T(w2.codes), T(w2.scale), T(w2.bias), p2)
+        p2s = [p2, p2.clone()]
+        x2 = T(synth.activations(synth.seed_of(2), synth.S_X, t2, d2))
+        y2 = torch.empty(t2, n2, dtype=torch.int16, device=dev)
+        b2 = n2 * d2 * 36 // 64 + 2 * t2 * d2 + 2 * t2 * n2
+        work["prefill"] = [(lambda s: qmm.qmm_gemm(A, p2s[s % 2], t2, n2, d2, x2, y2),
+                            "gemm", b2, 2.0 * t2 * n2 * d2)]
+        log("prefill ready")
+
+    # ---- MoE: 896-expert MXFP4 stacks built on the device ----------------------------------
+    if "moe_dec" in rows or "moe_pre" in rows:
+        import synth.gpu as sg
+        gu_n, gu_d, dn_n, dn_d = 6144, 3584, 3584, 3072
+        gsz = qmm.qmm_packed_bytes(M, gu_n, gu_d)
+        gu = torch.empty(gsz * 896, dtype=torch.uint8, device=dev)
+        sg.expert_stack(synth.seed_of(3), "gate_up", 896,
+                        lambda c, e, ptr: qmm.qmm_pack(M, gu_n, gu_d, c, e, None, ptr), gsz, gsz, gu)
+        log("gate_up stack ready", gu.numel() / 1e9, "GB")
+    if "moe_dec" in rows:
+        dsz = qmm.qmm_packed_bytes(M, dn_n, dn_d)
+        dn = torch.empty(dsz * 896, dtype=torch.uint8, device=dev)
+        sg.expert_stack(synth.seed_of(3), "down", 896,
+                        lambda c, e, ptr: qmm.qmm_pack(M, dn_n, dn_d, c, e, None, ptr), dsz, dsz, dn)
+        log("down stack ready")
+        seed3 = synth.seed_of(3)
+        x3 = T(synth.activations(seed3, synth.S_X, 1, gu_d))
+        z3 = T(synth.activations(seed3, synth.S_Z, 16, dn_d))
+        nsteps = args.steps + args.warmup
+        draws = T(np.stack([synth.draw_experts(seed3, 16, 896, s) for s in range(nsteps)]).astype(np.int32))
+        offs = T(np.arange(17, dtype=np.int32))
+        zero_idx = T(np.zeros(16, np.int32))
+        iden_idx = T(np.arange(16, dtype=np.int32))
+        h3 = torch.empty(16, gu_n, dtype=torch.int16, device=dev)
+        o3 = torch.empty(16, dn_n, dtype=torch.int16, device=dev)
+        bg = 16 * (gsz - 256) + 2 * gu_d + 2 * 16 * gu_n
+        bd = 16 * (dsz - 256) + 2 * 16 * dn_d + 2 * 16 * dn_n
+        work["moe_dec"] = [
+            (lambda s: qmm.qmm_grouped_gemm(M, gu, gsz, 896, gu_n, gu_d, x3, 1, zero_idx, draws[s],
+                                            offs, 16, 16, 1, h3), "grouped_gemv_gate_up", bg,
+             2.0 * 16 * gu_n * gu_d),
+            (lambda s: qmm.qmm_grouped_gemm(M, dn, dsz, 896, dn_n, dn_d, z3, 16, iden_idx, draws[s],
+                                            offs, 16, 16, 1, o3), "grouped_gemv_down", bd,
+             2.0 * 16 * dn_n * dn_d),
+        ]
+    if "moe_pre" in rows:
+        seed4 = synth.seed_of(4)
+        xb, rb, bias = synth.router_inputs(seed4)
+        rt = synth.route(xb, rb, bias)
+        x4 = T(xb)
+        ri, se, so = T(rt.row_index), T(rt.seg_expert), T(rt.seg_offsets)
+        y4 = torch.empty(rt.m_total, gu_n, dtype=torch.int16, device=dev)
+        b4 = rt.n_seg * (gsz - 256) + 2 * xb.size + 2 * rt.m_total * gu_n
+        moe_pre_info = dict(active_experts=rt.n_seg, routed_rows=rt.m_total, max_seg_rows=rt.max_seg_rows)
+        work["moe_pre"] = [(lambda s: qmm.qmm_grouped_gemm(M, gu, gsz, 896, gu_n, gu_d, x4, xb.shape[0], ri,
+                                                           se, so, rt.n_seg, rt.m_total, rt.max_seg_rows, y4),
+                            "grouped_gemm", b4, 2.0 * rt.m_total * gu_n * gu_d)]
+        log("moe_pre ready", moe_pre_info)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    launches = [(row, fn, name, nb, fl) for row in rows for (fn, name, nb, fl) in work[row]]
+    stream = torch.cuda.current_stream()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches] for _ in range(args.steps)]
+
+    for s in range(args.warmup):
+        for (_, fn, _, _, _) in launches:
+            fn(s + args.steps)
+    torch.cuda.synchronize()
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for s in range(args.steps):
+        for i, (_, fn, _, _, _) in enumerate(launches):
+            ev[s][i][0].record(stream)
+            fn(s)
+            ev[s][i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    results = {}
+    for i, (row, fn, name, nb, fl) in enumerate(launches):
+        us = np.array([ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e3 for s in range(args.steps)])
+        mean = float(us.mean())
+        results[name] = dict(row=row, us_mean=round(mean, 3), us_median=round(float(np.median(us)), 3),
+                             us_p10=round(float(np.percentile(us, 10)), 3),
+                             us_p90=round(float(np.percentile(us, 90)), 3),
+                             bytes=int(nb), flops=fl,
+                             GBps=round(nb / mean / 1e3, 1), TFLOPs=round(fl / mean / 1e6, 2),
+                             hbm_frac=round(nb / mean / 1e3 / HBM_PEAK_GBPS, 4),
+                             mfma_frac=round(fl / mean / 1e6 / BF16_PEAK_TFLOPS, 4))
+
+    out = {
+        "metric": METRIC,
+        "value": None, "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded counter-based generator; no weights or datasets)",
+        "config": {"workload": synth.CONFIGS[1]["name"], "t": 1, "d": d1, "n": n1,
+                   "format": "affine4_g64", "rotation_copies": args.rotate,
+                   "step": "decode GEMV + prefill GEMM + MoE decode grouped GEMV x2 + MoE prefill grouped GEMM"
+                   if len(rows) == 4 else ",".join(rows)},
+    }
+    if "gemv" in results:
+        g = results["gemv"]
+        out["value"] = g["GBps"]
+        kh = kernel_sources_hash(GEMV_SOURCES)
+        traffic = recorded_traffic(kh)
+        out["roofline"] = {"bound": "hbm", "achieved": g["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": g["hbm_frac"], "traffic": traffic, "kernel": "gemv_kernel<affine>",
+                           "algorithmic_bytes_per_launch": g["bytes"], "kernel_sources_hash": kh}
+    if "gemm" in results:
+        g = results["gemm"]
+        out["prefill_gemm"] = {"value": g["TFLOPs"], "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
+                               "frac": g["mfma_frac"], "us_mean": g["us_mean"],
+                               "workload": synth.CONFIGS[2]["name"]}
+    out["rows"] = results
+    if "moe_pre" in rows:
+        out["rows"]["grouped_gemm"].update(moe_pre_info)
+    out["gpu"] = {"name": props.name, "cus": props.multi_processor_count,
+                  "hip": torch.version.hip, "torch": torch.__version__}
+    out["setup_s"] = round(t_setup, 1)
+    out["wall_s_timed"] = round(wall, 3)
+
+    if not args.no_cpu_baseline and "decode" in rows:
+        out["cpu_baseline"] = cpu_baseline(w1, synth.activations(synth.seed_of(1), synth.S_X, 1, d1), b1)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(w, x_bits, nbytes, budget_s: float = 12.0):
+    """The oracle as it stands, on this host, on whole decode GEMVs of the
+    headline workload (repeated until `budget_s` of CPU work is spent)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    reps, t = 0, 0.0
+    while t < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        oracle.gemm_affine(x_bits, w.codes, w.scale, w.bias)
+        t += time.perf_counter() - t0
+        reps += 1
+    per = t / reps
+    return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle", "seconds_per_gemv": round(per, 3),
+            "sample": f"{reps} full 13824x5120 affine GEMVs (fp64 dequant in numpy, single thread; "
+                      f"fp64 matvec in the numpy BLAS with {blas_threads} threads)"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,158 @@
+"""Python binding of libqmm, the MI355X 4-bit weight-quantized matmul library.
+
+Argument marshalling only: every function here forwards to the C ABI of the
+same name in ``libqmm.so`` (declared in ``include/qmm.h``); all computation
+runs in the library's HIP kernels.  Pointer arguments accept a torch tensor
+(its ``data_ptr()``), a raw integer address, or ``None`` for NULL.  Calls are
+asynchronous on ``stream`` (default: torch's current stream).  A non-OK status
+raises :class:`QmmError`; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "QMM_AFFINE4_G64", "QMM_MXFP4_G32", "QmmError", "lib_path", "load",
+    "qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
+    "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
+    "qmm_layout_version", "EXPORTS",
+]
+
+QMM_AFFINE4_G64 = 1
+QMM_MXFP4_G32 = 2
+
+STATUS = {0: "QMM_OK", 1: "QMM_E_ARG", 2: "QMM_E_SHAPE", 3: "QMM_E_ALIGN", 4: "QMM_E_UNSUPPORTED",
+          5: "QMM_E_WORKSPACE", 6: "QMM_E_HIP", 7: "QMM_E_LAYOUT", 8: "QMM_E_VALUE"}
+
+EXPORTS = ("qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
+           "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
+           "qmm_layout_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libqmm.so")
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{func} -> {self.name}: {detail}")
+
+
+def load():
+    """Load libqmm.so (once).  Fails loudly when the library is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m bit_weight_quantized_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    i64, i32, sz, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    sig = {
+        "qmm_packed_bytes": (sz, [ctypes.c_int, i64, i64]),
+        "qmm_workspace_bytes": (sz, [ctypes.c_int, i64, i64, i64]),
+        "qmm_pack": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, vp, vp, vp]),
+        "qmm_unpack": (ctypes.c_int, [ctypes.c_int, i64, i64, vp, vp, vp, vp, vp]),
+        "qmm_gemv": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp, vp, sz, vp]),
+        "qmm_gemm": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, i64, vp, vp, vp, sz, vp]),
+        "qmm_grouped_gemm": (ctypes.c_int, [ctypes.c_int, vp, i64, i32, i64, i64, vp, i64, vp, vp,
+                                            vp, i32, i32, i32, vp, vp, sz, vp]),
+        "qmm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "qmm_last_error": (ctypes.c_char_p, []),
+        "qmm_layout_version": (ctypes.c_uint32, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _ptr(v):
+    if v is None:
+        return None
+    if isinstance(v, int):
+        return v
+    return v.data_ptr()
+
+
+def _nbytes(v):
+    if v is None:
+        return 0
+    if isinstance(v, int):
+        raise TypeError("pass the workspace as a tensor so its size is known")
+    return v.numel() * v.element_size()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(status: int, func: str):
+    if status != 0:
+        lib = load()
+        raise QmmError(status, func, (lib.qmm_last_error() or b"").decode())
+
+
+def qmm_packed_bytes(fmt: int, n: int, d: int) -> int:
+    return int(load().qmm_packed_bytes(fmt, n, d))
+
+
+def qmm_workspace_bytes(fmt: int, t: int, n: int, d: int) -> int:
+    return int(load().qmm_workspace_bytes(fmt, t, n, d))
+
+
+def qmm_layout_version() -> int:
+    return int(load().qmm_layout_version())
+
+
+def qmm_status_string(status: int) -> str:
+    return load().qmm_status_string(status).decode()
+
+
+def qmm_last_error() -> str:
+    return (load().qmm_last_error() or b"").decode()
+
+
+def qmm_pack(fmt, n, d, codes, scales, biases, packed, stream=None):
+    _check(load().qmm_pack(fmt, n, d, _ptr(codes), _ptr(scales), _ptr(biases), _ptr(packed),
+                           _stream(stream)), "qmm_pack")
+
+
+def qmm_unpack(fmt, n, d, packed, codes, scales, biases, stream=None):
+    _check(load().qmm_unpack(fmt, n, d, _ptr(packed), _ptr(codes), _ptr(scales), _ptr(biases),
+                             _stream(stream)), "qmm_unpack")
+
+
+def qmm_gemv(fmt, packed, n, d, x, y, ws=None, stream=None):
+    _check(load().qmm_gemv(fmt, _ptr(packed), n, d, _ptr(x), _ptr(y), _ptr(ws), _nbytes(ws),
+                           _stream(stream)), "qmm_gemv")
+
+
+def qmm_gemm(fmt, packed, t, n, d, x, y, ws=None, stream=None):
+    _check(load().qmm_gemm(fmt, _ptr(packed), t, n, d, _ptr(x), _ptr(y), _ptr(ws), _nbytes(ws),
+                           _stream(stream)), "qmm_gemm")
+
+
+def qmm_grouped_gemm(fmt, packed_stack, expert_stride_bytes, n_experts, n, d, x, t_x, row_index,
+                     seg_expert, seg_offsets, n_seg, m_total, max_seg_rows, y, ws=None,
+                     stream=None):
+    _check(load().qmm_grouped_gemm(fmt, _ptr(packed_stack), expert_stride_bytes, n_experts, n, d,
+                                   _ptr(x), t_x, _ptr(row_index), _ptr(seg_expert),
+                                   _ptr(seg_offsets), n_seg, m_total, max_seg_rows, _ptr(y),
+                                   _ptr(ws), _nbytes(ws), _stream(stream)), "qmm_grouped_gemm")

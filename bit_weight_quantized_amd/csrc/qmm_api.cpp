@@ -1,0 +1,235 @@
+// C-ABI entry points of libqmm: argument validation (host only, before any
+// HIP call), kernel selection and error mapping.  See include/qmm.h.
+#include <hip/hip_runtime.h>
+
+#include <stdio.h>
+#include <string.h>
+
+#include "qmm_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+qmm_status fail(qmm_status s, const char* what) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s", what);
+  return s;
+}
+
+qmm_status hip_fail(int err, const char* where) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where,
+           hipGetErrorString(static_cast<hipError_t>(err)));
+  return QMM_E_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool valid_format(int f) { return f == QMM_AFFINE4_G64 || f == QMM_MXFP4_G32; }
+
+qmm_status check_shape(int f, int64_t n, int64_t d, qmm::Layout* l) {
+  if (!valid_format(f)) return fail(QMM_E_ARG, "unknown format");
+  if (n < 1 || d < 1) return fail(QMM_E_ARG, "n and d must be >= 1");
+  if (!qmm::layout_of(f, n, d, l)) return fail(QMM_E_SHAPE, "d must be a multiple of the group size, n <= 2^28, d <= 65536");
+  return QMM_OK;
+}
+
+qmm_status check_ws(int f, int64_t t, int64_t n, int64_t d, const void* ws, size_t ws_bytes) {
+  const size_t need = qmm_workspace_bytes(static_cast<qmm_format>(f), t, n, d);
+  if (need && (!ws || ws_bytes < need)) return fail(QMM_E_WORKSPACE, "workspace too small");
+  return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d) {
+  qmm::Layout l;
+  if (!valid_format(f) || !qmm::layout_of(f, n, d, &l)) return 0;
+  return size_t(l.total_bytes);
+}
+
+size_t qmm_workspace_bytes(qmm_format, int64_t, int64_t, int64_t) { return 0; }
+
+uint32_t qmm_layout_version(void) { return qmm::kLayoutVersion; }
+
+const char* qmm_last_error(void) { return g_last_error; }
+
+const char* qmm_status_string(qmm_status s) {
+  switch (s) {
+    case QMM_OK: return "ok";
+    case QMM_E_ARG: return "invalid argument";
+    case QMM_E_SHAPE: return "unsupported shape";
+    case QMM_E_ALIGN: return "misaligned pointer";
+    case QMM_E_UNSUPPORTED: return "unsupported request";
+    case QMM_E_WORKSPACE: return "workspace too small";
+    case QMM_E_HIP: return "HIP runtime error";
+    case QMM_E_LAYOUT: return "packed blob does not match the requested weights";
+    case QMM_E_VALUE: return "value outside the format";
+  }
+  return "unknown status";
+}
+
+qmm_status qmm_pack(qmm_format f, int64_t n, int64_t d, const void* codes, const void* scales,
+                    const void* biases, void* packed, void* stream) {
+  g_last_error[0] = 0;
+  qmm::Layout l;
+  qmm_status st = check_shape(f, n, d, &l);
+  if (st) return st;
+  if (!codes || !scales || !packed) return fail(QMM_E_ARG, "NULL pointer");
+  if (f == QMM_AFFINE4_G64 && !biases) return fail(QMM_E_ARG, "affine weights need biases");
+  if (f == QMM_MXFP4_G32 && biases) return fail(QMM_E_ARG, "MXFP4 weights take no biases");
+  if (!aligned(packed, 256)) return fail(QMM_E_ALIGN, "packed must be 256-byte aligned");
+  if (!aligned(codes, 4) || !aligned(scales, 2) || (biases && !aligned(biases, 2)))
+    return fail(QMM_E_ALIGN, "codes must be 4-byte, scales/biases 2-byte aligned");
+  int err = qmm::launch_pack(f, n, d, codes, scales, biases, packed, stream);
+  if (err) return hip_fail(err, "qmm_pack");
+  if (f == QMM_MXFP4_G32) {
+    qmm::PackedHeader h;
+    err = qmm::read_header(packed, &h, stream);
+    if (err) return hip_fail(err, "qmm_pack");
+    if (h.flags & qmm::kFlagInvalid) return fail(QMM_E_VALUE, "E8M0 scale 255 (NaN) in the input");
+  }
+  return QMM_OK;
+}
+
+qmm_status qmm_unpack(qmm_format f, int64_t n, int64_t d, const void* packed, void* codes,
+                      void* scales, void* biases, void* stream) {
+  g_last_error[0] = 0;
+  qmm::Layout l;
+  qmm_status st = check_shape(f, n, d, &l);
+  if (st) return st;
+  if (!codes || !scales || !packed) return fail(QMM_E_ARG, "NULL pointer");
+  if (f == QMM_AFFINE4_G64 && !biases) return fail(QMM_E_ARG, "affine weights need biases");
+  if (!aligned(packed, 256)) return fail(QMM_E_ALIGN, "packed must be 256-byte aligned");
+  if (!aligned(codes, 4) || !aligned(scales, 2) || (biases && !aligned(biases, 2)))
+    return fail(QMM_E_ALIGN, "codes must be 4-byte, scales/biases 2-byte aligned");
+  qmm::PackedHeader h;
+  int err = qmm::read_header(packed, &h, stream);
+  if (err) return hip_fail(err, "qmm_unpack");
+  if (h.magic != qmm::kMagic || h.version != qmm::kLayoutVersion || h.format != uint32_t(f) ||
+      h.n != n || h.d != d || (h.flags & qmm::kFlagInvalid))
+    return fail(QMM_E_LAYOUT, "blob header does not match (magic, version, format, n, d)");
+  err = qmm::launch_unpack(f, n, d, packed, codes, scales, biases, stream);
+  if (err) return hip_fail(err, "qmm_unpack");
+  return QMM_OK;
+}
+
+qmm_status qmm_gemv(qmm_format f, const void* packed, int64_t n, int64_t d, const qmm_bf16* x,
+                    qmm_bf16* y, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  qmm::Layout l;
+  qmm_status st = check_shape(f, n, d, &l);
+  if (st) return st;
+  if (!packed || !x || !y) return fail(QMM_E_ARG, "NULL pointer");
+  if (!aligned(packed, 256)) return fail(QMM_E_ALIGN, "packed must be 256-byte aligned");
+  if (!aligned(x, 16)) return fail(QMM_E_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(y, 2)) return fail(QMM_E_ALIGN, "y must be 2-byte aligned");
+  if ((st = check_ws(f, 1, n, d, ws, ws_bytes))) return st;
+  qmm::GemvArgs a{};
+  a.f = f;
+  a.packed = static_cast<const uint8_t*>(packed);
+  a.n = int(n);
+  a.d = int(d);
+  a.x = x;
+  a.y = y;
+  int err = qmm::launch_gemv(a, stream);
+  if (err) return hip_fail(err, "qmm_gemv");
+  return QMM_OK;
+}
+
+qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
+                    const qmm_bf16* x, qmm_bf16* y, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  qmm::Layout l;
+  qmm_status st = check_shape(f, n, d, &l);
+  if (st) return st;
+  if (t < 1) return fail(QMM_E_ARG, "t must be >= 1");
+  if (t > qmm::kMaxT) return fail(QMM_E_SHAPE, "t must be <= 2^24");
+  if (!packed || !x || !y) return fail(QMM_E_ARG, "NULL pointer");
+  if (!aligned(packed, 256)) return fail(QMM_E_ALIGN, "packed must be 256-byte aligned");
+  if (!aligned(x, 16)) return fail(QMM_E_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(y, 2)) return fail(QMM_E_ALIGN, "y must be 2-byte aligned");
+  if ((st = check_ws(f, t, n, d, ws, ws_bytes))) return st;
+  if (t == 1) return qmm_gemv(f, packed, n, d, x, y, ws, ws_bytes, stream);
+  qmm::GemmArgs a{};
+  a.f = f;
+  a.packed = static_cast<const uint8_t*>(packed);
+  a.t = int(t);
+  a.n = int(n);
+  a.d = int(d);
+  a.x = x;
+  a.y = y;
+  int err = qmm::launch_gemm(a, stream);
+  if (err) return hip_fail(err, "qmm_gemm");
+  return QMM_OK;
+}
+
+qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expert_stride_bytes,
+                            int32_t n_experts, int64_t n, int64_t d, const qmm_bf16* x,
+                            int64_t t_x, const int32_t* row_index, const int32_t* seg_expert,
+                            const int32_t* seg_offsets, int32_t n_seg, int32_t m_total,
+                            int32_t max_seg_rows, qmm_bf16* y, void* ws, size_t ws_bytes,
+                            void* stream) {
+  g_last_error[0] = 0;
+  qmm::Layout l;
+  qmm_status st = check_shape(f, n, d, &l);
+  if (st) return st;
+  if (n_experts < 1) return fail(QMM_E_ARG, "n_experts must be >= 1");
+  if (expert_stride_bytes < l.total_bytes || expert_stride_bytes % 256)
+    return fail(QMM_E_ARG, "expert_stride_bytes must be a multiple of 256 and >= qmm_packed_bytes");
+  if (n_seg < 0 || m_total < 0 || t_x < 1) return fail(QMM_E_ARG, "n_seg, m_total >= 0 and t_x >= 1 required");
+  if (n_seg > 65535) return fail(QMM_E_SHAPE, "n_seg must be <= 65535");
+  if (!packed_stack || !x || !y) return fail(QMM_E_ARG, "NULL pointer");
+  if (n_seg > 0 && (!row_index || !seg_expert || !seg_offsets))
+    return fail(QMM_E_ARG, "NULL routing table");
+  if (n_seg > 0 && max_seg_rows < 1) return fail(QMM_E_ARG, "max_seg_rows must be >= 1");
+  if (!aligned(packed_stack, 256)) return fail(QMM_E_ALIGN, "packed_stack must be 256-byte aligned");
+  if (!aligned(x, 16)) return fail(QMM_E_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(y, 2)) return fail(QMM_E_ALIGN, "y must be 2-byte aligned");
+  if (!aligned(row_index, 4) || !aligned(seg_expert, 4) || !aligned(seg_offsets, 4))
+    return fail(QMM_E_ALIGN, "routing tables must be 4-byte aligned");
+  if ((st = check_ws(f, m_total, n, d, ws, ws_bytes))) return st;
+  if (n_seg == 0 || m_total == 0) return QMM_OK;
+  int err;
+  if (max_seg_rows == 1) {
+    qmm::GemvArgs a{};
+    a.f = f;
+    a.packed = static_cast<const uint8_t*>(packed_stack);
+    a.expert_stride = expert_stride_bytes;
+    a.n_experts = n_experts;
+    a.n = int(n);
+    a.d = int(d);
+    a.x = x;
+    a.t_x = t_x;
+    a.row_index = row_index;
+    a.seg_expert = seg_expert;
+    a.seg_offsets = seg_offsets;
+    a.n_seg = n_seg;
+    a.m_total = m_total;
+    a.y = y;
+    err = qmm::launch_gemv(a, stream);
+  } else {
+    qmm::GemmArgs a{};
+    a.f = f;
+    a.packed = static_cast<const uint8_t*>(packed_stack);
+    a.expert_stride = expert_stride_bytes;
+    a.n_experts = n_experts;
+    a.n = int(n);
+    a.d = int(d);
+    a.x = x;
+    a.t_x = t_x;
+    a.row_index = row_index;
+    a.seg_expert = seg_expert;
+    a.seg_offsets = seg_offsets;
+    a.n_seg = n_seg;
+    a.m_total = m_total;
+    a.max_seg_rows = max_seg_rows;
+    a.y = y;
+    err = qmm::launch_grouped_gemm(a, stream);
+  }
+  if (err) return hip_fail(err, "qmm_grouped_gemm");
+  return QMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Internal definitions shared by the qmm library sources (host and device).
+//
+// Packed device layout, version 1 (written by qmm_pack, read by every kernel):
+//
+//   [0, 256)            header (PackedHeader)
+//   [256, meta_off)     codes, row-major, d/2 bytes per row
+//   [meta_off, total)   per-group metadata, row-major
+//
+// affine codes: one uint32 per 8 codes, nibbles regrouped so that the low
+//   half-word holds the even codes and the high half-word the odd codes:
+//   bits 4i..4i+3 = q[8w + 2i], bits 16+4i..16+4i+3 = q[8w + 2i + 1], i = 0..3.
+//   (w >> 4i) & 0x000F000F then isolates the consecutive pair (q[2i], q[2i+1])
+//   in the two bf16 lanes of a register, ready for a 2-wide bf16 dot with the
+//   matching pair of activations.
+// affine metadata: uint32 per group, bf16 scale in the low half, bf16 bias in
+//   the high half (4 bytes per 64 codes, so 36 bytes per group in total).
+// MXFP4 codes: the canonical byte order (even code in the low nibble), which
+//   is the order the gfx950 FP4 -> bf16 pair conversion consumes.
+// MXFP4 metadata: the E8M0 bytes, one per 32 codes.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qmm.h"
+
+namespace qmm {
+
+constexpr uint32_t kMagic = 0x344D4D51u;  // "QMM4"
+constexpr uint32_t kLayoutVersion = 1;
+constexpr uint32_t kFlagInvalid = 1u;     // set by qmm_pack when an E8M0 byte is 255
+constexpr int64_t kHeaderBytes = 256;
+constexpr int64_t kMaxN = int64_t(1) << 28;  // keeps every grid below 2^32 work-items
+constexpr int64_t kMaxD = 65536;
+constexpr int64_t kMaxT = int64_t(1) << 24;
+
+struct PackedHeader {
+  uint32_t magic;
+  uint32_t version;
+  uint32_t format;
+  uint32_t flags;
+  int64_t n;
+  int64_t d;
+  int64_t codes_offset;
+  int64_t meta_offset;
+  int64_t total_bytes;
+};
+static_assert(sizeof(PackedHeader) <= kHeaderBytes, "header too large");
+
+inline int group_of(int f) { return f == QMM_AFFINE4_G64 ? 64 : (f == QMM_MXFP4_G32 ? 32 : 0); }
+
+inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+  int64_t codes_offset, meta_offset, meta_bytes, total_bytes;
+};
+
+inline bool layout_of(int f, int64_t n, int64_t d, Layout* out) {
+  const int g = group_of(f);
+  if (g == 0 || n < 1 || n > kMaxN || d < g || d > kMaxD || d % g) return false;
+  Layout l;
+  l.codes_offset = kHeaderBytes;
+  l.meta_offset = round_up(l.codes_offset + n * (d / 2), 256);
+  l.meta_bytes = f == QMM_AFFINE4_G64 ? n * (d / 64) * 4 : n * (d / 32);
+  l.total_bytes = round_up(l.meta_offset + l.meta_bytes, 256);
+  *out = l;
+  return true;
+}
+
+}  // namespace qmm
+
+// ---------------------------------------------------------------------------
+// Launchers implemented in the .hip files (host side, return hipError_t as int)
+// ---------------------------------------------------------------------------
+namespace qmm {
+
+struct DevInfo {
+  int cus;
+};
+int device_info(DevInfo* out);  // 0 on success, else a hipError_t
+
+int launch_pack(int f, int64_t n, int64_t d, const void* codes, const void* scales,
+                const void* biases, void* packed, void* stream);
+int launch_unpack(int f, int64_t n, int64_t d, const void* packed, void* codes, void* scales,
+                  void* biases, void* stream);
+int read_header(const void* packed, PackedHeader* out, void* stream);
+
+struct GemvArgs {
+  int f;
+  const uint8_t* packed;         // blob (dense) or stack (grouped)
+  int64_t expert_stride;         // grouped only
+  int n_experts;                 // grouped only
+  int n, d;
+  const uint16_t* x;
+  int64_t t_x;                   // grouped: rows of x
+  const int32_t* row_index;      // grouped only
+  const int32_t* seg_expert;     // grouped only
+  const int32_t* seg_offsets;    // grouped only
+  int n_seg;                     // grouped only (0 = dense)
+  int m_total;                   // grouped only
+  uint16_t* y;
+};
+int launch_gemv(const GemvArgs& a, void* stream);
+
+struct GemmArgs {
+  int f;
+  const uint8_t* packed;
+  int64_t expert_stride;
+  int n_experts;
+  int t, n, d;
+  const uint16_t* x;
+  int64_t t_x;
+  const int32_t* row_index;
+  const int32_t* seg_expert;
+  const int32_t* seg_offsets;
+  int n_seg;
+  int m_total;
+  int max_seg_rows;
+  uint16_t* y;
+};
+int launch_gemm(const GemmArgs& a, void* stream);
+int launch_grouped_gemm(const GemmArgs& a, void* stream);
+
+}  // namespace qmm

@@ -1,0 +1,171 @@
+// qmm_pack / qmm_unpack kernels: canonical weights <-> MI355X device layout.
+// A bit/byte permutation plus a header; no arithmetic on weight values
+// (format and layout in qmm_internal.h).
+#include <hip/hip_runtime.h>
+
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+namespace {
+
+// Canonical word: nibble j holds q[8w + j].  Device word: even codes in the
+// low half-word, odd codes in the high half-word (see qmm_internal.h).
+__device__ __forceinline__ uint32_t to_device_word(uint32_t c) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r |= ((c >> (8 * i)) & 0xFu) << (4 * i);
+    r |= ((c >> (8 * i + 4)) & 0xFu) << (16 + 4 * i);
+  }
+  return r;
+}
+
+__device__ __forceinline__ uint32_t from_device_word(uint32_t v) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r |= ((v >> (4 * i)) & 0xFu) << (8 * i);
+    r |= ((v >> (16 + 4 * i)) & 0xFu) << (8 * i + 4);
+  }
+  return r;
+}
+
+// Zeroes the header block and the alignment gaps after the codes and after
+// the metadata, then writes the header fields.  One block of 64 threads.
+__global__ void write_header_kernel(uint8_t* packed, PackedHeader h, int64_t gap0, int64_t gap0_end,
+                                    int64_t gap1, int64_t gap1_end) {
+  for (int64_t i = threadIdx.x; i < kHeaderBytes; i += blockDim.x) packed[i] = 0;
+  for (int64_t i = gap0 + threadIdx.x; i < gap0_end; i += blockDim.x) packed[i] = 0;
+  for (int64_t i = gap1 + threadIdx.x; i < gap1_end; i += blockDim.x) packed[i] = 0;
+  __syncthreads();
+  if (threadIdx.x == 0) *reinterpret_cast<PackedHeader*>(packed) = h;
+}
+
+__global__ void pack_affine_kernel(const uint32_t* __restrict__ codes,
+                                   const uint16_t* __restrict__ scales,
+                                   const uint16_t* __restrict__ biases,
+                                   uint32_t* __restrict__ out_codes, uint32_t* __restrict__ out_meta,
+                                   int64_t n_words, int64_t n_groups) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_words; i += stride) {
+    out_codes[i] = to_device_word(codes[i]);
+  }
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_groups; i += stride) {
+    out_meta[i] = uint32_t(scales[i]) | (uint32_t(biases[i]) << 16);
+  }
+}
+
+__global__ void unpack_affine_kernel(const uint32_t* __restrict__ in_codes,
+                                     const uint32_t* __restrict__ in_meta, uint32_t* __restrict__ codes,
+                                     uint16_t* __restrict__ scales, uint16_t* __restrict__ biases,
+                                     int64_t n_words, int64_t n_groups) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_words; i += stride) {
+    codes[i] = from_device_word(in_codes[i]);
+  }
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_groups; i += stride) {
+    const uint32_t m = in_meta[i];
+    scales[i] = uint16_t(m & 0xFFFFu);
+    biases[i] = uint16_t(m >> 16);
+  }
+}
+
+// MXFP4 codes are stored in canonical byte order; the E8M0 bytes are copied
+// and any 255 (NaN scale) flags the blob invalid.
+__global__ void pack_mxfp4_meta_kernel(const uint8_t* __restrict__ e8m0, uint8_t* __restrict__ out,
+                                       int64_t count, uint32_t* __restrict__ flags) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  bool bad = false;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) {
+    const uint8_t e = e8m0[i];
+    bad |= (e == 255);
+    out[i] = e;
+  }
+  if (bad) atomicOr(flags, kFlagInvalid);
+}
+
+int grid_for(int64_t items) {
+  int64_t g = (items + 255) / 256;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return int(g);
+}
+
+}  // namespace
+
+int device_info(DevInfo* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return int(e);
+  static int cached_dev = -1, cached_cus = 0;
+  if (cached_dev != dev) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return int(e);
+    cached_cus = cus;
+    cached_dev = dev;
+  }
+  out->cus = cached_cus;
+  return 0;
+}
+
+int launch_pack(int f, int64_t n, int64_t d, const void* codes, const void* scales,
+                const void* biases, void* packed, void* stream) {
+  Layout l;
+  if (!layout_of(f, n, d, &l)) return int(hipErrorInvalidValue);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* p = static_cast<uint8_t*>(packed);
+  PackedHeader h{kMagic, kLayoutVersion, uint32_t(f), 0u, n, d, l.codes_offset, l.meta_offset,
+                 l.total_bytes};
+  hipError_t e = hipSuccess;
+  hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, s, p, h,
+                     l.codes_offset + n * (d / 2), l.meta_offset, l.meta_offset + l.meta_bytes,
+                     l.total_bytes);
+  if (f == QMM_AFFINE4_G64) {
+    const int64_t n_words = n * (d / 8), n_groups = n * (d / 64);
+    hipLaunchKernelGGL(pack_affine_kernel, dim3(grid_for(n_words)), dim3(256), 0, s,
+                       static_cast<const uint32_t*>(codes), static_cast<const uint16_t*>(scales),
+                       static_cast<const uint16_t*>(biases),
+                       reinterpret_cast<uint32_t*>(p + l.codes_offset),
+                       reinterpret_cast<uint32_t*>(p + l.meta_offset), n_words, n_groups);
+  } else {
+    e = hipMemcpyAsync(p + l.codes_offset, codes, size_t(n * (d / 2)), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return int(e);
+    hipLaunchKernelGGL(pack_mxfp4_meta_kernel, dim3(grid_for(l.meta_bytes)), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(scales), p + l.meta_offset, l.meta_bytes,
+                       reinterpret_cast<uint32_t*>(p + offsetof(PackedHeader, flags)));
+  }
+  return int(hipGetLastError());
+}
+
+int read_header(const void* packed, PackedHeader* out, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(out, packed, sizeof(PackedHeader), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return int(e);
+  return int(hipStreamSynchronize(s));
+}
+
+int launch_unpack(int f, int64_t n, int64_t d, const void* packed, void* codes, void* scales,
+                  void* biases, void* stream) {
+  Layout l;
+  if (!layout_of(f, n, d, &l)) return int(hipErrorInvalidValue);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint8_t* p = static_cast<const uint8_t*>(packed);
+  if (f == QMM_AFFINE4_G64) {
+    const int64_t n_words = n * (d / 8), n_groups = n * (d / 64);
+    hipLaunchKernelGGL(unpack_affine_kernel, dim3(grid_for(n_words)), dim3(256), 0, s,
+                       reinterpret_cast<const uint32_t*>(p + l.codes_offset),
+                       reinterpret_cast<const uint32_t*>(p + l.meta_offset),
+                       static_cast<uint32_t*>(codes), static_cast<uint16_t*>(scales),
+                       static_cast<uint16_t*>(biases), n_words, n_groups);
+    return int(hipGetLastError());
+  }
+  hipError_t e = hipMemcpyAsync(codes, p + l.codes_offset, size_t(n * (d / 2)),
+                                hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return int(e);
+  e = hipMemcpyAsync(scales, p + l.meta_offset, size_t(l.meta_bytes), hipMemcpyDeviceToDevice, s);
+  return int(e);
+}
+
+}  // namespace qmm

@@ -1,0 +1,156 @@
+/*
+ * qmm.h — 4-bit weight-quantized matmul Y = X·Wᵀ on AMD MI355X (gfx950).
+ *
+ * X[T, D] holds bf16 activations, W[N, D] holds 4-bit codes (one output
+ * feature per row of W), Y[T, N] is stored as bf16 (row-vector convention of
+ * Kapitsa 源码拆解 02：权重、矩阵与 Metal, section "矩阵乘法中数据和参数").
+ *
+ * Weight formats
+ *   QMM_AFFINE4_G64  groups of 64 codes along D, one bf16 scale and one bf16
+ *                    bias per group, w = scale·q + bias with q in 0..15
+ *                    (same page, section "权重怎样存储": 32 bytes of codes plus
+ *                    two bf16, 36 bytes per 64 weights).
+ *   QMM_MXFP4_G32    groups of 32 E2M1 codes along D sharing one E8M0
+ *                    exponent, w = E2M1(c)·2^(E-127) (Kimi K3 迁移到 Google TPU
+ *                    的可行性评估（v2）, section 2 模型解剖, quantisation row:
+ *                    W4 group 32 + E8M0, 4.25 bit; element encoding per the
+ *                    OCP Microscaling Formats v1.0 specification).
+ *
+ * Canonical (input) layouts, row-major:
+ *   affine codes  uint32[N][D/8]: code k of row n is bits 4(k%8)..4(k%8)+3 of
+ *                 word k/8 (lowest nibble first);
+ *   affine scale, bias  bf16[N][D/64];
+ *   MXFP4 codes   uint8[N][D/2]: code k of row n is the low nibble of byte k/2
+ *                 for even k, the high nibble for odd k;
+ *   MXFP4 E8M0    uint8[N][D/32].
+ *
+ * Conventions for every call
+ *   - Pointers are caller-owned DEVICE memory unless stated otherwise; the
+ *     library never allocates, frees or retains them.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are
+ *     asynchronous on it and return after the kernels are enqueued, except
+ *     where a call says it synchronizes.  Reading results on the host needs a
+ *     stream or event synchronization first (the non-blocking commit + explicit
+ *     wait of Kapitsa 源码拆解 02, section "C++ 代码如何提交 GPU 计算").
+ *   - Validation happens on the host before any launch; a rejected call
+ *     launches nothing and touches no memory.  Nothing aborts, throws or
+ *     exits across this interface.  QMM_E_HIP reports a HIP runtime error
+ *     (launch failure, no device); qmm_last_error() then holds the HIP text.
+ *   - Alignment (QMM_E_ALIGN otherwise): `packed` 256 bytes, x 16 bytes,
+ *     codes and routing tables 4 bytes, y, scales and biases 2 bytes.
+ *   - The kernels trust that `packed` holds a blob of this (format, n, d);
+ *     only qmm_unpack reads the header back to check it.
+ *   - Summation order is fixed per shape and launch configuration, so
+ *     repeated calls give bitwise identical results (no float atomics).
+ *   - Calls on different streams may run concurrently; the only process
+ *     state is a per-device cache of device properties.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QMM_OK = 0,
+  QMM_E_ARG = 1,          /* NULL pointer, bad enum, negative size, inconsistent argument */
+  QMM_E_SHAPE = 2,        /* D not a multiple of the group, size out of supported range */
+  QMM_E_ALIGN = 3,        /* pointer misaligned for the call */
+  QMM_E_UNSUPPORTED = 4,  /* valid request this build does not implement */
+  QMM_E_WORKSPACE = 5,    /* workspace NULL or smaller than qmm_workspace_bytes() */
+  QMM_E_HIP = 6,          /* HIP runtime error; see qmm_last_error() */
+  QMM_E_LAYOUT = 7,       /* packed blob header does not match (format, n, d, version) */
+  QMM_E_VALUE = 8         /* input value outside the format (E8M0 = 255 is NaN) */
+} qmm_status;
+
+typedef enum { QMM_AFFINE4_G64 = 1, QMM_MXFP4_G32 = 2 } qmm_format;
+
+typedef uint16_t qmm_bf16; /* raw bf16 bits */
+
+/* Supported ranges: 1 <= n <= 2^28; group <= d <= 65536 with d % group == 0;
+ * 1 <= t <= 2^24 rows for qmm_gemm. */
+
+/* Bytes of the packed device blob for a W[n, d] (a 256-byte header followed by
+ * the codes and the per-group metadata; 36 payload bytes per 64 affine
+ * weights, 17 per 32 MXFP4 weights), rounded up to 256.  0 if the shape or
+ * format is invalid.  Host only; touches no device. */
+size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
+
+/* Workspace the matmul calls need for these sizes (bytes, 0 = none).  The
+ * kernels of this build need none; callers may pass ws = NULL, ws_bytes = 0. */
+size_t qmm_workspace_bytes(qmm_format f, int64_t t, int64_t n, int64_t d);
+
+/* Pack canonical weights into the MI355X device layout.
+ *   codes   canonical codes (see above), device
+ *   scales  affine: bf16 scales [n][d/64]; MXFP4: uint8 E8M0 [n][d/32], device
+ *   biases  affine: bf16 biases [n][d/64]; MXFP4: must be NULL
+ *   packed  device buffer of qmm_packed_bytes(f, n, d) bytes, written whole
+ * A pure bit/byte permutation plus header: no arithmetic on values.  For
+ * MXFP4 the call SYNCHRONIZES `stream` to report E8M0 = 255 (NaN scale) as
+ * QMM_E_VALUE; the blob is then marked invalid.  One-time preparation, not a
+ * hot-path call. */
+qmm_status qmm_pack(qmm_format f, int64_t n, int64_t d, const void* codes, const void* scales,
+                    const void* biases, void* packed, void* stream);
+
+/* Inverse of qmm_pack (test support): rewrites the canonical arrays from a
+ * blob.  SYNCHRONIZES `stream` to check the blob header first
+ * (QMM_E_LAYOUT on a mismatch or an invalid blob). */
+qmm_status qmm_unpack(qmm_format f, int64_t n, int64_t d, const void* packed, void* codes,
+                      void* scales, void* biases, void* stream);
+
+/* Decode GEMV: y[n] = Σ_k x[k]·ŵ[n,k] for one activation row.
+ *   packed  blob from qmm_pack(f, n, d); x bf16[d]; y bf16[n] (written whole).
+ * fp32 accumulation, bf16 round-to-nearest-even output. */
+qmm_status qmm_gemv(qmm_format f, const void* packed, int64_t n, int64_t d, const qmm_bf16* x,
+                    qmm_bf16* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Prefill GEMM: Y[t][n] = Σ_k X[t][k]·ŵ[n,k].
+ *   x bf16[t][d] row-major; y bf16[t][n] row-major (written whole).
+ * t = 1 runs the GEMV kernel; t > 1 dequantizes weight tiles to bf16 and
+ * feeds bf16 MFMA with fp32 accumulation (the weight is rounded to bf16 once,
+ * as the MFMA operand). */
+qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
+                    const qmm_bf16* x, qmm_bf16* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Routed-expert grouped matmul (all experts in one launch).
+ *   packed_stack        n_experts blobs of qmm_packed_bytes(f, n, d) bytes,
+ *                       blob e at packed_stack + e·expert_stride_bytes
+ *                       (stride a multiple of 256, >= the blob size)
+ *   x                   bf16[t_x][d] activation rows
+ *   row_index           int32[m_total]: grouped row r reads x row row_index[r]
+ *   seg_expert          int32[n_seg]: expert of segment s
+ *   seg_offsets         int32[n_seg + 1]: segment s owns grouped rows
+ *                       [seg_offsets[s], seg_offsets[s+1])
+ *   max_seg_rows        host upper bound on segment sizes; it selects the
+ *                       kernel (1 = decode GEMV path), never memory bounds
+ *   y                   bf16[m_total][n]: row r = x[row_index[r]]·Ŵ_eᵀ
+ * row_index, seg_expert, seg_offsets are device arrays; n_seg, m_total,
+ * max_seg_rows, t_x, n_experts are host scalars.  The kernels clamp segment
+ * bounds to [0, m_total] and never read outside x or the stack: a segment
+ * whose expert is outside [0, n_experts), or a row whose row_index is outside
+ * [0, t_x), gets NaN outputs.  Rows covered by no segment are not written. */
+qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expert_stride_bytes,
+                            int32_t n_experts, int64_t n, int64_t d, const qmm_bf16* x,
+                            int64_t t_x, const int32_t* row_index, const int32_t* seg_expert,
+                            const int32_t* seg_offsets, int32_t n_seg, int32_t m_total,
+                            int32_t max_seg_rows, qmm_bf16* y, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Static description of a status code. */
+const char* qmm_status_string(qmm_status s);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* qmm_last_error(void);
+
+/* Layout version stamped into packed blobs. */
+uint32_t qmm_layout_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

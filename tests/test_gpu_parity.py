@@ -1,0 +1,413 @@
+"""GPU parity: every libqmm kernel against the fp64 CPU oracle (needs an MI355X).
+
+Acceptance per element: |y_gpu − y| ≤ 2e-3·Σ|x·ŵ| + 1e-5 with the bf16 output
+widened exactly; integer-exact inputs must match bit for bit; outputs start as
+a NaN sentinel so an unwritten element fails.  All inputs come from the seeded
+generator; nothing expected is produced by the HIP path itself.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import bit_weight_quantized_amd as qmm  # noqa: E402
+
+A, M = qmm.QMM_AFFINE4_G64, qmm.QMM_MXFP4_G32
+NAN16 = 0x7FC0
+DEV = "cuda"
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qmm.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host_u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def nan_out(*shape):
+    return torch.full(shape, NAN16, dtype=torch.int16, device=DEV)
+
+
+def pack_affine(w):
+    packed = torch.empty(qmm.qmm_packed_bytes(A, w.n, w.d), dtype=torch.uint8, device=DEV)
+    qmm.qmm_pack(A, w.n, w.d, dev(w.codes), dev(w.scale), dev(w.bias), packed)
+    return packed
+
+
+def pack_mxfp4(w):
+    packed = torch.empty(qmm.qmm_packed_bytes(M, w.n, w.d), dtype=torch.uint8, device=DEV)
+    qmm.qmm_pack(M, w.n, w.d, dev(w.codes), dev(w.e8m0), None, packed)
+    return packed
+
+
+def rand_mxfp4(seed, n, d, e_lo=118, e_count=9):
+    return synth.mxfp4_weights(seed, n, d, synth.S_GU_CODES, synth.S_GU_E8M0, 0, e_lo, e_count)
+
+
+def assert_parity(y_bits, y_ref, a_ref, what):
+    r = oracle.check(y_bits, y_ref, a_ref)
+    say(what, {k: r[k] for k in ("n", "n_fail", "max_ratio", "max_abs")})
+    assert r["ok"], (what, r)
+
+
+# ---------------------------------------------------------------------------
+# pack / unpack
+# ---------------------------------------------------------------------------
+
+def test_roundtrip_affine():
+    say("roundtrip affine 37x192")
+    w = synth.affine_weights(11, 37, 192)
+    w.codes[0, :] = 0
+    w.codes[1, :] = 0xFFFFFFFF
+    p = pack_affine(w)
+    c, s, b = (torch.empty_like(dev(w.codes)), torch.empty_like(dev(w.scale)), torch.empty_like(dev(w.bias)))
+    qmm.qmm_unpack(A, w.n, w.d, p, c, s, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.cpu().numpy().view(np.uint32), w.codes)
+    assert np.array_equal(host_u16(s), w.scale) and np.array_equal(host_u16(b), w.bias)
+    # header: the payload follows 256 header bytes and is 36 B per 64 weights
+    assert p.numel() >= 256 + 37 * 192 * 36 // 64
+
+
+def test_roundtrip_mxfp4_all_codes_and_scales():
+    say("roundtrip mxfp4 33x96")
+    w = rand_mxfp4(12, 33, 96)
+    w.e8m0.reshape(-1)[:] = np.arange(w.e8m0.size) % 255        # every E8M0 in 0..254
+    w.codes[0, :] = (np.arange(48) * 0x11 % 256).astype(np.uint8)
+    p = pack_mxfp4(w)
+    c, e = torch.empty_like(dev(w.codes)), torch.empty_like(dev(w.e8m0))
+    qmm.qmm_unpack(M, w.n, w.d, p, c, e, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.cpu().numpy(), w.codes) and np.array_equal(e.cpu().numpy(), w.e8m0)
+
+
+def test_pack_rejects_nan_scale_and_unpack_checks_header():
+    say("pack NaN scale")
+    w = rand_mxfp4(13, 8, 64)
+    w.e8m0[3, 1] = 255
+    with pytest.raises(qmm.QmmError) as ei:
+        pack_mxfp4(w)
+    assert ei.value.status == 8
+    w2 = synth.affine_weights(14, 16, 128)
+    p = pack_affine(w2)
+    c = torch.empty(16 * 16, dtype=torch.int32, device=DEV)
+    s = torch.empty(16 * 2, dtype=torch.int16, device=DEV)
+    with pytest.raises(qmm.QmmError) as ei:
+        qmm.qmm_unpack(A, 16, 64, p, c, s, s)                        # wrong d
+    assert ei.value.status == 7
+    with pytest.raises(qmm.QmmError) as ei:
+        qmm.qmm_unpack(M, 16, 128, p, c, s, None)                    # wrong format
+    assert ei.value.status == 7
+
+
+def test_gpu_generator_matches_host():
+    say("generator gpu vs host")
+    import synth.gpu as sg
+    t = torch.empty(1001, dtype=torch.uint8, device=DEV)
+    sg.code_bytes(1003, synth.S_GU_CODES, 17, t, start_byte=13)
+    assert np.array_equal(t.cpu().numpy(), synth.code_bytes(1003, synth.S_GU_CODES, 17, 1001, start_byte=13))
+    e = torch.empty(777, dtype=torch.uint8, device=DEV)
+    sg.small_int_u8(1003, synth.S_GU_E8M0, 17, e, 118, 9, start=5)
+    assert np.array_equal(e.cpu().numpy(), synth.small_int(1003, synth.S_GU_E8M0, 17, 777, 118, 9, start=5))
+
+
+# ---------------------------------------------------------------------------
+# GEMV
+# ---------------------------------------------------------------------------
+
+def run_gemv(fmt, packed, w, x_bits):
+    y = nan_out(w.n)
+    if fmt == A:
+        qmm.qmm_gemv(A, packed, w.n, w.d, dev(x_bits), y)
+    else:
+        qmm.qmm_gemv(M, packed, w.n, w.d, dev(x_bits), y)
+    torch.cuda.synchronize()
+    return host_u16(y)
+
+
+@pytest.mark.parametrize("n,d", [(512, 256), (1, 64), (3, 64), (37, 192), (100, 576), (257, 1088),
+                                 (1000, 5120), (5, 8704), (300, 65536)])
+def test_gemv_affine(n, d):
+    say("gemv affine", n, d)
+    w = synth.affine_weights(1000 + n, n, d)
+    x = synth.activations(2000 + d, synth.S_X, 1, d)
+    y = run_gemv(A, pack_affine(w), w, x[0])
+    yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    assert_parity(y, yr[0], ar[0], f"gemv affine {n}x{d}")
+
+
+def test_gemv_affine_decode_workload_full():
+    """13824 x 5120, every output against the oracle."""
+    say("gemv affine 13824x5120 full")
+    cfg = synth.CONFIGS[1]
+    w = synth.affine_weights(synth.seed_of(1), cfg["n"], cfg["d"])
+    x = synth.activations(synth.seed_of(1), synth.S_X, 1, cfg["d"])
+    y = run_gemv(A, pack_affine(w), w, x[0])
+    yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    assert_parity(y, yr[0], ar[0], "gemv affine 13824x5120")
+
+
+@pytest.mark.parametrize("n,d,elo,ecount", [(1, 32, 118, 9), (7, 96, 118, 9), (100, 3584, 118, 9),
+                                            (33, 3072, 118, 9), (64, 512, 1, 200), (9, 1056, 100, 60)])
+def test_gemv_mxfp4(n, d, elo, ecount):
+    say("gemv mxfp4", n, d, elo, ecount)
+    w = rand_mxfp4(3000 + n, n, d, elo, ecount)
+    x = synth.activations(4000 + d, synth.S_X, 1, d)
+    y = run_gemv(M, pack_mxfp4(w), w, x[0])
+    yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    # E8M0 up to 200 keeps every product and sum inside the fp32/bf16 range;
+    # E8M0 = 1 exercises the smallest normal scale 2^-126
+    assert_parity(y, yr[0], ar[0], f"gemv mxfp4 {n}x{d} E in [{elo}, {elo + ecount})")
+
+
+def integer_affine(seed, n, d):
+    w = synth.affine_weights(seed, n, d)
+    w.scale[:] = 0x3F80      # 1.0
+    w.bias[:] = 0            # 0.0
+    return w
+
+
+def test_gemv_integer_exact():
+    say("gemv integer exact")
+    rng = np.random.default_rng(5)
+    n, d = 300, 1088
+    w = integer_affine(21, n, d)
+    xi = rng.integers(-3, 4, size=(1, d)).astype(float)
+    x = synth.bf16_bits(xi)
+    yr, _ = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    # every partial sum is an integer below 2^24, exact in fp32, so both sides
+    # round the same exact integer to bf16
+    assert np.all(np.abs(yr) < 2 ** 24)
+    y = run_gemv(A, pack_affine(w), w, x[0])
+    assert np.array_equal(y, oracle.f64_to_bf16_bits(yr[0]))
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+
+def run_gemm(fmt, packed, n, d, x_bits):
+    t = x_bits.shape[0]
+    y = nan_out(t, n)
+    qmm.qmm_gemm(fmt, packed, t, n, d, dev(x_bits), y)
+    torch.cuda.synchronize()
+    return host_u16(y)
+
+
+@pytest.mark.parametrize("t,n,d", [(2, 5, 64), (3, 300, 320), (130, 257, 576), (129, 512, 1024),
+                                   (300, 520, 640), (257, 256, 256), (513, 100, 5120)])
+def test_gemm_affine(t, n, d):
+    say("gemm affine", t, n, d)
+    w = synth.affine_weights(5000 + n, n, d)
+    x = synth.activations(6000 + t, synth.S_X, t, d)
+    y = run_gemm(A, pack_affine(w), n, d, x)
+    yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    assert_parity(y, yr, ar, f"gemm affine {t}x{n}x{d}")
+
+
+@pytest.mark.parametrize("t,n,d,elo,ecount", [(2, 5, 32, 118, 9), (3, 300, 96, 118, 9),
+                                              (130, 257, 3584, 118, 9), (257, 300, 3072, 118, 9),
+                                              (64, 70, 1056, 100, 50)])
+def test_gemm_mxfp4(t, n, d, elo, ecount):
+    say("gemm mxfp4", t, n, d)
+    w = rand_mxfp4(7000 + n, n, d, elo, ecount)
+    x = synth.activations(8000 + t, synth.S_X, t, d)
+    y = run_gemm(M, pack_mxfp4(w), n, d, x)
+    yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    assert_parity(y, yr, ar, f"gemm mxfp4 {t}x{n}x{d}")
+
+
+def test_gemm_integer_exact():
+    say("gemm integer exact")
+    rng = np.random.default_rng(6)
+    t, n, d = 260, 300, 1024
+    w = integer_affine(22, n, d)
+    x = synth.bf16_bits(rng.integers(-3, 4, size=(t, d)).astype(float))
+    yr, _ = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    assert np.all(np.abs(yr) < 2 ** 24)
+    y = run_gemm(A, pack_affine(w), n, d, x)
+    assert np.array_equal(y, oracle.f64_to_bf16_bits(yr))
+
+
+def test_gemm_prefill_workload_sampled():
+    """2048 x 5120 x 13824 in the benchmark's launch configuration; the oracle
+    evaluates 3000 sampled outputs one by one (all tile corners included)."""
+    say("gemm affine 2048x13824x5120 sampled")
+    cfg = synth.CONFIGS[2]
+    t, n, d = cfg["t"], cfg["n"], cfg["d"]
+    w = synth.affine_weights(synth.seed_of(2), n, d)
+    x = synth.activations(synth.seed_of(2), synth.S_X, t, d)
+    y = run_gemm(A, pack_affine(w), n, d, x)
+    assert not np.any(y == NAN16)
+    rng = np.random.default_rng(7)
+    pairs = {(int(a), int(b)) for a, b in zip(rng.integers(0, t, 2600), rng.integers(0, n, 2600))}
+    for tt in (0, 127, 128, 255, 256, 2047):
+        for nn in (0, 31, 32, 63, 64, 255, 256, 13823):
+            pairs.add((tt, nn))
+    pairs = sorted(pairs)
+    wrow = lambda j: oracle.dequant_affine(w.codes[j:j + 1], w.scale[j:j + 1], w.bias[j:j + 1])[0]
+    yr, ar = oracle.sampled(x, wrow, pairs)
+    got = np.array([y[tt, nn] for tt, nn in pairs], np.uint16)
+    assert_parity(got, yr, ar, "gemm 2048x13824x5120 sampled")
+
+
+# ---------------------------------------------------------------------------
+# Grouped (routed experts)
+# ---------------------------------------------------------------------------
+
+def stack(fmt, weights):
+    size = qmm.qmm_packed_bytes(fmt, weights[0].n, weights[0].d)
+    out = torch.empty(size * len(weights), dtype=torch.uint8, device=DEV)
+    for e, w in enumerate(weights):
+        p = pack_affine(w) if fmt == A else pack_mxfp4(w)
+        out[e * size:(e + 1) * size].copy_(p)
+    return out, size
+
+
+def run_grouped(fmt, stk, stride, n_exp, n, d, x_bits, seg_expert, seg_offsets, row_index, max_rows):
+    m_total = int(seg_offsets[-1])
+    y = nan_out(m_total, n)
+    qmm.qmm_grouped_gemm(fmt, stk, stride, n_exp, n, d, dev(x_bits), x_bits.shape[0],
+                         dev(np.asarray(row_index, np.int32)), dev(np.asarray(seg_expert, np.int32)),
+                         dev(np.asarray(seg_offsets, np.int32)), len(seg_expert), m_total, max_rows, y)
+    torch.cuda.synchronize()
+    return host_u16(y)
+
+
+@pytest.mark.parametrize("fmt", [A, M])
+def test_grouped_gemm_small(fmt):
+    say("grouped small", fmt)
+    n, d, n_exp, t = 300, 256, 5, 140
+    ws = [synth.affine_weights(900 + e, n, d) if fmt == A else rand_mxfp4(900 + e, n, d) for e in range(n_exp)]
+    stk, size = stack(fmt, ws)
+    x = synth.activations(901, synth.S_X, t, d)
+    sizes = [0, 1, 17, 64, 65, 130]
+    seg_expert = [4, 0, 2, 1, 3, 2]
+    seg_offsets = np.concatenate([[0], np.cumsum(sizes)])
+    rng = np.random.default_rng(8)
+    row_index = np.concatenate([np.sort(rng.choice(t, s, replace=False)) for s in sizes]).astype(np.int32)
+    deq = (lambda e: oracle.dequant_affine(ws[e].codes, ws[e].scale, ws[e].bias)) if fmt == A else \
+          (lambda e: oracle.dequant_mxfp4(ws[e].codes, ws[e].e8m0))
+    yr, ar = oracle.grouped(x, row_index, seg_expert, seg_offsets, deq)
+    for max_rows in (max(sizes), 1):      # MFMA path, then the GEMV path on the same table
+        y = run_grouped(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, max_rows)
+        assert_parity(y, yr, ar, f"grouped fmt={fmt} max_rows={max_rows}")
+
+
+def test_grouped_invalid_entries_give_nan():
+    say("grouped invalid entries")
+    n, d, n_exp, t = 40, 128, 2, 8
+    ws = [rand_mxfp4(950 + e, n, d) for e in range(n_exp)]
+    stk, size = stack(M, ws)
+    x = synth.activations(951, synth.S_X, t, d)
+    seg_expert = [0, 7, 1]                  # expert 7 does not exist
+    seg_offsets = [0, 2, 4, 6]
+    row_index = [1, 2, 3, 4, 5, 99]         # row 99 does not exist
+    for max_rows in (2, 1):
+        y = run_grouped(M, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, max_rows)
+        yf = oracle.bf16_to_f64(y)
+        assert np.all(np.isnan(yf[2:4])) and np.all(np.isnan(yf[5]))
+        assert np.all(np.isfinite(yf[0:2])) and np.all(np.isfinite(yf[4]))
+
+
+def make_expert_stack(which, n_exp):
+    import synth.gpu as sg
+    n, d = (6144, 3584) if which == "gate_up" else (3584, 3072)
+    size = qmm.qmm_packed_bytes(M, n, d)
+    out = torch.empty(size * n_exp, dtype=torch.uint8, device=DEV)
+    sg.expert_stack(synth.seed_of(3), which, n_exp,
+                    lambda c, e, ptr: qmm.qmm_pack(M, n, d, c, e, None, ptr), size, size, out)
+    return out, size
+
+
+@pytest.fixture(scope="module")
+def expert_stacks():
+    say("building 896-expert stacks on the GPU")
+    gu = make_expert_stack("gate_up", 896)
+    dn = make_expert_stack("down", 896)
+    torch.cuda.synchronize()
+    yield gu, dn
+    del gu, dn
+    torch.cuda.empty_cache()
+
+
+def test_moe_decode_workload_full(expert_stacks):
+    """16 routed experts, gate_up on x then down on a seeded z per expert,
+    every output against the oracle."""
+    say("moe decode grouped gemv full")
+    (gu, gsz), (dn, dsz) = expert_stacks
+    seed = synth.seed_of(3)
+    experts = synth.draw_experts(seed, 16, 896, 0)
+    x = synth.activations(seed, synth.S_X, 1, 3584)
+    z = synth.activations(seed, synth.S_Z, 16, 3072)
+    seg_offsets = np.arange(17)
+    y1 = run_grouped(M, gu, gsz, 896, 6144, 3584, x, experts, seg_offsets, np.zeros(16, np.int32), 1)
+    y2 = run_grouped(M, dn, dsz, 896, 3584, 3072, z, experts, seg_offsets, np.arange(16), 1)
+    for i, e in enumerate(experts):
+        g = synth.expert_gate_up(seed, int(e))
+        yr, ar = oracle.gemm_mxfp4(x, g.codes, g.e8m0)
+        assert_parity(y1[i], yr[0], ar[0], f"gate_up expert {e}")
+        dw = synth.expert_down(seed, int(e))
+        yr, ar = oracle.gemm_mxfp4(z[i:i + 1], dw.codes, dw.e8m0)
+        assert_parity(y2[i], yr[0], ar[0], f"down expert {e}")
+
+
+def test_moe_prefill_workload_sampled(expert_stacks):
+    """512 tokens routed top-16 over 896 experts, one grouped call; the oracle
+    checks every row and column of 10 segments (largest, smallest, random)."""
+    say("moe prefill grouped gemm sampled")
+    (gu, gsz), _ = expert_stacks
+    seed = synth.seed_of(4)
+    xb, rb, bias = synth.router_inputs(seed)
+    rt = synth.route(xb, rb, bias)
+    # config 4 reuses config 3's expert weights
+    y = run_grouped(M, gu, gsz, 896, 6144, 3584, xb, rt.seg_expert, rt.seg_offsets, rt.row_index,
+                    rt.max_seg_rows)
+    assert not np.any(y == NAN16)
+    sizes = np.diff(rt.seg_offsets)
+    rng = np.random.default_rng(9)
+    pick = sorted({int(np.argmax(sizes)), int(np.argmin(sizes)), *rng.choice(rt.n_seg, 8, replace=False).tolist()})
+    for s in pick:
+        r0, r1 = int(rt.seg_offsets[s]), int(rt.seg_offsets[s + 1])
+        g = synth.expert_gate_up(synth.seed_of(3), int(rt.seg_expert[s]))
+        yr, ar = oracle.gemm_mxfp4(xb[rt.row_index[r0:r1]], g.codes, g.e8m0)
+        assert_parity(y[r0:r1], yr, ar, f"segment {s} expert {rt.seg_expert[s]} rows {r1 - r0}")
+
+
+def test_bitwise_deterministic():
+    say("determinism")
+    w = synth.affine_weights(31, 1000, 5120)
+    p = pack_affine(w)
+    x = synth.activations(32, synth.S_X, 300, 5120)
+    a = run_gemm(A, p, 1000, 5120, x)
+    b = run_gemm(A, p, 1000, 5120, x)
+    assert np.array_equal(a, b)
+    a = run_gemv(A, p, w, x[0])
+    b = run_gemv(A, p, w, x[0])
+    assert np.array_equal(a, b)
