@@ -13,8 +13,9 @@ in HBM:
 Weights of the decode row rotate over enough packed copies (> 2x the 256 MB
 Infinity Cache) that every launch reads HBM, not the cache.
 
-Each kernel launch is bracketed by HIP events on the stream it runs on; its
-average duration gives achieved GB/s (bytes the algorithm must move: packed
+Each kernel launch gets HIP start/stop events stamped by its own dispatch
+(qmm_profile_next -> hipExtLaunchKernel, on the stream it runs on); their
+average interval, the kernel's execution time, gives achieved GB/s (bytes the algorithm must move: packed
 weights + activations + outputs) or TFLOP/s against the chip's peaks.  The
 headline is the decode GEMV's GB/s.  rank 0 prints one JSON line.
 """
@@ -37,6 +38,47 @@ BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
 METRIC = "decode GEMV HBM GB/s (% of peak) + prefill GEMM TFLOP/s (% MFMA peak)"
 
 
+class HipEvents:
+    """Raw hipEvent_t handles (libamdhip64 through ctypes), so a launch can have
+    its start/stop stamped by the dispatch itself (qmm_profile_next)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.events = []
+
+    def new(self) -> int:
+        h = self.ct.c_void_p()
+        err = self.hip.hipEventCreate(self.ct.byref(h))
+        if err:
+            raise RuntimeError(f"hipEventCreate: {err}")
+        self.events.append(h.value)
+        return h.value
+
+    def record(self, ev: int, stream: int) -> None:
+        err = self.hip.hipEventRecord(self.ct.c_void_p(ev), self.ct.c_void_p(stream))
+        if err:
+            raise RuntimeError(f"hipEventRecord: {err}")
+
+    def ms(self, a: int, b: int) -> float:
+        out = self.ct.c_float()
+        err = self.hip.hipEventElapsedTime(self.ct.byref(out), self.ct.c_void_p(a), self.ct.c_void_p(b))
+        if err:
+            raise RuntimeError(f"hipEventElapsedTime: {err}")
+        return out.value
+
+    def close(self):
+        for h in self.events:
+            self.hip.hipEventDestroy(self.ct.c_void_p(h))
+        self.events = []
+
+
 def kernel_sources_hash(files) -> str:
     h = hashlib.sha256()
     for f in files:
@@ -45,7 +87,8 @@ def kernel_sources_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-GEMV_SOURCES = ["bit_weight_quantized_amd/csrc/qmm_gemv.hip", "bit_weight_quantized_amd/csrc/qmm_device.h"]
+GEMV_SOURCES = ["bit_weight_quantized_amd/csrc/qmm_gemv.hip", "bit_weight_quantized_amd/csrc/qmm_device.h",
+                "bit_weight_quantized_amd/csrc/qmm_internal.h", "bit_weight_quantized_amd/csrc/qmm_launch.h"]
 
 
 def recorded_traffic(kernel_hash: str):
@@ -69,7 +112,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotate", type=int, default=24, help="packed copies of the decode weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rows", default="decode,prefill,moe_dec,moe_pre")
+    ap.add_argument("--rows", default="decode,prefill,moe_dec,moe_pre",
+                    help="comma list of decode, prefill, moe_dec, moe_pre; 'copy' adds a plain "
+                         "256 MiB device copy used to calibrate HBM byte counters")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -184,10 +229,15 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
 
+    if "copy" in rows:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        work["copy"] = [(lambda s: dst.copy_(src), "copy_256MiB", 2 * src.numel(), 0.0)]
+
     launches = [(row, fn, name, nb, fl) for row in rows for (fn, name, nb, fl) in work[row]]
     stream = torch.cuda.current_stream()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in launches] for _ in range(args.steps)]
+    hev = HipEvents()
+    ev = [[(hev.new(), hev.new()) for _ in launches] for _ in range(args.steps)]
 
     for s in range(args.warmup):
         for (_, fn, _, _, _) in launches:
@@ -200,10 +250,14 @@ def main(argv=None) -> int:
     wall0 = time.perf_counter()
     t0.record(stream)
     for s in range(args.steps):
-        for i, (_, fn, _, _, _) in enumerate(launches):
-            ev[s][i][0].record(stream)
-            fn(s)
-            ev[s][i][1].record(stream)
+        for i, (row, fn, _, _, _) in enumerate(launches):
+            if row == "copy":            # not a libqmm launch: plain stream events
+                hev.record(ev[s][i][0], stream.cuda_stream)
+                fn(s)
+                hev.record(ev[s][i][1], stream.cuda_stream)
+            else:
+                qmm.qmm_profile_next(ev[s][i][0], ev[s][i][1])   # stamped by the kernel's dispatch
+                fn(s)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -211,7 +265,7 @@ def main(argv=None) -> int:
 
     results = {}
     for i, (row, fn, name, nb, fl) in enumerate(launches):
-        us = np.array([ev[s][i][0].elapsed_time(ev[s][i][1]) * 1e3 for s in range(args.steps)])
+        us = np.array([hev.ms(ev[s][i][0], ev[s][i][1]) * 1e3 for s in range(args.steps)])
         mean = float(us.mean())
         results[name] = dict(row=row, us_mean=round(mean, 3), us_median=round(float(np.median(us)), 3),
                              us_p10=round(float(np.percentile(us, 10)), 3),
@@ -221,6 +275,7 @@ def main(argv=None) -> int:
                              hbm_frac=round(nb / mean / 1e3 / HBM_PEAK_GBPS, 4),
                              mfma_frac=round(fl / mean / 1e6 / BF16_PEAK_TFLOPS, 4))
 
+    hev.close()
     out = {
         "metric": METRIC,
         "value": None, "unit": "GB/s",
@@ -231,7 +286,7 @@ def main(argv=None) -> int:
         "config": {"workload": synth.CONFIGS[1]["name"], "t": 1, "d": d1, "n": n1,
                    "format": "affine4_g64", "rotation_copies": args.rotate,
                    "step": "decode GEMV + prefill GEMM + MoE decode grouped GEMV x2 + MoE prefill grouped GEMM"
-                   if len(rows) == 4 else ",".join(rows)},
+                   if rows == ["decode", "prefill", "moe_dec", "moe_pre"] else ",".join(rows)},
     }
     if "gemv" in results:
         g = results["gemv"]

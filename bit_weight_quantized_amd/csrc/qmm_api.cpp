@@ -10,6 +10,7 @@
 namespace {
 
 thread_local char g_last_error[256] = "";
+thread_local qmm::ProfileEvents g_profile = {nullptr, nullptr};
 
 qmm_status fail(qmm_status s, const char* what) {
   snprintf(g_last_error, sizeof(g_last_error), "%s", what);
@@ -41,7 +42,18 @@ qmm_status check_ws(int f, int64_t t, int64_t n, int64_t d, const void* ws, size
 
 }  // namespace
 
+qmm::ProfileEvents qmm::take_profile_events() {
+  const ProfileEvents pe = g_profile;
+  g_profile = {nullptr, nullptr};
+  return pe;
+}
+
 extern "C" {
+
+qmm_status qmm_profile_next(void* start_event, void* stop_event) {
+  g_profile = {start_event, stop_event};
+  return QMM_OK;
+}
 
 size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d) {
   qmm::Layout l;

@@ -63,34 +63,42 @@ __device__ __forceinline__ float sum16(float v) {
 // ---------------------------------------------------------------------------
 constexpr uint32_t kMagic128x2 = 0x43004300u;
 
+// (a & mask) | magic in one VOP3 instruction.  gfx9 VOP3 cannot encode a
+// 32-bit literal, so left to itself the compiler splits this into an AND and
+// an OR with literals; here the mask sits in an SGPR and the magic in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+  return r;
+}
+
+// Four independent accumulator chains (one per word) keep the dot unit busy
+// without relying on other waves to hide its latency.
 __device__ __forceinline__ float affine_dot32(const u32x4_t w, const uint32_t* xp) {
-  float a0 = 0.f, a1 = 0.f;
+  const uint32_t mask = 0x000F000Fu, magic = kMagic128x2;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t v = w[i];
-    float& acc = (i & 1) ? a1 : a0;
-    acc = dot2_bf16((v & 0x000F000Fu) | kMagic128x2, xp[4 * i + 0], acc);
-    acc = dot2_bf16(((v >> 4) & 0x000F000Fu) | kMagic128x2, xp[4 * i + 1], acc);
-    acc = dot2_bf16(((v >> 8) & 0x000F000Fu) | kMagic128x2, xp[4 * i + 2], acc);
-    acc = dot2_bf16(((v >> 12) & 0x000F000Fu) | kMagic128x2, xp[4 * i + 3], acc);
-  }
-  return a0 + a1;
+  for (int sh = 0; sh < 4; ++sh)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc[i] = dot2_bf16(and_or(w[i] >> (4 * sh), mask, magic), xp[4 * i + sh], acc[i]);
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // MXFP4: 32 codes (16 bytes) against 32 activations, E2M1 values unscaled
 // (the conversion's scale operand is 1.0); the caller applies 2^(E-127).
 __device__ __forceinline__ float mxfp4_dot32(const u32x4_t w, const uint32_t* xp) {
-  float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t v = w[i];
-    float& acc = (i & 1) ? a1 : a0;
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0)), xp[4 * i + 0], acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1)), xp[4 * i + 1], acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2)), xp[4 * i + 2], acc);
-    acc = dot2_bf16(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3)), xp[4 * i + 3], acc);
-  }
-  return a0 + a1;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#define QMM_FP4_STEP(SEL)                                                                 \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i) acc[i] = dot2_bf16(                       \
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], 1.0f, SEL)), \
+      xp[4 * i + SEL], acc[i]);
+  QMM_FP4_STEP(0)
+  QMM_FP4_STEP(1)
+  QMM_FP4_STEP(2)
+  QMM_FP4_STEP(3)
+#undef QMM_FP4_STEP
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -134,6 +142,21 @@ __device__ __forceinline__ u32x4_t mxfp4_word_to_bf16x8(uint32_t v, float scale)
 
 __device__ __forceinline__ u32x4_t load16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Raw buffer resource over [base, base + bytes): loads take a 32-bit byte
+// offset, and any dword outside the range reads as zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, int(off), 0, 0);
 }
 
 }  // namespace qmm

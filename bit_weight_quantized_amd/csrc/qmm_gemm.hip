@@ -25,6 +25,7 @@
 
 #include "qmm_device.h"
 #include "qmm_internal.h"
+#include "qmm_launch.h"
 
 namespace qmm {
 namespace {
@@ -43,11 +44,17 @@ __device__ __forceinline__ void dequant_chunk(const u32x4_t w, uint32_t m, u32x4
   }
 }
 
+// Codes [k, k + 32) of weight row `col` (one 16-byte chunk) and the metadata
+// of their group, from the K-slabbed layout (qmm_internal.h).
 template <int FMT>
-__device__ __forceinline__ uint32_t load_meta(const uint8_t* meta, int64_t col, int groups, int k) {
+__device__ __forceinline__ void load_chunk(const uint8_t* codes, const uint8_t* meta,
+                                           const Slabs& L, int64_t col, int k, u32x4_t& w,
+                                           uint32_t& m) {
+  w = load16(codes + L.code_byte(col, k));
   if (FMT == QMM_AFFINE4_G64)
-    return reinterpret_cast<const uint32_t*>(meta)[col * groups + k / 64];
-  return meta[col * groups + k / 32];
+    m = *reinterpret_cast<const uint32_t*>(meta + L.meta_byte(col, k));
+  else
+    m = meta[L.meta_byte(col, k)];
 }
 
 // ---------------------------------------------------------------------------
@@ -77,8 +84,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   const int tm = tile / tiles_n, tn = tile % tiles_n;
   const int m0 = tm * WM, n0 = tn * 256;
 
-  const int64_t row_bytes = d / 2;
-  const int groups = FMT == QMM_AFFINE4_G64 ? d / 64 : d / 32;
+  const Slabs L{n, d, FMT};
   const int nk = (d + 63) / 64;
 
   // this lane's two weight columns
@@ -114,8 +120,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       if (col_ok[cb] && k < d) {
-        wreg[cb] = load16(codes + col[cb] * row_bytes + k / 2);
-        mreg[cb] = load_meta<FMT>(meta, col[cb], groups, k);
+        load_chunk<FMT>(codes, meta, L, col[cb], k, wreg[cb], mreg[cb]);
       } else {
         wreg[cb] = u32x4_t{0, 0, 0, 0};
         mreg[cb] = 0;
@@ -210,8 +215,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
   const uint8_t* codes = blob + codes_off;
   const uint8_t* meta = blob + meta_off;
 
-  const int64_t row_bytes = d / 2;
-  const int groups = FMT == QMM_AFFINE4_G64 ? d / 64 : d / 32;
+  const Slabs L{n, d, FMT};
   const int nk = (d + 127) / 128;
 
   int64_t col[4];
@@ -258,8 +262,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         if (col_ok[cb] && k < d) {
-          wreg[cb] = load16(codes + col[cb] * row_bytes + k / 2);
-          mreg[cb] = load_meta<FMT>(meta, col[cb], groups, k);
+          load_chunk<FMT>(codes, meta, L, col[cb], k, wreg[cb], mreg[cb]);
         } else {
           wreg[cb] = u32x4_t{0, 0, 0, 0};
           mreg[cb] = 0;
@@ -344,19 +347,19 @@ int launch_gemm(const GemmArgs& a, void* stream) {
     const int tiles_m = (a.t + 255) / 256;
     dim3 grid(unsigned(tiles_m * tiles_n));
     if (a.f == QMM_AFFINE4_G64)
-      hipLaunchKernelGGL((gemm_kernel<QMM_AFFINE4_G64, 256>), grid, dim3(256), 0, s, codes, meta,
+      launch_kernel((gemm_kernel<QMM_AFFINE4_G64, 256>), grid, dim3(256), s, codes, meta,
                          a.t, a.n, a.d, a.x, a.y, tiles_m, tiles_n);
     else
-      hipLaunchKernelGGL((gemm_kernel<QMM_MXFP4_G32, 256>), grid, dim3(256), 0, s, codes, meta,
+      launch_kernel((gemm_kernel<QMM_MXFP4_G32, 256>), grid, dim3(256), s, codes, meta,
                          a.t, a.n, a.d, a.x, a.y, tiles_m, tiles_n);
   } else {
     const int tiles_m = (a.t + 127) / 128;
     dim3 grid(unsigned(tiles_m * tiles_n));
     if (a.f == QMM_AFFINE4_G64)
-      hipLaunchKernelGGL((gemm_kernel<QMM_AFFINE4_G64, 128>), grid, dim3(256), 0, s, codes, meta,
+      launch_kernel((gemm_kernel<QMM_AFFINE4_G64, 128>), grid, dim3(256), s, codes, meta,
                          a.t, a.n, a.d, a.x, a.y, tiles_m, tiles_n);
     else
-      hipLaunchKernelGGL((gemm_kernel<QMM_MXFP4_G32, 128>), grid, dim3(256), 0, s, codes, meta,
+      launch_kernel((gemm_kernel<QMM_MXFP4_G32, 128>), grid, dim3(256), s, codes, meta,
                          a.t, a.n, a.d, a.x, a.y, tiles_m, tiles_n);
   }
   return int(hipGetLastError());
@@ -368,11 +371,11 @@ int launch_grouped_gemm(const GemmArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid(unsigned((a.n + 255) / 256), unsigned(a.n_seg));
   if (a.f == QMM_AFFINE4_G64)
-    hipLaunchKernelGGL(grouped_gemm_kernel<QMM_AFFINE4_G64>, grid, dim3(256), 0, s, a.packed,
+    launch_kernel(grouped_gemm_kernel<QMM_AFFINE4_G64>, grid, dim3(256), s, a.packed,
                        a.expert_stride, a.n_experts, l.codes_offset, l.meta_offset, a.n, a.d, a.x,
                        a.t_x, a.row_index, a.seg_expert, a.seg_offsets, a.m_total, a.y);
   else
-    hipLaunchKernelGGL(grouped_gemm_kernel<QMM_MXFP4_G32>, grid, dim3(256), 0, s, a.packed,
+    launch_kernel(grouped_gemm_kernel<QMM_MXFP4_G32>, grid, dim3(256), s, a.packed,
                        a.expert_stride, a.n_experts, l.codes_offset, l.meta_offset, a.n, a.d, a.x,
                        a.t_x, a.row_index, a.seg_expert, a.seg_offsets, a.m_total, a.y);
   return int(hipGetLastError());

@@ -1,10 +1,20 @@
 // Internal definitions shared by the qmm library sources (host and device).
 //
-// Packed device layout, version 1 (written by qmm_pack, read by every kernel):
+// Packed device layout, version 2 (written by qmm_pack, read by every kernel):
 //
 //   [0, 256)            header (PackedHeader)
-//   [256, meta_off)     codes, row-major, d/2 bytes per row
-//   [meta_off, total)   per-group metadata, row-major
+//   [256, meta_off)     codes, K-slabbed
+//   [meta_off, total)   per-group metadata, K-slabbed
+//
+// K-slabbed: the reduction axis is cut into slabs of 512 codes (the last slab
+// may be narrower, any multiple of 32).  Slab s stores its width w_s of every
+// row, rows consecutive, and the slabs follow one another:
+//   codes of (slab s, row r) at  s·n·256 + r·w_s/2
+//   metadata of (slab s, row r)  at  s·n·mslab + r·(w_s/group)·mbytes
+// with mslab = 32 (affine: 8 groups × 4 bytes) or 16 (MXFP4: 16 groups × 1).
+// A decode GEMV sweeps the matrix slab by slab with all rows in flight, so at
+// any moment the whole GPU reads one contiguous window of memory, and each wave
+// load instruction covers 4 rows × 256 bytes = 1 KiB contiguous.
 //
 // affine codes: one uint32 per 8 codes, nibbles regrouped so that the low
 //   half-word holds the even codes and the high half-word the odd codes:
@@ -22,12 +32,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <hip/hip_runtime.h>
+
 #include "../../include/qmm.h"
 
 namespace qmm {
 
 constexpr uint32_t kMagic = 0x344D4D51u;  // "QMM4"
-constexpr uint32_t kLayoutVersion = 1;
+constexpr uint32_t kLayoutVersion = 2;
 constexpr uint32_t kFlagInvalid = 1u;     // set by qmm_pack when an E8M0 byte is 255
 constexpr int64_t kHeaderBytes = 256;
 constexpr int64_t kMaxN = int64_t(1) << 28;  // keeps every grid below 2^32 work-items
@@ -67,12 +79,52 @@ inline bool layout_of(int f, int64_t n, int64_t d, Layout* out) {
   return true;
 }
 
+// Geometry of the K-slabbed layout (bytes relative to the codes / metadata
+// section starts).
+constexpr int kSlabCodes = 512;
+
+struct Slabs {
+  int64_t n;
+  int d;
+  int fmt;
+  __host__ __device__ int count() const { return (d + kSlabCodes - 1) / kSlabCodes; }
+  __host__ __device__ int width(int s) const {
+    const int w = d - kSlabCodes * s;
+    return w < kSlabCodes ? w : kSlabCodes;
+  }
+  __host__ __device__ int64_t codes(int s, int64_t row) const {
+    return int64_t(s) * n * (kSlabCodes / 2) + row * (width(s) / 2);
+  }
+  __host__ __device__ int meta_row(int s) const {
+    return fmt == QMM_AFFINE4_G64 ? width(s) / 16 : width(s) / 32;
+  }
+  __host__ __device__ int64_t meta(int s, int64_t row) const {
+    return int64_t(s) * n * (fmt == QMM_AFFINE4_G64 ? 32 : 16) + row * meta_row(s);
+  }
+  // byte offsets of code k / of the metadata of the group holding code k
+  __host__ __device__ int64_t code_byte(int64_t row, int k) const {
+    return codes(k / kSlabCodes, row) + (k % kSlabCodes) / 2;
+  }
+  __host__ __device__ int64_t meta_byte(int64_t row, int k) const {
+    return meta(k / kSlabCodes, row) +
+           (fmt == QMM_AFFINE4_G64 ? 4 * ((k % kSlabCodes) / 64) : (k % kSlabCodes) / 32);
+  }
+};
+
 }  // namespace qmm
 
 // ---------------------------------------------------------------------------
 // Launchers implemented in the .hip files (host side, return hipError_t as int)
 // ---------------------------------------------------------------------------
 namespace qmm {
+
+// Events armed by qmm_profile_next() for the next hot-path launch on this
+// thread; take_profile_events() returns and disarms them.
+struct ProfileEvents {
+  void* start;
+  void* stop;
+};
+ProfileEvents take_profile_events();
 
 struct DevInfo {
   int cus;

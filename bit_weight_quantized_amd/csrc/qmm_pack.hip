@@ -42,47 +42,86 @@ __global__ void write_header_kernel(uint8_t* packed, PackedHeader h, int64_t gap
   if (threadIdx.x == 0) *reinterpret_cast<PackedHeader*>(packed) = h;
 }
 
+// One thread per canonical code word (8 codes) and per metadata group; the
+// word of row r holding codes [8j, 8j + 8) goes to its slab position.
 __global__ void pack_affine_kernel(const uint32_t* __restrict__ codes,
                                    const uint16_t* __restrict__ scales,
                                    const uint16_t* __restrict__ biases,
-                                   uint32_t* __restrict__ out_codes, uint32_t* __restrict__ out_meta,
-                                   int64_t n_words, int64_t n_groups) {
+                                   uint8_t* __restrict__ out_codes, uint8_t* __restrict__ out_meta,
+                                   Slabs L) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_words; i += stride) {
-    out_codes[i] = to_device_word(codes[i]);
+  const int64_t wpr = L.d / 8, gpr = L.d / 64;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < L.n * wpr; i += stride) {
+    const int64_t r = i / wpr;
+    const int k = int(i % wpr) * 8;
+    *reinterpret_cast<uint32_t*>(out_codes + L.code_byte(r, k)) = to_device_word(codes[i]);
   }
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_groups; i += stride) {
-    out_meta[i] = uint32_t(scales[i]) | (uint32_t(biases[i]) << 16);
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < L.n * gpr; i += stride) {
+    const int64_t r = i / gpr;
+    const int k = int(i % gpr) * 64;
+    *reinterpret_cast<uint32_t*>(out_meta + L.meta_byte(r, k)) =
+        uint32_t(scales[i]) | (uint32_t(biases[i]) << 16);
   }
 }
 
-__global__ void unpack_affine_kernel(const uint32_t* __restrict__ in_codes,
-                                     const uint32_t* __restrict__ in_meta, uint32_t* __restrict__ codes,
+__global__ void unpack_affine_kernel(const uint8_t* __restrict__ in_codes,
+                                     const uint8_t* __restrict__ in_meta, uint32_t* __restrict__ codes,
                                      uint16_t* __restrict__ scales, uint16_t* __restrict__ biases,
-                                     int64_t n_words, int64_t n_groups) {
+                                     Slabs L) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_words; i += stride) {
-    codes[i] = from_device_word(in_codes[i]);
+  const int64_t wpr = L.d / 8, gpr = L.d / 64;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < L.n * wpr; i += stride) {
+    const int64_t r = i / wpr;
+    const int k = int(i % wpr) * 8;
+    codes[i] = from_device_word(*reinterpret_cast<const uint32_t*>(in_codes + L.code_byte(r, k)));
   }
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_groups; i += stride) {
-    const uint32_t m = in_meta[i];
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < L.n * gpr; i += stride) {
+    const int64_t r = i / gpr;
+    const int k = int(i % gpr) * 64;
+    const uint32_t m = *reinterpret_cast<const uint32_t*>(in_meta + L.meta_byte(r, k));
     scales[i] = uint16_t(m & 0xFFFFu);
     biases[i] = uint16_t(m >> 16);
   }
 }
 
-// MXFP4 codes are stored in canonical byte order; the E8M0 bytes are copied
-// and any 255 (NaN scale) flags the blob invalid.
-__global__ void pack_mxfp4_meta_kernel(const uint8_t* __restrict__ e8m0, uint8_t* __restrict__ out,
-                                       int64_t count, uint32_t* __restrict__ flags) {
+// MXFP4 codes keep their canonical byte order and only move to their slab
+// position (16-byte pieces: 32 codes, one group); the E8M0 bytes move the same
+// way, and any 255 (NaN scale) flags the blob invalid.
+__global__ void pack_mxfp4_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ e8m0,
+                                  uint8_t* __restrict__ out_codes, uint8_t* __restrict__ out_meta,
+                                  Slabs L, uint32_t* __restrict__ flags) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  const int64_t gpr = L.d / 32;
   bool bad = false;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < count; i += stride) {
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < L.n * gpr; i += stride) {
+    const int64_t r = i / gpr;
+    const int k = int(i % gpr) * 32;
+    // the canonical array is only guaranteed 4-byte aligned
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(codes) + 4 * i;
+    *reinterpret_cast<u32x4_t*>(out_codes + L.code_byte(r, k)) = u32x4_t{src[0], src[1], src[2], src[3]};
     const uint8_t e = e8m0[i];
     bad |= (e == 255);
-    out[i] = e;
+    out_meta[L.meta_byte(r, k)] = e;
   }
   if (bad) atomicOr(flags, kFlagInvalid);
+}
+
+__global__ void unpack_mxfp4_kernel(const uint8_t* __restrict__ in_codes,
+                                    const uint8_t* __restrict__ in_meta, uint8_t* __restrict__ codes,
+                                    uint8_t* __restrict__ e8m0, Slabs L) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  const int64_t gpr = L.d / 32;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < L.n * gpr; i += stride) {
+    const int64_t r = i / gpr;
+    const int k = int(i % gpr) * 32;
+    const u32x4_t v = load16(in_codes + L.code_byte(r, k));
+    uint32_t* dst = reinterpret_cast<uint32_t*>(codes) + 4 * i;
+    dst[0] = v[0];
+    dst[1] = v[1];
+    dst[2] = v[2];
+    dst[3] = v[3];
+    e8m0[i] = in_meta[L.meta_byte(r, k)];
+  }
 }
 
 int grid_for(int64_t items) {
@@ -118,22 +157,18 @@ int launch_pack(int f, int64_t n, int64_t d, const void* codes, const void* scal
   uint8_t* p = static_cast<uint8_t*>(packed);
   PackedHeader h{kMagic, kLayoutVersion, uint32_t(f), 0u, n, d, l.codes_offset, l.meta_offset,
                  l.total_bytes};
-  hipError_t e = hipSuccess;
   hipLaunchKernelGGL(write_header_kernel, dim3(1), dim3(64), 0, s, p, h,
                      l.codes_offset + n * (d / 2), l.meta_offset, l.meta_offset + l.meta_bytes,
                      l.total_bytes);
+  const Slabs L{n, int(d), f};
   if (f == QMM_AFFINE4_G64) {
-    const int64_t n_words = n * (d / 8), n_groups = n * (d / 64);
-    hipLaunchKernelGGL(pack_affine_kernel, dim3(grid_for(n_words)), dim3(256), 0, s,
+    hipLaunchKernelGGL(pack_affine_kernel, dim3(grid_for(n * (d / 8))), dim3(256), 0, s,
                        static_cast<const uint32_t*>(codes), static_cast<const uint16_t*>(scales),
-                       static_cast<const uint16_t*>(biases),
-                       reinterpret_cast<uint32_t*>(p + l.codes_offset),
-                       reinterpret_cast<uint32_t*>(p + l.meta_offset), n_words, n_groups);
+                       static_cast<const uint16_t*>(biases), p + l.codes_offset, p + l.meta_offset, L);
   } else {
-    e = hipMemcpyAsync(p + l.codes_offset, codes, size_t(n * (d / 2)), hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return int(e);
-    hipLaunchKernelGGL(pack_mxfp4_meta_kernel, dim3(grid_for(l.meta_bytes)), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(scales), p + l.meta_offset, l.meta_bytes,
+    hipLaunchKernelGGL(pack_mxfp4_kernel, dim3(grid_for(n * (d / 32))), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),
+                       p + l.codes_offset, p + l.meta_offset, L,
                        reinterpret_cast<uint32_t*>(p + offsetof(PackedHeader, flags)));
   }
   return int(hipGetLastError());
@@ -152,20 +187,17 @@ int launch_unpack(int f, int64_t n, int64_t d, const void* packed, void* codes, 
   if (!layout_of(f, n, d, &l)) return int(hipErrorInvalidValue);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const uint8_t* p = static_cast<const uint8_t*>(packed);
+  const Slabs L{n, int(d), f};
   if (f == QMM_AFFINE4_G64) {
-    const int64_t n_words = n * (d / 8), n_groups = n * (d / 64);
-    hipLaunchKernelGGL(unpack_affine_kernel, dim3(grid_for(n_words)), dim3(256), 0, s,
-                       reinterpret_cast<const uint32_t*>(p + l.codes_offset),
-                       reinterpret_cast<const uint32_t*>(p + l.meta_offset),
-                       static_cast<uint32_t*>(codes), static_cast<uint16_t*>(scales),
-                       static_cast<uint16_t*>(biases), n_words, n_groups);
-    return int(hipGetLastError());
+    hipLaunchKernelGGL(unpack_affine_kernel, dim3(grid_for(n * (d / 8))), dim3(256), 0, s,
+                       p + l.codes_offset, p + l.meta_offset, static_cast<uint32_t*>(codes),
+                       static_cast<uint16_t*>(scales), static_cast<uint16_t*>(biases), L);
+  } else {
+    hipLaunchKernelGGL(unpack_mxfp4_kernel, dim3(grid_for(n * (d / 32))), dim3(256), 0, s,
+                       p + l.codes_offset, p + l.meta_offset, static_cast<uint8_t*>(codes),
+                       static_cast<uint8_t*>(scales), L);
   }
-  hipError_t e = hipMemcpyAsync(codes, p + l.codes_offset, size_t(n * (d / 2)),
-                                hipMemcpyDeviceToDevice, s);
-  if (e != hipSuccess) return int(e);
-  e = hipMemcpyAsync(scales, p + l.meta_offset, size_t(l.meta_bytes), hipMemcpyDeviceToDevice, s);
-  return int(e);
+  return int(hipGetLastError());
 }
 
 }  // namespace qmm

@@ -140,6 +140,15 @@ qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expe
                             int32_t max_seg_rows, qmm_bf16* y, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* Per-kernel GPU timing (per-op GPU timestamps, as in the op profiling of
+ * "LLM Decode / Prefill 优化案例（Metal）", Step 1).  Arms two caller-owned
+ * hipEvent_t handles for the next qmm_gemv / qmm_gemm / qmm_grouped_gemm call
+ * on this thread: its kernel is launched with hipExtLaunchKernel so `start`
+ * and `stop` are stamped by the dispatch itself, and their elapsed time is
+ * the kernel's execution time.  Either may be NULL.  The arming is consumed
+ * by that next launch; a call rejected by validation leaves it armed. */
+qmm_status qmm_profile_next(void* start_event, void* stop_event);
+
 /* Static description of a status code. */
 const char* qmm_status_string(qmm_status s);
 

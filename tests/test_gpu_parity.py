@@ -174,7 +174,8 @@ def test_gemv_affine_decode_workload_full():
 
 
 @pytest.mark.parametrize("n,d,elo,ecount", [(1, 32, 118, 9), (7, 96, 118, 9), (100, 3584, 118, 9),
-                                            (33, 3072, 118, 9), (64, 512, 1, 200), (9, 1056, 100, 60)])
+                                            (33, 3072, 118, 9), (64, 512, 1, 200), (9, 1056, 100, 60),
+                                            (40, 20480, 118, 9)])
 def test_gemv_mxfp4(n, d, elo, ecount):
     say("gemv mxfp4", n, d, elo, ecount)
     w = rand_mxfp4(3000 + n, n, d, elo, ecount)
@@ -411,3 +412,21 @@ def test_bitwise_deterministic():
     a = run_gemv(A, p, w, x[0])
     b = run_gemv(A, p, w, x[0])
     assert np.array_equal(a, b)
+
+
+def test_profile_events_time_the_kernel():
+    say("profile events")
+    import bench
+    hev = bench.HipEvents()
+    w = synth.affine_weights(41, 4096, 4096)
+    p = pack_affine(w)
+    x = dev(synth.activations(42, synth.S_X, 1, 4096))
+    y = nan_out(4096)
+    a, b = hev.new(), hev.new()
+    qmm.qmm_profile_next(a, b)
+    qmm.qmm_gemv(A, p, 4096, 4096, x, y)
+    torch.cuda.synchronize()
+    ms = hev.ms(a, b)
+    hev.close()
+    assert 0.0 < ms < 5.0
+    assert not np.any(host_u16(y) == NAN16)
