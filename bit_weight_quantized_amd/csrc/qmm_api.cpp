@@ -96,12 +96,13 @@ qmm_status qmm_pack(qmm_format f, int64_t n, int64_t d, const void* codes, const
     return fail(QMM_E_ALIGN, "codes must be 4-byte, scales/biases 2-byte aligned");
   int err = qmm::launch_pack(f, n, d, codes, scales, biases, packed, stream);
   if (err) return hip_fail(err, "qmm_pack");
-  if (f == QMM_MXFP4_G32) {
-    qmm::PackedHeader h;
-    err = qmm::read_header(packed, &h, stream);
-    if (err) return hip_fail(err, "qmm_pack");
-    if (h.flags & qmm::kFlagInvalid) return fail(QMM_E_VALUE, "E8M0 scale 255 (NaN) in the input");
-  }
+  qmm::PackedHeader h;
+  err = qmm::read_header(packed, &h, stream);
+  if (err) return hip_fail(err, "qmm_pack");
+  if (h.flags & qmm::kFlagInvalid)
+    return fail(QMM_E_VALUE, f == QMM_MXFP4_G32
+                                 ? "E8M0 scale 255 (NaN) in the input"
+                                 : "affine scale not finite or |scale| >= 2^100, or bias not finite");
   return QMM_OK;
 }
 

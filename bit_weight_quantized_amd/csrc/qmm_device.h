@@ -124,6 +124,37 @@ __device__ __forceinline__ u32x4_t affine_word_to_bf16x8(uint32_t v, float s, fl
   return r;
 }
 
+// Affine, MFMA path: the same w = s·q + b with one instruction per weight.
+// Masking a nibble pair into the two halves of a register makes two fp16
+// subnormals q·2^-24 (nibbles at bits 0..3 of each half) or q·2^-20 (bits
+// 4..7), and v_fma_mix_f32 then forms s'·(fp16) + b in fp32 with one rounding,
+// where s' = s·2^24 or s·2^20 (exact while finite; qmm_pack rejects scales of
+// magnitude 2^100 or more).  The result equals fmaf(s, q, b) bit for bit.
+struct AffineMix {
+  float s24, s20, b;
+};
+__device__ __forceinline__ AffineMix affine_mix_consts(uint32_t m) {
+  const float s = bf16_lo(m);
+  return {s * 16777216.0f, s * 1048576.0f, bf16_hi(m)};
+}
+__device__ __forceinline__ float f16_lo(uint32_t v) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(v)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t v) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(v >> 16)));
+}
+__device__ __forceinline__ u32x4_t affine_word_to_bf16x8_mix(uint32_t v, const AffineMix& c) {
+  const uint32_t v8 = v >> 8;
+  const uint32_t p0 = v & 0x000F000Fu, p1 = v & 0x00F000F0u;    // (q0, q1), (q2, q3)
+  const uint32_t p2 = v8 & 0x000F000Fu, p3 = v8 & 0x00F000F0u;  // (q4, q5), (q6, q7)
+  u32x4_t r;
+  r[0] = pack_bf16x2(__builtin_fmaf(c.s24, f16_lo(p0), c.b), __builtin_fmaf(c.s24, f16_hi(p0), c.b));
+  r[1] = pack_bf16x2(__builtin_fmaf(c.s20, f16_lo(p1), c.b), __builtin_fmaf(c.s20, f16_hi(p1), c.b));
+  r[2] = pack_bf16x2(__builtin_fmaf(c.s24, f16_lo(p2), c.b), __builtin_fmaf(c.s24, f16_hi(p2), c.b));
+  r[3] = pack_bf16x2(__builtin_fmaf(c.s20, f16_lo(p3), c.b), __builtin_fmaf(c.s20, f16_hi(p3), c.b));
+  return r;
+}
+
 // 2^(e - 127) as fp32 for an E8M0 byte e in [0, 254] (e = 0 is the subnormal 2^-127).
 __device__ __forceinline__ float e8m0_scale(uint32_t e) {
   return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);

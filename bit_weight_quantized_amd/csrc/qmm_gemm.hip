@@ -23,6 +23,8 @@
 // per 64 routed rows.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "qmm_device.h"
 #include "qmm_internal.h"
 #include "qmm_launch.h"
@@ -59,8 +61,94 @@ __device__ __forceinline__ void load_chunk(const uint8_t* codes, const uint8_t* 
 
 // ---------------------------------------------------------------------------
 // Dense GEMM
+//
+// Workgroup tile WM×256, wave w owns columns [64w, 64w + 64) and all WM rows,
+// v_mfma_f32_32x32x16_bf16, K step 64.  Software pipeline per wave, one K
+// step per stage:
+//   * activations X(ks + 2) are copied global -> LDS by buffer loads with the
+//     LDS destination (no registers), into one of three slots shared by the
+//     workgroup;
+//   * the wave's own weight codes and group metadata for step ks + 3 are
+//     copied the same way into one of three per-wave slots;
+//   * the weights of step ks + 1 are read back from LDS and dequantised into
+//     bf16 B operands while the MFMAs of step ks run;
+//   * the A operand of each MFMA pair is read from LDS kAhead pairs ahead.
+// Each stage starts with one wait (the copies issued two stages back are
+// complete: vmcnt counts in issue order and every stage issues the same
+// number) and one barrier.  The stage body is written in issue order and
+// pinned pair by pair, so the matrix core never waits for the VALU work.
+// Rows or columns past the tile edge and k past d are out-of-range buffer
+// reads and arrive as zeros, so the loop has no per-lane branches.
+//
+// LDS X slot: WM rows of 128 bytes (64 bf16); 16-byte chunk c of row r is
+// stored at position c ^ ((r >> 1) & 7).  The LDS has 64 banks (256 bytes):
+// the 16 lanes of one MFMA operand read phase touch 16 consecutive rows, and
+// this swizzle puts their 16-byte pieces in 16 distinct bank groups.  The
+// copies write whole 1 KiB blocks, which never conflict.
 // ---------------------------------------------------------------------------
-constexpr int kXs = 72;  // LDS row stride in bf16 for a 64-wide K step (16-byte pad)
+
+// 2^31 when k >= limit, else 0: OR-ed into a buffer offset (always below 2^31
+// here) it pushes the load past every buffer range, so it returns zero.
+// Arithmetic rather than a select, which the compiler would turn into
+// branches around the loads.
+__device__ __forceinline__ uint32_t oob_bit(int k, int limit) {
+  return uint32_t(limit - 1 - k) & 0x80000000u;
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// global (buffer) -> LDS copies: every lane moves 16 (4) bytes to LDS byte
+// address lds + 16·lane (lds + 4·lane); lds is wave-uniform.  Written as
+// inline asm so the compiler does not track them: it cannot tell the LDS
+// slots apart and would wait for every copy in flight before each LDS read.
+// The kernels order them with explicit vmcnt waits instead, and issue no
+// other vector-memory loads while copies are in flight.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(lds)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(uintptr_t((lds_ptr_t)p));
+}
+
+// bf16 pair r (codes 2r, 2r + 1) of an MXFP4 word; r folds to a constant
+// once the caller's loops are unrolled.
+__device__ __forceinline__ uint32_t mxfp4_pair(uint32_t v, float sc, int r) {
+  switch (r) {
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, sc, 3));
+  }
+}
+
+// A lane's raw weights for one K step: one 16-byte chunk (32 codes) and its
+// group metadata for each of its two columns.
+struct WChunk {
+  u32x4_t w[2];
+  uint32_t m[2];
+};
+
+constexpr int kXSlots = 3;          // activation slots (copy distance 2)
+constexpr int kWSlots = 3;          // weight slots (copy distance 3)
+constexpr int kWSlotBytes = 9216;   // 256 columns × (32 B codes + 4 B metadata)
+
+template <int WM>
+constexpr int gemm_lds_bytes() {
+  return kXSlots * WM * 128 + kWSlots * kWSlotBytes;
+}
 
 template <int FMT, int WM>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ codes,
@@ -69,10 +157,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
                                                    uint16_t* __restrict__ y, int tiles_m,
                                                    int tiles_n) {
   constexpr int RB = WM / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][WM * kXs];
+  constexpr int XSLOT = WM * 128;
+  constexpr int WBASE = kXSlots * XSLOT;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[gemm_lds_bytes<WM>()];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col_l = lane & 31, g = lane >> 5;
 
   // XCD-aware tile order: consecutive workgroups are dealt round-robin to the
@@ -83,48 +174,70 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   if ((tiles & 7) == 0) tile = (blockIdx.x & 7) * (tiles >> 3) + (blockIdx.x >> 3);
   const int tm = tile / tiles_n, tn = tile % tiles_n;
   const int m0 = tm * WM, n0 = tn * 256;
+  const int rows_m = min(WM, t - m0);
+  const int cols_n = min(256, n - n0);
 
   const Slabs L{n, d, FMT};
   const int nk = (d + 63) / 64;
+  const uint32_t lds_base = lds_addr(lds);
 
-  // this lane's two weight columns
-  int64_t col[2];
-  bool col_ok[2];
-#pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    col[cb] = n0 + 64 * wave + 32 * cb + col_l;
-    col_ok[cb] = col[cb] < n;
-  }
-
-  // activation tile loader: thread -> row (tid / 8) + 32 i, 16-byte slot tid % 8
-  const int xr = tid >> 3, xslot = tid & 7;
-  u32x4_t xreg[RB];
-  auto load_x = [&](int k0) {
-    const int k = k0 + 8 * xslot;
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int row = m0 + xr + 32 * i;
-      xreg[i] = (row < t && k < d) ? load16(x + int64_t(row) * d + k) : u32x4_t{0, 0, 0, 0};
-    }
-  };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-      *reinterpret_cast<u32x4_t*>(&xs[buf][(xr + 32 * i) * kXs + 8 * xslot]) = xreg[i];
+  // ---- activation copies: wave instruction i moves rows 8(w + 4i) .. +7 ----
+  const auto xrs = make_rsrc(x + int64_t(m0) * d, uint32_t(rows_m) * uint32_t(d) * 2u);
+  // instruction rows r0 = 8(w + 4i): ((r0 + lane/8) >> 1) & 7 = (4(w & 1) + lane/16) & 7
+  const int xrow = lane >> 3, xpos = lane & 7, xchunk = xpos ^ ((4 * (wave & 1) + (lane >> 4)) & 7);
+  const uint32_t xlane = (uint32_t(8 * wave + xrow) * uint32_t(d) + 8u * xchunk) * 2u;
+  const uint32_t xstep = 64u * uint32_t(d);  // bytes between instruction i and i + 1 (32 rows)
+  auto copy_x = [&](int ks, int slot, int i) {
+    const int k0 = 64 * ks;
+    const uint32_t o = (xlane + 2u * uint32_t(k0) + uint32_t(i) * xstep) | oob_bit(k0 + 8 * xchunk, d);
+    copy16_to_lds(xrs, o, lds_base + slot * XSLOT + 1024 * (wave + 4 * i));
   };
 
-  u32x4_t wreg[2];
-  uint32_t mreg[2];
-  auto load_w = [&](int k0) {
-    const int k = k0 + 32 * g;
+  // ---- weight copies: the wave's 64 columns, codes (2 instructions, lane ->
+  // column 64w + 32cb + lane%32, 16-byte half lane/32) and one metadata dword
+  // per column.  Only the wave itself reads them back, each lane the piece its
+  // own copy lane moved.
+  const uint32_t ccol = uint32_t(64 * wave + (lane & 31)), chalf = uint32_t(lane >> 5);
+  const uint32_t mcol = uint32_t(64 * wave + lane);
+  auto copy_w = [&](int ks, int slot) {
+    const int k0 = 64 * ks;
+    const bool any = k0 < d;
+    const int sl = (any ? k0 : 0) >> 9;
+    const int kk = k0 & (kSlabCodes - 1);
+    const uint32_t hw = uint32_t(L.width(sl) >> 1), mrow = uint32_t(L.meta_row(sl));
+    // byte of this step's metadata dword within a row's slab metadata
+    const int mk = FMT == QMM_AFFINE4_G64 ? 4 * (kk >> 6) : 4 * (kk >> 7);
+    const auto crs = make_rsrc(codes + L.codes(sl, n0) + (kk >> 1),
+                               any ? uint32_t(cols_n) * hw - uint32_t(kk >> 1) : 0u);
+    const auto mrs = make_rsrc(meta + L.meta(sl, n0) + mk,
+                               any ? uint32_t(cols_n) * mrow - uint32_t(mk) : 0u);
+    const uint32_t dst = lds_base + WBASE + slot * kWSlotBytes;
+    const uint32_t koob = oob_bit(k0 + 32 * int(chalf), d);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+      copy16_to_lds(crs, ((ccol + 32u * cb) * hw + 16u * chalf) | koob,
+                    dst + 1024 * (2 * wave + cb));
+    copy4_to_lds(mrs, (mcol * mrow) | oob_bit(k0, d), dst + 8192 + 256 * wave);
+  };
+  // per-stage copy instructions of one wave (the stage-start wait counts them)
+  constexpr int Q = RB + 3;
+
+  // ---- LDS reads ----
+  // A operand of pair (i, j): row 32i + col_l, chunk 4g + j
+  uint32_t aoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    aoff[j] = uint32_t(col_l * 128 + (((4 * g + j) ^ ((col_l >> 1) & 7)) << 4));
+  auto read_w = [&](int slot, int parity, WChunk& c) {
+    const uint8_t* src = lds + WBASE + slot * kWSlotBytes;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      if (col_ok[cb] && k < d) {
-        load_chunk<FMT>(codes, meta, L, col[cb], k, wreg[cb], mreg[cb]);
-      } else {
-        wreg[cb] = u32x4_t{0, 0, 0, 0};
-        mreg[cb] = 0;
-      }
+      c.w[cb] = *reinterpret_cast<const u32x4_t*>(src + 1024 * (2 * wave + cb) + 16 * lane);
+      const uint8_t* mp = src + 8192 + 256 * wave + 4 * (32 * cb + col_l);
+      if (FMT == QMM_AFFINE4_G64)
+        c.m[cb] = *reinterpret_cast<const uint32_t*>(mp);
+      else
+        c.m[cb] = mp[2 * parity + g];
     }
   };
 
@@ -136,39 +249,110 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][cb][r] = 0.f;
 
-  load_x(0);
-  load_w(0);
-  store_x(0);
-
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    const int k0 = ks * 64;
-    u32x4_t bfrag[2][4];
+  // The 32 B-operand registers of a step, enumerated e = 8 j + 4 cb + r
+  // (word j of the chunk, column cb, bf16 pair r of the word).
+  auto dequant_reg = [&](const WChunk& c, const AffineMix* am, const float* sc, int e) {
+    const int j = e >> 3, cb = (e >> 2) & 1, r = e & 3;
+    const uint32_t v = c.w[cb][j];
+    if (FMT == QMM_AFFINE4_G64) {
+      const uint32_t pr = (r >= 2 ? v >> 8 : v) & ((r & 1) ? 0x00F000F0u : 0x000F000Fu);
+      const float sv = (r & 1) ? am[cb].s20 : am[cb].s24;
+      return pack_bf16x2(__builtin_fmaf(sv, f16_lo(pr), am[cb].b),
+                         __builtin_fmaf(sv, f16_hi(pr), am[cb].b));
+    }
+    return mxfp4_pair(v, sc[cb], r);
+  };
+  auto consts = [&](const WChunk& c, AffineMix* am, float* sc) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      dequant_chunk<FMT>(wreg[cb], mreg[cb], bfrag[cb]);
-      if (!(col_ok[cb] && k0 + 32 * g < d))
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bfrag[cb][j] = u32x4_t{0, 0, 0, 0};
+      if (FMT == QMM_AFFINE4_G64)
+        am[cb] = affine_mix_consts(c.m[cb]);
+      else
+        sc[cb] = e8m0_scale(c.m[cb]);
     }
-    if (ks + 1 < nk) {
-      load_x(k0 + 64);
-      load_w(k0 + 64);
-    }
+  };
+
+  // One pipeline stage.  Pair p issues the two MFMAs of row block p % RB and
+  // word p / RB, the A read kAhead pairs later, one (or two) of the step
+  // ks + 1 B registers, and in pairs 0 .. Q-1 one copy instruction each.
+  constexpr int NP = 4 * RB;     // MFMA pairs per step
+  constexpr int EPP = 32 / NP;   // B registers dequantised per pair
+  constexpr int kAhead = 5;
+  static_assert(Q <= NP, "copies must fit the pairs");
+  auto stage = [&](int ks, auto parc, int xs_rd, int xs_wr, int ws_rd, int ws_wr,
+                   u32x4_t bcur[2][4], u32x4_t bnext[2][4]) {
+    constexpr int PAR = decltype(parc)::value;   // ks & 1
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(Q));
     __syncthreads();
+    WChunk wn;
+    read_w(ws_rd, PAR ^ 1, wn);
+    __builtin_amdgcn_sched_barrier(0);   // the weight reads go first: the constants wait for them
+    const uint8_t* ab = lds + xs_rd * XSLOT;
+    u32x4_t a[NP];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int p = 0; p < kAhead; ++p)
+      a[p] = *reinterpret_cast<const u32x4_t*>(ab + aoff[p / RB] + 4096 * (p % RB));
+    AffineMix am[2];
+    float sc[2];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xs[buf][(32 * i + col_l) * kXs + 32 * g + 8 * j]);
+    for (int p = 0; p < NP; ++p) {
+      const int i = p % RB, j = p / RB;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-          acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bfrag[cb][j]),
-              acc[i][cb], 0, 0, 0);
+      for (int cb = 0; cb < 2; ++cb)
+        acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8_t, a[p]), __builtin_bit_cast(bf16x8_t, bcur[cb][j]),
+            acc[i][cb], 0, 0, 0);
+      if (p + kAhead < NP) {
+        const int q = p + kAhead;
+        a[q] = *reinterpret_cast<const u32x4_t*>(ab + aoff[q / RB] + 4096 * (q % RB));
       }
+      if (p < RB) copy_x(ks + 2, xs_wr, p);
+      if (p == RB) copy_w(ks + 3, ws_wr);
+      if (p == 0) consts(wn, am, sc);
+#pragma unroll
+      for (int u = 0; u < EPP; ++u) {
+        const int e = p * EPP + u;
+        bnext[(e >> 2) & 1][e >> 3][e & 3] = dequant_reg(wn, am, sc, e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (ks + 1 < nk) store_x(buf ^ 1);
+  };
+
+  // prologue: W(0) first, then the copies a steady-state stage -2 and -1
+  // would have issued, so that every stage finds the same counts in flight
+  copy_w(0, 0);
+#pragma unroll
+  for (int i = 0; i < RB; ++i) copy_x(0, 0, i);
+  copy_w(1, 1);
+#pragma unroll
+  for (int i = 0; i < RB; ++i) copy_x(1, 1, i);
+  copy_w(2, 2);
+  u32x4_t ba[2][4], bb[2][4];
+  {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Q));
+    WChunk w0;
+    read_w(0, 0, w0);
+    AffineMix am[2];
+    float sc[2];
+    consts(w0, am, sc);
+#pragma unroll
+    for (int e = 0; e < 32; ++e) ba[(e >> 2) & 1][e >> 3][e & 3] = dequant_reg(w0, am, sc, e);
+  }
+
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  // slot indices rotate mod 3: stage ks reads X slot ks % 3 and W slot
+  // (ks + 1) % 3, and fills X slot (ks + 2) % 3 and W slot ks % 3.  An odd
+  // step count runs one extra stage past d: all its loads are out of range,
+  // so it adds exact zeros (a conditional exit would make the compiler copy
+  // the accumulators every iteration).
+  int s0 = 0;
+  for (int ks = 0; ks < nk; ks += 2) {
+    const int s1 = s0 == 2 ? 0 : s0 + 1, s2 = s1 == 2 ? 0 : s1 + 1;
+    stage(ks, P0{}, s0, s2, s1, s0, ba, bb);
+    stage(ks + 1, P1{}, s1, s0, s2, s1, bb, ba);
+    s0 = s2;
   }
 
   // epilogue: lane holds column col_l of each 32x32 block, rows 8(r/4) + 4g + r%4
@@ -176,11 +360,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      if (!col_ok[cb]) continue;
+      const int cl = 64 * wave + 32 * cb + col_l;
+      if (cl >= cols_n) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (row < t) y[int64_t(row) * n + col[cb]] = f32_to_bf16(acc[i][cb][r]);
+        const int rl = 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (rl < rows_m) y[int64_t(m0 + rl) * n + n0 + cl] = f32_to_bf16(acc[i][cb][r]);
       }
     }
 }

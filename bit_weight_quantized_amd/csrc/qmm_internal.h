@@ -1,6 +1,6 @@
 // Internal definitions shared by the qmm library sources (host and device).
 //
-// Packed device layout, version 2 (written by qmm_pack, read by every kernel):
+// Packed device layout, version 3 (written by qmm_pack, read by every kernel):
 //
 //   [0, 256)            header (PackedHeader)
 //   [256, meta_off)     codes, K-slabbed
@@ -10,8 +10,11 @@
 // may be narrower, any multiple of 32).  Slab s stores its width w_s of every
 // row, rows consecutive, and the slabs follow one another:
 //   codes of (slab s, row r) at  s·n·256 + r·w_s/2
-//   metadata of (slab s, row r)  at  s·n·mslab + r·(w_s/group)·mbytes
-// with mslab = 32 (affine: 8 groups × 4 bytes) or 16 (MXFP4: 16 groups × 1).
+//   metadata of (slab s, row r)  at  s·n·mslab + r·m_s
+// with mslab = 32 (affine: 8 groups × 4 bytes) or 16 (MXFP4: 16 groups × 1)
+// and m_s the metadata bytes of one row in slab s: (w_s/64)·4 for affine,
+// w_s/32 rounded up to a multiple of 4 for MXFP4 (padding bytes are zero), so
+// every row's metadata starts 4-byte aligned and can be fetched as dwords.
 // A decode GEMV sweeps the matrix slab by slab with all rows in flight, so at
 // any moment the whole GPU reads one contiguous window of memory, and each wave
 // load instruction covers 4 rows × 256 bytes = 1 KiB contiguous.
@@ -39,7 +42,7 @@
 namespace qmm {
 
 constexpr uint32_t kMagic = 0x344D4D51u;  // "QMM4"
-constexpr uint32_t kLayoutVersion = 2;
+constexpr uint32_t kLayoutVersion = 3;
 constexpr uint32_t kFlagInvalid = 1u;     // set by qmm_pack when an E8M0 byte is 255
 constexpr int64_t kHeaderBytes = 256;
 constexpr int64_t kMaxN = int64_t(1) << 28;  // keeps every grid below 2^32 work-items
@@ -73,7 +76,11 @@ inline bool layout_of(int f, int64_t n, int64_t d, Layout* out) {
   Layout l;
   l.codes_offset = kHeaderBytes;
   l.meta_offset = round_up(l.codes_offset + n * (d / 2), 256);
-  l.meta_bytes = f == QMM_AFFINE4_G64 ? n * (d / 64) * 4 : n * (d / 32);
+  // full slabs carry 32 (affine) or 16 (MXFP4) metadata bytes per row; the
+  // last slab's MXFP4 rows are padded to a multiple of 4 bytes
+  const int64_t wl = d - (d - 1) / 512 * 512;  // width of the last slab
+  l.meta_bytes = f == QMM_AFFINE4_G64 ? n * (d / 64) * 4
+                                      : n * ((d - wl) / 32 + round_up(wl / 32, 4));
   l.total_bytes = round_up(l.meta_offset + l.meta_bytes, 256);
   *out = l;
   return true;
@@ -96,7 +103,7 @@ struct Slabs {
     return int64_t(s) * n * (kSlabCodes / 2) + row * (width(s) / 2);
   }
   __host__ __device__ int meta_row(int s) const {
-    return fmt == QMM_AFFINE4_G64 ? width(s) / 16 : width(s) / 32;
+    return fmt == QMM_AFFINE4_G64 ? width(s) / 16 : (width(s) / 32 + 3) & ~3;
   }
   __host__ __device__ int64_t meta(int s, int64_t row) const {
     return int64_t(s) * n * (fmt == QMM_AFFINE4_G64 ? 32 : 16) + row * meta_row(s);

@@ -43,14 +43,18 @@ __global__ void write_header_kernel(uint8_t* packed, PackedHeader h, int64_t gap
 }
 
 // One thread per canonical code word (8 codes) and per metadata group; the
-// word of row r holding codes [8j, 8j + 8) goes to its slab position.
+// word of row r holding codes [8j, 8j + 8) goes to its slab position.  A scale
+// that is not finite or has magnitude 2^100 or more, or a bias that is not
+// finite, flags the blob invalid (the MFMA dequantisation multiplies the scale
+// by 2^24, which must stay finite).
 __global__ void pack_affine_kernel(const uint32_t* __restrict__ codes,
                                    const uint16_t* __restrict__ scales,
                                    const uint16_t* __restrict__ biases,
                                    uint8_t* __restrict__ out_codes, uint8_t* __restrict__ out_meta,
-                                   Slabs L) {
+                                   Slabs L, uint32_t* __restrict__ flags) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   const int64_t wpr = L.d / 8, gpr = L.d / 64;
+  bool bad = false;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < L.n * wpr; i += stride) {
     const int64_t r = i / wpr;
     const int k = int(i % wpr) * 8;
@@ -59,9 +63,11 @@ __global__ void pack_affine_kernel(const uint32_t* __restrict__ codes,
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < L.n * gpr; i += stride) {
     const int64_t r = i / gpr;
     const int k = int(i % gpr) * 64;
-    *reinterpret_cast<uint32_t*>(out_meta + L.meta_byte(r, k)) =
-        uint32_t(scales[i]) | (uint32_t(biases[i]) << 16);
+    const uint32_t sc = scales[i], bi = biases[i];
+    bad |= ((sc >> 7) & 0xFFu) >= 127u + 100u || ((bi >> 7) & 0xFFu) == 0xFFu;
+    *reinterpret_cast<uint32_t*>(out_meta + L.meta_byte(r, k)) = sc | (bi << 16);
   }
+  if (bad) atomicOr(flags, kFlagInvalid);
 }
 
 __global__ void unpack_affine_kernel(const uint8_t* __restrict__ in_codes,
@@ -103,6 +109,11 @@ __global__ void pack_mxfp4_kernel(const uint8_t* __restrict__ codes, const uint8
     bad |= (e == 255);
     out_meta[L.meta_byte(r, k)] = e;
   }
+  // zero the padding that ends each row's metadata in a narrow last slab
+  const int sl = L.count() - 1;
+  const int used = L.width(sl) / 32, pad = L.meta_row(sl) - used;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < L.n * pad; i += stride)
+    out_meta[L.meta(sl, i / pad) + used + i % pad] = 0;
   if (bad) atomicOr(flags, kFlagInvalid);
 }
 
@@ -164,7 +175,8 @@ int launch_pack(int f, int64_t n, int64_t d, const void* codes, const void* scal
   if (f == QMM_AFFINE4_G64) {
     hipLaunchKernelGGL(pack_affine_kernel, dim3(grid_for(n * (d / 8))), dim3(256), 0, s,
                        static_cast<const uint32_t*>(codes), static_cast<const uint16_t*>(scales),
-                       static_cast<const uint16_t*>(biases), p + l.codes_offset, p + l.meta_offset, L);
+                       static_cast<const uint16_t*>(biases), p + l.codes_offset, p + l.meta_offset, L,
+                       reinterpret_cast<uint32_t*>(p + offsetof(PackedHeader, flags)));
   } else {
     hipLaunchKernelGGL(pack_mxfp4_kernel, dim3(grid_for(n * (d / 32))), dim3(256), 0, s,
                        static_cast<const uint8_t*>(codes), static_cast<const uint8_t*>(scales),

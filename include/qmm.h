@@ -64,7 +64,7 @@ typedef enum {
   QMM_E_WORKSPACE = 5,    /* workspace NULL or smaller than qmm_workspace_bytes() */
   QMM_E_HIP = 6,          /* HIP runtime error; see qmm_last_error() */
   QMM_E_LAYOUT = 7,       /* packed blob header does not match (format, n, d, version) */
-  QMM_E_VALUE = 8         /* input value outside the format (E8M0 = 255 is NaN) */
+  QMM_E_VALUE = 8         /* input value outside the supported range (see qmm_pack) */
 } qmm_status;
 
 typedef enum { QMM_AFFINE4_G64 = 1, QMM_MXFP4_G32 = 2 } qmm_format;
@@ -89,10 +89,13 @@ size_t qmm_workspace_bytes(qmm_format f, int64_t t, int64_t n, int64_t d);
  *   scales  affine: bf16 scales [n][d/64]; MXFP4: uint8 E8M0 [n][d/32], device
  *   biases  affine: bf16 biases [n][d/64]; MXFP4: must be NULL
  *   packed  device buffer of qmm_packed_bytes(f, n, d) bytes, written whole
- * A pure bit/byte permutation plus header: no arithmetic on values.  For
- * MXFP4 the call SYNCHRONIZES `stream` to report E8M0 = 255 (NaN scale) as
- * QMM_E_VALUE; the blob is then marked invalid.  One-time preparation, not a
- * hot-path call. */
+ * A pure bit/byte permutation plus header: no arithmetic on values.  The
+ * call SYNCHRONIZES `stream` to report values outside the supported range as
+ * QMM_E_VALUE, and the blob is then marked invalid: for MXFP4 an E8M0 byte of
+ * 255 (NaN scale); for affine a scale that is not finite or whose magnitude is
+ * 2^100 or more, or a bias that is not finite (the MFMA kernels scale s by
+ * 2^24 while dequantising, which must not overflow).  One-time preparation,
+ * not a hot-path call. */
 qmm_status qmm_pack(qmm_format f, int64_t n, int64_t d, const void* codes, const void* scales,
                     const void* biases, void* packed, void* stream);
 
