@@ -199,6 +199,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   // own copy lane moved.
   const uint32_t ccol = uint32_t(64 * wave + (lane & 31)), chalf = uint32_t(lane >> 5);
   const uint32_t mcol = uint32_t(64 * wave + lane);
+  const uint32_t mquad = uint32_t(L.meta_quad());
+  const int64_t meta_total = L.meta_quad() * ((int64_t(n) + 3) / 4);
   auto copy_w = [&](int ks, int slot) {
     const int k0 = 64 * ks;
     const bool any = k0 < d;
@@ -209,15 +211,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
     const int mk = FMT == QMM_AFFINE4_G64 ? 4 * (kk >> 6) : 4 * (kk >> 7);
     const auto crs = make_rsrc(codes + L.codes(sl, n0) + (kk >> 1),
                                any ? uint32_t(cols_n) * hw - uint32_t(kk >> 1) : 0u);
-    const auto mrs = make_rsrc(meta + L.meta(sl, n0) + mk,
-                               any ? uint32_t(cols_n) * mrow - uint32_t(mk) : 0u);
+    // quad-major metadata: column c of the tile at (c / 4)·meta_quad + (c % 4)·mrow
+    const int64_t mo = L.meta(sl, n0) + mk;
+    const auto mrs = make_rsrc(meta + mo, any ? uint32_t(meta_total - mo) : 0u);
     const uint32_t dst = lds_base + WBASE + slot * kWSlotBytes;
     const uint32_t koob = oob_bit(k0 + 32 * int(chalf), d);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
       copy16_to_lds(crs, ((ccol + 32u * cb) * hw + 16u * chalf) | koob,
                     dst + 1024 * (2 * wave + cb));
-    copy4_to_lds(mrs, (mcol * mrow) | oob_bit(k0, d), dst + 8192 + 256 * wave);
+    copy4_to_lds(mrs, ((mcol >> 2) * mquad + (mcol & 3) * mrow) | oob_bit(k0, d),
+                 dst + 8192 + 256 * wave);
   };
   // per-stage copy instructions of one wave (the stage-start wait counts them)
   constexpr int Q = RB + 3;

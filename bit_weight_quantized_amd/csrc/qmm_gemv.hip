@@ -20,7 +20,8 @@
 // Activations and metadata are staged in LDS once per pass of up to
 // kPassSlabs slabs: the workgroup's activation row, cut into 32-code chunks
 // of 80 bytes (64 bytes of bf16, the chunk's sum at +64), and each wave's
-// metadata for its quad (the slabbed metadata of 4 rows, copied as it lies).
+// metadata for its quad (one contiguous piece of the quad-major metadata,
+// copied as it lies: slab by slab, row by row).
 //
 // Arithmetic.  Per chunk the dot product runs on 2-wide bf16 dot instructions
 // against (128 + q), built by OR-ing each nibble pair into the bf16 constant
@@ -47,15 +48,16 @@ namespace {
 constexpr int kWaves = 4;                 // quads per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRing = 2;                  // code slabs in flight per lane
-constexpr int kPassSlabs = 16;            // slabs staged in LDS per pass
+constexpr int kPassSlabs = 12;            // slabs staged in LDS per pass
 constexpr int kChunkBytes = 80;           // LDS activation chunk: 64 B of x, sum at +64
 constexpr int kXL = kPassSlabs * 64 / kThreads;   // 16-byte activation pieces per thread
+static_assert(kPassSlabs * 64 % kThreads == 0, "activation pieces must divide evenly");
 
 // metadata bytes of one quad (4 rows) in a full slab, loaded as 16-byte pieces
 template <int FMT>
 constexpr int quad_meta_bytes() { return FMT == QMM_AFFINE4_G64 ? 128 : 64; }
 template <int FMT>
-constexpr int meta_pieces_per_lane() { return kPassSlabs * quad_meta_bytes<FMT>() / 16 / 64; }
+constexpr int meta_pieces_per_lane() { return (kPassSlabs * quad_meta_bytes<FMT>() / 16 + 63) / 64; }
 
 constexpr uint32_t kOOB = 0x80000000u;    // OR-ed into a buffer offset: past every range
 
@@ -98,7 +100,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const int32_t* __restrict__ seg_expert, const int32_t* __restrict__ seg_offsets, int m_total,
     uint16_t* __restrict__ y) {
   constexpr int QMB = quad_meta_bytes<FMT>();
-  constexpr int MPS = QMB / 16;                  // metadata pieces per slab
   constexpr int ML = meta_pieces_per_lane<FMT>();
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -153,14 +154,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
       u32x4_t xv[kXL];
 #pragma unroll
       for (int i = 0; i < kXL; ++i) xv[i] = ld16(xr, 16u * uint32_t(tid + i * kThreads));
-      // 2. the quad's metadata, slab by slab as it lies in memory
+      // 2. the quad's metadata for the pass: one contiguous piece (quad-major layout)
+      const uint32_t m0 = uint32_t(quad) * uint32_t(L.meta_quad()) + uint32_t(p0 * QMB);
+      const int mbytes = (ps - 1) * QMB + 4 * L.meta_row(p0 + ps - 1);
       u32x4_t mv[ML];
 #pragma unroll
       for (int i = 0; i < ML; ++i) {
-        const int pc = lane + 64 * i, s = pc / MPS, q = pc % MPS;
-        const int sg = min(p0 + s, nslabs - 1);
-        const bool ok = s < ps && 16 * q < 4 * L.meta_row(sg);
-        mv[i] = ld16(mr, ok ? uint32_t(L.meta(sg, int64_t(quad) * 4)) + 16u * q : kOOB);
+        const int pc = lane + 64 * i;
+        mv[i] = ld16(mr, 16 * pc < mbytes ? m0 + 16u * pc : kOOB);
       }
       // 3. the code ring: this lane's chunk of slab s (zeros past the slab's width)
       auto code_off = [&](int s) -> uint32_t {
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
       for (int i = 0; i < ML; ++i) {
         const int pc = lane + 64 * i;
-        const uint32_t dst = pc < ps * MPS ? m_base + wave * m_wave + 16u * pc : m_trash;
+        const uint32_t dst = 16 * pc < mbytes ? m_base + wave * m_wave + 16u * pc : m_trash;
         *reinterpret_cast<u32x4_t*>(smem + dst) = mv[i];
       }
       __syncthreads();

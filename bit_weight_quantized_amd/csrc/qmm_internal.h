@@ -1,23 +1,30 @@
 // Internal definitions shared by the qmm library sources (host and device).
 //
-// Packed device layout, version 3 (written by qmm_pack, read by every kernel):
+// Packed device layout, version 4 (written by qmm_pack, read by every kernel):
 //
 //   [0, 256)            header (PackedHeader)
 //   [256, meta_off)     codes, K-slabbed
-//   [meta_off, total)   per-group metadata, K-slabbed
+//   [meta_off, total)   per-group metadata, quad-major
 //
-// K-slabbed: the reduction axis is cut into slabs of 512 codes (the last slab
-// may be narrower, any multiple of 32).  Slab s stores its width w_s of every
-// row, rows consecutive, and the slabs follow one another:
+// K-slabbed codes: the reduction axis is cut into slabs of 512 codes (the last
+// slab may be narrower, any multiple of 32).  Slab s stores its width w_s of
+// every row, rows consecutive, and the slabs follow one another:
 //   codes of (slab s, row r) at  s·n·256 + r·w_s/2
-//   metadata of (slab s, row r)  at  s·n·mslab + r·m_s
-// with mslab = 32 (affine: 8 groups × 4 bytes) or 16 (MXFP4: 16 groups × 1)
-// and m_s the metadata bytes of one row in slab s: (w_s/64)·4 for affine,
-// w_s/32 rounded up to a multiple of 4 for MXFP4 (padding bytes are zero), so
-// every row's metadata starts 4-byte aligned and can be fetched as dwords.
 // A decode GEMV sweeps the matrix slab by slab with all rows in flight, so at
 // any moment the whole GPU reads one contiguous window of memory, and each wave
 // load instruction covers 4 rows × 256 bytes = 1 KiB contiguous.
+//
+// Quad-major metadata: rows are taken in quads (4 consecutive rows; n is
+// padded to a multiple of 4 with zero metadata).  A quad's metadata is one
+// contiguous block of 4·M bytes, M the metadata bytes of one row, ordered
+// slab by slab and, inside a slab, row by row:
+//   metadata of (slab s, row r) at  (r / 4)·4M + 4·s·m_full + (r % 4)·m_s
+// where m_s is the metadata bytes of one row in slab s: (w_s/64)·4 for affine,
+// w_s/32 rounded up to a multiple of 4 for MXFP4 (padding bytes are zero), so
+// every row's metadata starts 4-byte aligned and can be fetched as dwords, and
+// m_full = m_s of a full slab (32 affine, 16 MXFP4).  A GEMV wave fetches its
+// quad's metadata for a run of slabs as one contiguous piece; a GEMM column
+// block reads 4 rows of a slab from one 128- (64-) byte segment.
 //
 // affine codes: one uint32 per 8 codes, nibbles regrouped so that the low
 //   half-word holds the even codes and the high half-word the odd codes:
@@ -42,7 +49,7 @@
 namespace qmm {
 
 constexpr uint32_t kMagic = 0x344D4D51u;  // "QMM4"
-constexpr uint32_t kLayoutVersion = 3;
+constexpr uint32_t kLayoutVersion = 4;
 constexpr uint32_t kFlagInvalid = 1u;     // set by qmm_pack when an E8M0 byte is 255
 constexpr int64_t kHeaderBytes = 256;
 constexpr int64_t kMaxN = int64_t(1) << 28;  // keeps every grid below 2^32 work-items
@@ -70,17 +77,22 @@ struct Layout {
   int64_t codes_offset, meta_offset, meta_bytes, total_bytes;
 };
 
+// metadata bytes of one row: 4 per 64 codes (affine), or one byte per 32
+// codes with each slab's bytes padded to a multiple of 4 (MXFP4; only the
+// last slab can be narrower than 512 codes)
+inline int64_t row_meta_bytes(int f, int64_t d) {
+  if (f == QMM_AFFINE4_G64) return d / 16;
+  const int64_t wl = d - (d - 1) / 512 * 512;  // width of the last slab
+  return (d - wl) / 32 + round_up(wl / 32, 4);
+}
+
 inline bool layout_of(int f, int64_t n, int64_t d, Layout* out) {
   const int g = group_of(f);
   if (g == 0 || n < 1 || n > kMaxN || d < g || d > kMaxD || d % g) return false;
   Layout l;
   l.codes_offset = kHeaderBytes;
   l.meta_offset = round_up(l.codes_offset + n * (d / 2), 256);
-  // full slabs carry 32 (affine) or 16 (MXFP4) metadata bytes per row; the
-  // last slab's MXFP4 rows are padded to a multiple of 4 bytes
-  const int64_t wl = d - (d - 1) / 512 * 512;  // width of the last slab
-  l.meta_bytes = f == QMM_AFFINE4_G64 ? n * (d / 64) * 4
-                                      : n * ((d - wl) / 32 + round_up(wl / 32, 4));
+  l.meta_bytes = round_up(n, 4) * row_meta_bytes(f, d);
   l.total_bytes = round_up(l.meta_offset + l.meta_bytes, 256);
   *out = l;
   return true;
@@ -102,11 +114,17 @@ struct Slabs {
   __host__ __device__ int64_t codes(int s, int64_t row) const {
     return int64_t(s) * n * (kSlabCodes / 2) + row * (width(s) / 2);
   }
+  // metadata bytes of one row in slab s, and in a full slab
   __host__ __device__ int meta_row(int s) const {
     return fmt == QMM_AFFINE4_G64 ? width(s) / 16 : (width(s) / 32 + 3) & ~3;
   }
+  __host__ __device__ int meta_full() const { return fmt == QMM_AFFINE4_G64 ? 32 : 16; }
+  // metadata bytes of one quad (4 rows, all slabs)
+  __host__ __device__ int64_t meta_quad() const {
+    return 4 * (int64_t(count() - 1) * meta_full() + meta_row(count() - 1));
+  }
   __host__ __device__ int64_t meta(int s, int64_t row) const {
-    return int64_t(s) * n * (fmt == QMM_AFFINE4_G64 ? 32 : 16) + row * meta_row(s);
+    return (row >> 2) * meta_quad() + 4 * int64_t(s) * meta_full() + (row & 3) * meta_row(s);
   }
   // byte offsets of code k / of the metadata of the group holding code k
   __host__ __device__ int64_t code_byte(int64_t row, int k) const {

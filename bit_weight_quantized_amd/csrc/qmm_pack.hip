@@ -42,6 +42,19 @@ __global__ void write_header_kernel(uint8_t* packed, PackedHeader h, int64_t gap
   if (threadIdx.x == 0) *reinterpret_cast<PackedHeader*>(packed) = h;
 }
 
+// Zero the metadata of the rows that pad n to a multiple of 4 (the last quad).
+__device__ void zero_pad_rows(uint8_t* __restrict__ out_meta, const Slabs& L) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  const int64_t n4 = (L.n + 3) & ~int64_t(3);
+  const int rmb = int(L.meta_quad() / 4), full = L.meta_full(), last = L.count() - 1;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < (n4 - L.n) * rmb; i += stride) {
+    const int64_t r = L.n + i / rmb;
+    const int b = int(i % rmb);
+    const int s = b / full < last ? b / full : last;
+    out_meta[L.meta(s, r) + (b - s * full)] = 0;
+  }
+}
+
 // One thread per canonical code word (8 codes) and per metadata group; the
 // word of row r holding codes [8j, 8j + 8) goes to its slab position.  A scale
 // that is not finite or has magnitude 2^100 or more, or a bias that is not
@@ -67,6 +80,7 @@ __global__ void pack_affine_kernel(const uint32_t* __restrict__ codes,
     bad |= ((sc >> 7) & 0xFFu) >= 127u + 100u || ((bi >> 7) & 0xFFu) == 0xFFu;
     *reinterpret_cast<uint32_t*>(out_meta + L.meta_byte(r, k)) = sc | (bi << 16);
   }
+  zero_pad_rows(out_meta, L);
   if (bad) atomicOr(flags, kFlagInvalid);
 }
 
@@ -114,6 +128,7 @@ __global__ void pack_mxfp4_kernel(const uint8_t* __restrict__ codes, const uint8
   const int used = L.width(sl) / 32, pad = L.meta_row(sl) - used;
   for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < L.n * pad; i += stride)
     out_meta[L.meta(sl, i / pad) + used + i % pad] = 0;
+  zero_pad_rows(out_meta, L);
   if (bad) atomicOr(flags, kFlagInvalid);
 }
 
