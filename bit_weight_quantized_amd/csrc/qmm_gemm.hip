@@ -17,10 +17,13 @@
 //
 // Dense kernel: workgroup tile WM×256, wave w owns columns [64w, 64w + 64)
 // and all WM rows, v_mfma_f32_32x32x16_bf16, K step 64 (one affine group).
-// Grouped kernel: one workgroup per (segment, 256-column tile), rows of the
+// Grouped kernel: one workgroup per (segment, 128-column tile), rows of the
 // segment gathered through row_index in blocks of 64, 16x16x32 MFMA so short
 // segments waste little, K step 128.  Each expert's weight tile is read once
-// per 64 routed rows.
+// per 64 routed rows.  Group metadata is loaded once per 512-code slab, one
+// column per lane (16 or 32 contiguous bytes), and handed to the lanes that
+// dequantise that column with ds_bpermute: loading it per K step and column
+// block cost a quarter of the kernel's time in extra load instructions.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -44,19 +47,6 @@ __device__ __forceinline__ void dequant_chunk(const u32x4_t w, uint32_t m, u32x4
 #pragma unroll
     for (int j = 0; j < 4; ++j) out[j] = mxfp4_word_to_bf16x8(w[j], sc);
   }
-}
-
-// Codes [k, k + 32) of weight row `col` (one 16-byte chunk) and the metadata
-// of their group, from the K-slabbed layout (qmm_internal.h).
-template <int FMT>
-__device__ __forceinline__ void load_chunk(const uint8_t* codes, const uint8_t* meta,
-                                           const Slabs& L, int64_t col, int k, u32x4_t& w,
-                                           uint32_t& m) {
-  w = load16(codes + L.code_byte(col, k));
-  if (FMT == QMM_AFFINE4_G64)
-    m = *reinterpret_cast<const uint32_t*>(meta + L.meta_byte(col, k));
-  else
-    m = meta[L.meta_byte(col, k)];
 }
 
 // ---------------------------------------------------------------------------
@@ -378,6 +368,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
 // Grouped GEMM (routed experts)
 // ---------------------------------------------------------------------------
 constexpr int kGBM = 64;    // routed rows per pass
+constexpr int kGCB = 4;     // 16-column blocks per wave
+constexpr int kGCols = 4 * 16 * kGCB;   // columns per workgroup
 constexpr int kGXs = 136;   // LDS row stride in bf16 for a 128-wide K step
 
 template <int FMT>
@@ -393,7 +385,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
   const int lane = tid & 63, wave = tid >> 6;
   const int col_l = lane & 15, g = lane >> 4;
   const int s = blockIdx.y;
-  const int n0 = blockIdx.x * 256;
+  const int n0 = blockIdx.x * kGCols;
 
   const int r_begin = min(max(seg_offsets[s], 0), m_total);
   const int r_end = min(max(seg_offsets[s + 1], r_begin), m_total);
@@ -407,15 +399,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
   const Slabs L{n, d, FMT};
   const int nk = (d + 127) / 128;
 
-  int64_t col[4];
-  bool col_ok[4];
+  int64_t col[kGCB];
+  bool col_ok[kGCB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    col[cb] = n0 + 64 * wave + 16 * cb + col_l;
+  for (int cb = 0; cb < kGCB; ++cb) {
+    col[cb] = n0 + 16 * kGCB * wave + 16 * cb + col_l;
     col_ok[cb] = col[cb] < n;
   }
 
   const int xr = tid >> 2, xq = tid & 3;  // activation loader: row tid/4, slots 4xq..4xq+3
+  constexpr int MW = FMT == QMM_AFFINE4_G64 ? 8 : 4;   // metadata dwords per row per full slab
+  const int64_t mcol = min(int64_t(n0 + 16 * kGCB * wave + lane), int64_t(n) - 1);
+  const __amdgpu_buffer_rsrc_t mrs =
+      make_rsrc(meta, uint32_t(L.meta_quad() * ((int64_t(n) + 3) / 4)));
 
   for (int mb = r_begin; mb < r_end; mb += kGBM) {
     const int nrows = min(kGBM, r_end - mb);
@@ -444,36 +440,70 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x4_t*>(&xs[buf][xr * kGXs + 8 * (4 * xq + i)]) = xreg[i];
     };
-    u32x4_t wreg[4];
-    uint32_t mreg[4];
+    u32x4_t wreg[kGCB];
     auto load_w = [&](int k0) {
       const int k = k0 + 32 * g;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        if (col_ok[cb] && k < d) {
-          load_chunk<FMT>(codes, meta, L, col[cb], k, wreg[cb], mreg[cb]);
-        } else {
-          wreg[cb] = u32x4_t{0, 0, 0, 0};
-          mreg[cb] = 0;
+      for (int cb = 0; cb < kGCB; ++cb)
+        wreg[cb] = (col_ok[cb] && k < d) ? load16(codes + L.code_byte(col[cb], k)) : u32x4_t{0, 0, 0, 0};
+    };
+    // metadata of the slab starting at code k0 for the wave's column `lane`
+    uint32_t mslab[MW];
+    auto load_meta = [&](int k0) {
+      const int sl = k0 >> 9;
+      const uint32_t off = uint32_t(L.meta(sl, mcol));
+      if (L.meta_row(sl) == MW * 4) {   // full slab: 16-byte aligned
+#pragma unroll
+        for (int i = 0; i < MW / 4; ++i) {
+          const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(mrs, int(off + 16u * i), 0, 0));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mslab[4 * i + j] = v[j];
         }
+      } else {                          // narrow last slab: dwords (bytes past d are never used)
+#pragma unroll
+        for (int i = 0; i < MW; ++i) mslab[i] = __builtin_amdgcn_raw_buffer_load_b32(mrs, int(off + 4u * i), 0, 0);
       }
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[4][kGCB];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < kGCB; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     load_x(0);
     load_w(0);
+    load_meta(0);
     store_x(0);
     for (int ks = 0; ks < nk; ++ks) {
       const int buf = ks & 1;
       const int k0 = ks * 128;
-      u32x4_t bfrag[4][4];
+      // this step's group metadata for each column block: dword q of the slab
+      // metadata (MXFP4, byte g) or dword 2q + g/2 (affine), from the lane that loaded it
+      const int q = ks & 3;
+      uint32_t mreg[kGCB];
+      {
+        const uint32_t v0 = FMT == QMM_AFFINE4_G64
+                                ? (q == 0 ? mslab[0] : q == 1 ? mslab[2] : q == 2 ? mslab[4] : mslab[6])
+                                : (q == 0 ? mslab[0] : q == 1 ? mslab[1] : q == 2 ? mslab[2] : mslab[3]);
+        const uint32_t v1 = FMT == QMM_AFFINE4_G64
+                                ? (q == 0 ? mslab[1] : q == 1 ? mslab[3] : q == 2 ? mslab[5] : mslab[7])
+                                : 0u;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+        for (int cb = 0; cb < kGCB; ++cb) {
+          const int src = 4 * (16 * cb + col_l);
+          if (FMT == QMM_AFFINE4_G64) {
+            const uint32_t a = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(v0)));
+            const uint32_t b = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(v1)));
+            mreg[cb] = (g >> 1) ? b : a;
+          } else {
+            mreg[cb] = (uint32_t(__builtin_amdgcn_ds_bpermute(src, int(v0))) >> (8 * g)) & 0xFFu;
+          }
+        }
+      }
+      u32x4_t bfrag[kGCB][4];
+#pragma unroll
+      for (int cb = 0; cb < kGCB; ++cb) {
         dequant_chunk<FMT>(wreg[cb], mreg[cb], bfrag[cb]);
         if (!(col_ok[cb] && k0 + 32 * g < d))
 #pragma unroll
@@ -482,6 +512,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
       if (ks + 1 < nk) {
         load_x(k0 + 128);
         load_w(k0 + 128);
+        if (((k0 + 128) & (kSlabCodes - 1)) == 0) load_meta(k0 + 128);
       }
       __syncthreads();
 #pragma unroll
@@ -491,7 +522,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
           if (i < nrb) {
             const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xs[buf][(16 * i + col_l) * kGXs + 32 * g + 8 * j]);
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
+            for (int cb = 0; cb < kGCB; ++cb)
               acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                   __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bfrag[cb][j]),
                   acc[i][cb], 0, 0, 0);
@@ -506,7 +537,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
     for (int i = 0; i < 4; ++i) {
       if (i >= nrb) continue;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < kGCB; ++cb) {
         if (!col_ok[cb]) continue;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -558,7 +589,7 @@ int launch_grouped_gemm(const GemmArgs& a, void* stream) {
   Layout l;
   if (!layout_of(a.f, a.n, a.d, &l)) return int(hipErrorInvalidValue);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid(unsigned((a.n + 255) / 256), unsigned(a.n_seg));
+  dim3 grid(unsigned((a.n + kGCols - 1) / kGCols), unsigned(a.n_seg));
   if (a.f == QMM_AFFINE4_G64)
     launch_kernel(grouped_gemm_kernel<QMM_AFFINE4_G64>, grid, dim3(256), s, a.packed,
                        a.expert_stride, a.n_experts, l.codes_offset, l.meta_offset, a.n, a.d, a.x,
