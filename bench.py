@@ -11,7 +11,10 @@ in HBM:
   moe_pre   MXFP4 grouped GEMM, 512 tokens routed top-16 over 896 experts,
             gate_up only
 Weights of the decode row rotate over enough packed copies (> 2x the 256 MB
-Infinity Cache) that every launch reads HBM, not the cache.
+Infinity Cache) that every launch reads HBM, not the cache.  After the timed
+steps, a plain streaming read of the decode row's byte count (qmm_stream_read,
+rotated the same way, timed the same way) is reported as the achievable read
+ceiling at that size (`stream_ceiling`).
 
 Each kernel launch gets HIP start/stop events stamped by its own dispatch
 (qmm_profile_next -> hipExtLaunchKernel, on the stream it runs on); their
@@ -275,6 +278,28 @@ def main(argv=None) -> int:
                              hbm_frac=round(nb / mean / 1e3 / HBM_PEAK_GBPS, 4),
                              mfma_frac=round(fl / mean / 1e6 / BF16_PEAK_TFLOPS, 4))
 
+    # read ceiling at the decode size: a plain streaming read of the same number
+    # of bytes, rotated over as many buffers, timed the same way (not part of a step)
+    stream_ceiling = None
+    if "decode" in rows:
+        sbytes = b1 // 16 * 16
+        sbufs = [torch.empty(sbytes, dtype=torch.uint8, device=dev).fill_(1) for _ in range(args.rotate)]
+        sink = torch.empty(2048, dtype=torch.int32, device=dev)
+        for i in range(10):
+            qmm.qmm_stream_read(sbufs[i % len(sbufs)], sbytes, sink)
+        sev = [(hev.new(), hev.new()) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(sev):
+            qmm.qmm_profile_next(a, b)
+            qmm.qmm_stream_read(sbufs[i % len(sbufs)], sbytes, sink)
+        torch.cuda.synchronize()
+        sus = np.array([hev.ms(a, b) * 1e3 for a, b in sev])
+        stream_ceiling = {"kernel": "stream_read_kernel", "bytes": int(sbytes),
+                          "us_mean": round(float(sus.mean()), 3),
+                          "GBps": round(sbytes / float(sus.mean()) / 1e3, 1),
+                          "frac": round(sbytes / float(sus.mean()) / 1e3 / HBM_PEAK_GBPS, 4)}
+        del sbufs
+
     hev.close()
     out = {
         "metric": METRIC,
@@ -296,6 +321,10 @@ def main(argv=None) -> int:
         out["roofline"] = {"bound": "hbm", "achieved": g["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": g["hbm_frac"], "traffic": traffic, "kernel": "gemv_kernel<affine>",
                            "algorithmic_bytes_per_launch": g["bytes"], "kernel_sources_hash": kh}
+    if stream_ceiling is not None:
+        out["stream_ceiling"] = stream_ceiling
+        if "roofline" in out:
+            out["roofline"]["achievable_stream_GBps"] = stream_ceiling["GBps"]
     if "gemm" in results:
         g = results["gemm"]
         out["prefill_gemm"] = {"value": g["TFLOPs"], "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,

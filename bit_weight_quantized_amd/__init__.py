@@ -16,7 +16,7 @@ __all__ = [
     "QMM_AFFINE4_G64", "QMM_MXFP4_G32", "QmmError", "lib_path", "load",
     "qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
     "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
-    "qmm_layout_version", "qmm_profile_next", "EXPORTS",
+    "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "EXPORTS",
 ]
 
 QMM_AFFINE4_G64 = 1
@@ -27,7 +27,7 @@ STATUS = {0: "QMM_OK", 1: "QMM_E_ARG", 2: "QMM_E_SHAPE", 3: "QMM_E_ALIGN", 4: "Q
 
 EXPORTS = ("qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
            "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
-           "qmm_layout_version", "qmm_profile_next")
+           "qmm_layout_version", "qmm_profile_next", "qmm_stream_read")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -68,6 +68,7 @@ def load():
         "qmm_last_error": (ctypes.c_char_p, []),
         "qmm_layout_version": (ctypes.c_uint32, []),
         "qmm_profile_next": (ctypes.c_int, [vp, vp]),
+        "qmm_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -133,6 +134,11 @@ def qmm_last_error() -> str:
 def qmm_profile_next(start_event, stop_event):
     """Arm two raw hipEvent_t handles (ints) for the next matmul launch on this thread."""
     _check(load().qmm_profile_next(start_event, stop_event), "qmm_profile_next")
+
+
+def qmm_stream_read(src, nbytes, sink, stream=None):
+    """Read `nbytes` of device memory once (measurement of the HBM read ceiling)."""
+    _check(load().qmm_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "qmm_stream_read")
 
 
 def qmm_pack(fmt, n, d, codes, scales, biases, packed, stream=None):

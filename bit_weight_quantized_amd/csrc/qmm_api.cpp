@@ -65,6 +65,17 @@ size_t qmm_workspace_bytes(qmm_format, int64_t, int64_t, int64_t) { return 0; }
 
 uint32_t qmm_layout_version(void) { return qmm::kLayoutVersion; }
 
+qmm_status qmm_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  g_last_error[0] = 0;
+  if (!src || !sink) return fail(QMM_E_ARG, "NULL pointer");
+  if (!aligned(src, 16) || !aligned(sink, 4)) return fail(QMM_E_ALIGN, "src must be 16-byte, sink 4-byte aligned");
+  if (bytes == 0 || bytes % 16 || bytes >= (size_t(1) << 31))
+    return fail(QMM_E_SHAPE, "bytes must be a positive multiple of 16 below 2^31");
+  int err = qmm::launch_stream_read(src, bytes, sink, stream);
+  if (err) return hip_fail(err, "qmm_stream_read");
+  return QMM_OK;
+}
+
 const char* qmm_last_error(void) { return g_last_error; }
 
 const char* qmm_status_string(qmm_status s) {

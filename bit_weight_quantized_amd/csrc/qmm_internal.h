@@ -198,4 +198,8 @@ struct GemmArgs {
 int launch_gemm(const GemmArgs& a, void* stream);
 int launch_grouped_gemm(const GemmArgs& a, void* stream);
 
+// read-only streaming kernel (measurement support): kStreamBlocks workgroups
+constexpr int kStreamBlocks = 2048;
+int launch_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 }  // namespace qmm

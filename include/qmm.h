@@ -152,6 +152,17 @@ qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expe
  * by that next launch; a call rejected by validation leaves it armed. */
 qmm_status qmm_profile_next(void* start_event, void* stop_event);
 
+/* Measurement support: the achievable HBM read rate.  Reads every byte of the
+ * device buffer `src` once (16-byte non-temporal loads, 2048 workgroups of 256
+ * threads, grid-stride) and stores one word per workgroup to `sink` (device,
+ * >= 2048 uint32): the XOR of the words it read, so the XOR of all 2048
+ * stored words equals the XOR of the buffer.  `src` 16-byte aligned, `bytes`
+ * a multiple of 16, 0 < bytes < 2^31 (QMM_E_ALIGN / QMM_E_SHAPE otherwise).
+ * Asynchronous on `stream`; armed profiling events apply to it as to the
+ * matmul calls.  Not part of the matmul path: a ceiling to report its
+ * HBM-bound kernels against. */
+qmm_status qmm_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 /* Static description of a status code. */
 const char* qmm_status_string(qmm_status s);
 

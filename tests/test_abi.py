@@ -105,6 +105,13 @@ def test_validation_errors_before_any_launch():
     expect(E_SHAPE, g, A, P, blob, 2, 16, 64, P, 4, P, P, P, 70000, 4, 4, P, None, 0)  # n_seg
     expect(E_ALIGN, g, A, P, blob, 2, 16, 64, P, 4, P + 2, P, P, 1, 4, 4, P, None, 0)
     assert "aligned" in qmm.qmm_last_error()
+    s = qmm.qmm_stream_read
+    expect(E_ARG, s, None, 1024, P, 0)
+    expect(E_ARG, s, P, 1024, None, 0)
+    expect(E_ALIGN, s, P + 8, 1024, P, 0)
+    expect(E_SHAPE, s, P, 0, P, 0)
+    expect(E_SHAPE, s, P, 1000, P, 0)
+    expect(E_SHAPE, s, P, 1 << 31, P, 0)
 
 
 def test_empty_grouped_call_is_a_no_op():

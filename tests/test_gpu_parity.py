@@ -430,3 +430,17 @@ def test_profile_events_time_the_kernel():
     hev.close()
     assert 0.0 < ms < 5.0
     assert not np.any(host_u16(y) == NAN16)
+
+
+def test_stream_read_reads_every_byte():
+    """The read-ceiling kernel: XOR of its per-workgroup words equals the
+    XOR of the buffer (ragged size: not a multiple of the grid's stride)."""
+    say("stream read")
+    rng = np.random.default_rng(77)
+    words = rng.integers(0, 2 ** 32, size=(39_851_008 // 4 + 4,), dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to(DEV)
+    sink = torch.zeros(2048, dtype=torch.int32, device=DEV)
+    qmm.qmm_stream_read(buf, words.size * 4, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)
