@@ -55,14 +55,18 @@ __device__ __forceinline__ void dequant_chunk(const u32x4_t w, uint32_t m, u32x4
 // Workgroup tile WM×256, wave w owns columns [64w, 64w + 64) and all WM rows,
 // v_mfma_f32_32x32x16_bf16, K step 64.  Software pipeline per wave, one K
 // step per stage:
-//   * activations X(ks + 2) are copied global -> LDS by buffer loads with the
-//     LDS destination (no registers), into one of three slots shared by the
+//   * activations X(ks + 3) are copied global -> LDS by buffer loads with the
+//     LDS destination (no registers), into one of four slots shared by the
 //     workgroup;
 //   * the wave's own weight codes and group metadata for step ks + 3 are
 //     copied the same way into one of three per-wave slots;
 //   * the weights of step ks + 1 are read back from LDS and dequantised into
-//     bf16 B operands while the MFMAs of step ks run;
-//   * the A operand of each MFMA pair is read from LDS kAhead pairs ahead.
+//     bf16 B operands while the MFMAs of step ks run, starting two MFMA pairs
+//     into the stage so the LDS reads have arrived;
+//   * the A operand of each MFMA pair is read from LDS kAhead pairs ahead, and
+//     the first kAhead of the next stage are read during this stage's last
+//     pairs (X(ks + 1) is complete and visible by then), so a stage starts
+//     its MFMAs right after the barrier.
 // Each stage starts with one wait (the copies issued two stages back are
 // complete: vmcnt counts in issue order and every stage issues the same
 // number) and one barrier.  The stage body is written in issue order and
@@ -131,7 +135,8 @@ struct WChunk {
   uint32_t m[2];
 };
 
-constexpr int kXSlots = 3;          // activation slots (copy distance 2)
+constexpr int kXSlots = 4;          // activation slots (copy distance 3)
+constexpr int kXDist = 3;
 constexpr int kWSlots = 3;          // weight slots (copy distance 3)
 constexpr int kWSlotBytes = 9216;   // 256 columns × (32 B codes + 4 B metadata)
 
@@ -270,22 +275,22 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   // word p / RB, the A read kAhead pairs later, one (or two) of the step
   // ks + 1 B registers, and in pairs 0 .. Q-1 one copy instruction each.
   constexpr int NP = 4 * RB;     // MFMA pairs per step
-  constexpr int EPP = 32 / NP;   // B registers dequantised per pair
+  constexpr int kDq = 2;         // first pair that dequantises the next step's weights
   constexpr int kAhead = 5;
   static_assert(Q <= NP, "copies must fit the pairs");
   auto stage = [&](int ks, auto parc, int xs_rd, int xs_wr, int ws_rd, int ws_wr,
-                   u32x4_t bcur[2][4], u32x4_t bnext[2][4]) {
+                   u32x4_t bcur[2][4], u32x4_t bnext[2][4], u32x4_t apre[kAhead],
+                   u32x4_t anext[kAhead]) {
     constexpr int PAR = decltype(parc)::value;   // ks & 1
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(Q));
     __syncthreads();
     WChunk wn;
     read_w(ws_rd, PAR ^ 1, wn);
-    __builtin_amdgcn_sched_barrier(0);   // the weight reads go first: the constants wait for them
     const uint8_t* ab = lds + xs_rd * XSLOT;
+    const int xs_nx = (xs_rd + 1) & 3;
     u32x4_t a[NP];
 #pragma unroll
-    for (int p = 0; p < kAhead; ++p)
-      a[p] = *reinterpret_cast<const u32x4_t*>(ab + aoff[p / RB] + 4096 * (p % RB));
+    for (int p = 0; p < kAhead; ++p) a[p] = apre[p];   // read during the previous stage
     AffineMix am[2];
     float sc[2];
     __builtin_amdgcn_sched_barrier(0);
@@ -300,14 +305,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
       if (p + kAhead < NP) {
         const int q = p + kAhead;
         a[q] = *reinterpret_cast<const u32x4_t*>(ab + aoff[q / RB] + 4096 * (q % RB));
+      } else {
+        // the first A operands of the next stage: X(ks + 1) is complete (its
+        // copies are two stages old) and visible since this stage's barrier
+        const int q = p + kAhead - NP;
+        anext[q] = *reinterpret_cast<const u32x4_t*>(lds + xs_nx * XSLOT + aoff[q / RB] + 4096 * (q % RB));
       }
-      if (p < RB) copy_x(ks + 2, xs_wr, p);
+      if (p < RB) copy_x(ks + kXDist, xs_wr, p);
       if (p == RB) copy_w(ks + 3, ws_wr);
-      if (p == 0) consts(wn, am, sc);
+      // the weight reads issued at the stage start have two pairs to arrive
+      if (p == kDq) consts(wn, am, sc);
+      if (p >= kDq) {
 #pragma unroll
-      for (int u = 0; u < EPP; ++u) {
-        const int e = p * EPP + u;
-        bnext[(e >> 2) & 1][e >> 3][e & 3] = dequant_reg(wn, am, sc, e);
+        for (int e = (p - kDq) * 32 / (NP - kDq); e < (p + 1 - kDq) * 32 / (NP - kDq); ++e)
+          bnext[(e >> 2) & 1][e >> 3][e & 3] = dequant_reg(wn, am, sc, e);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -315,16 +326,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
 
   // prologue: W(0) first, then the copies a steady-state stage -2 and -1
   // would have issued, so that every stage finds the same counts in flight
-  copy_w(0, 0);
 #pragma unroll
   for (int i = 0; i < RB; ++i) copy_x(0, 0, i);
-  copy_w(1, 1);
+  copy_w(0, 0);
 #pragma unroll
   for (int i = 0; i < RB; ++i) copy_x(1, 1, i);
+  copy_w(1, 1);
+#pragma unroll
+  for (int i = 0; i < RB; ++i) copy_x(2, 2, i);
   copy_w(2, 2);
   u32x4_t ba[2][4], bb[2][4];
+  u32x4_t pa[kAhead], pb[kAhead];
   {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Q));
+    __syncthreads();   // X(0) copied by every wave
+#pragma unroll
+    for (int p = 0; p < kAhead; ++p)
+      pa[p] = *reinterpret_cast<const u32x4_t*>(lds + aoff[p / RB] + 4096 * (p % RB));
     WChunk w0;
     read_w(0, 0, w0);
     AffineMix am[2];
@@ -336,16 +354,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
 
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  // slot indices rotate mod 3: stage ks reads X slot ks % 3 and W slot
-  // (ks + 1) % 3, and fills X slot (ks + 2) % 3 and W slot ks % 3.  An odd
+  // X slot of step k is k % 4, W slot of step k is k % 3: stage ks reads X
+  // slot ks % 4 and W slot (ks + 1) % 3, and fills X slot (ks + 3) % 4 and W
+  // slot ks % 3.  An odd
   // step count runs one extra stage past d: all its loads are out of range,
   // so it adds exact zeros (a conditional exit would make the compiler copy
   // the accumulators every iteration).
   int s0 = 0;
   for (int ks = 0; ks < nk; ks += 2) {
     const int s1 = s0 == 2 ? 0 : s0 + 1, s2 = s1 == 2 ? 0 : s1 + 1;
-    stage(ks, P0{}, s0, s2, s1, s0, ba, bb);
-    stage(ks + 1, P1{}, s1, s0, s2, s1, bb, ba);
+    stage(ks, P0{}, ks & 3, (ks + 3) & 3, s1, s0, ba, bb, pa, pb);
+    stage(ks + 1, P1{}, (ks + 1) & 3, ks & 3, s2, s1, bb, ba, pb, pa);
     s0 = s2;
   }
 

@@ -301,10 +301,13 @@ def run_grouped(fmt, stk, stride, n_exp, n, d, x_bits, seg_expert, seg_offsets, 
     return host_u16(y)
 
 
-@pytest.mark.parametrize("fmt", [A, M])
-def test_grouped_gemm_small(fmt):
-    say("grouped small", fmt)
-    n, d, n_exp, t = 300, 256, 5, 140
+@pytest.mark.parametrize("fmt,d", [(A, 256), (M, 256), (A, 576), (M, 1056)])
+def test_grouped_gemm_small(fmt, d):
+    """Segments of 0 .. 130 rows (two 64-row passes), n not a multiple of the
+    column tile; d = 256 is one narrow slab, 576 / 1056 add a narrow last slab
+    after full ones (metadata read per slab in both shapes)."""
+    say("grouped small", fmt, d)
+    n, n_exp, t = 300, 5, 140
     ws = [synth.affine_weights(900 + e, n, d) if fmt == A else rand_mxfp4(900 + e, n, d) for e in range(n_exp)]
     stk, size = stack(fmt, ws)
     x = synth.activations(901, synth.S_X, t, d)
@@ -318,7 +321,7 @@ def test_grouped_gemm_small(fmt):
     yr, ar = oracle.grouped(x, row_index, seg_expert, seg_offsets, deq)
     for max_rows in (max(sizes), 1):      # MFMA path, then the GEMV path on the same table
         y = run_grouped(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, max_rows)
-        assert_parity(y, yr, ar, f"grouped fmt={fmt} max_rows={max_rows}")
+        assert_parity(y, yr, ar, f"grouped fmt={fmt} d={d} max_rows={max_rows}")
 
 
 def test_grouped_invalid_entries_give_nan():
