@@ -356,10 +356,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   using P1 = std::integral_constant<int, 1>;
   // X slot of step k is k % 4, W slot of step k is k % 3: stage ks reads X
   // slot ks % 4 and W slot (ks + 1) % 3, and fills X slot (ks + 3) % 4 and W
-  // slot ks % 3.  An odd
-  // step count runs one extra stage past d: all its loads are out of range,
-  // so it adds exact zeros (a conditional exit would make the compiler copy
-  // the accumulators every iteration).
+  // slot ks % 3.  An odd step count runs one extra stage past d: all its
+  // loads are out of range, so it adds exact zeros (a conditional exit would
+  // make the compiler copy the accumulators every iteration).
   int s0 = 0;
   for (int ks = 0; ks < nk; ks += 2) {
     const int s1 = s0 == 2 ? 0 : s0 + 1, s2 = s1 == 2 ? 0 : s1 + 1;
