@@ -16,8 +16,11 @@ to change the last bits and is not an error).
 
 Pins (tests/test_oracle.py): the affine worked example, the 36-byte group size,
 the E2M1 value set, exact-rational brute force on tiny shapes, integer-exact
-cases, one-hot columns, row sums and the tolerance checker's self-test.  No
-function here is parity-unpinned.
+cases, one-hot columns, row sums and the tolerance checker's self-test; for the
+router, hand-worked scores and selections on tiny inputs (bias that changes the
+choice, ties to the lower id), a naive per-token full sort, the grouping's
+invariants and literal tables, and the top-k checker's self-test.  No function
+here is parity-unpinned.
 """
 from __future__ import annotations
 
@@ -228,6 +231,112 @@ def sampled(x_bits, w_row, pairs):
         y[i] = prod.sum()
         a[i] = np.abs(prod).sum()
     return y, a
+
+
+# ---------------------------------------------------------------------------
+# Router (MoE prefill): scores, top-k, tokens grouped by expert
+# ---------------------------------------------------------------------------
+
+def route_scores(x_bits, r_bits, bias):
+    """score[t, e] = sigmoid(Σ_j x[t,j]·R[e,j]) + bias[e] in fp64, and
+    A[t, e] = Σ_j |x[t,j]·R[e,j]| (the size of the logit's terms, for the
+    error bound of an fp32 evaluation).
+
+    A sigmoid router whose per-expert bias only corrects the selection (the
+    router with a score-correction bias of Colibri Kimi K3 Metal 后端实现全解析,
+    introduction; sigmoid scoring with 896 routed experts, top-16, in
+    Kimi K3 迁移到 Google TPU 的可行性评估（v2）, §2 模型解剖)."""
+    x = bf16_to_f64(x_bits)
+    r = bf16_to_f64(r_bits)
+    logits = x @ r.T
+    a = np.abs(x) @ np.abs(r).T
+    b = np.zeros(r.shape[0]) if bias is None else np.asarray(bias, np.float64)
+    return 1.0 / (1.0 + np.exp(-logits)) + b[None, :], a
+
+
+def topk(scores, k):
+    """The k experts of each token by score, highest first; equal scores go
+    to the lower expert id.  int64[T, k]."""
+    scores = np.asarray(scores, np.float64)
+    t, e = scores.shape
+    order = np.lexsort((np.broadcast_to(np.arange(e), scores.shape), -scores), axis=1)
+    return order[:, :k].astype(np.int64)
+
+
+def group(topk_ids, n_experts):
+    """Tokens grouped by expert: segment e (one per expert, possibly empty)
+    covers rows [seg_offsets[e], seg_offsets[e+1]) of the grouped order, and
+    row r of that order reads token row_index[r]; inside a segment tokens
+    ascend.  Returns (seg_offsets int32[E + 1], row_index int32[T·k])."""
+    topk_ids = np.asarray(topk_ids)
+    t, k = topk_ids.shape
+    pairs_e = topk_ids.reshape(-1)
+    pairs_t = np.repeat(np.arange(t), k)
+    o = np.lexsort((pairs_t, pairs_e))
+    counts = np.bincount(pairs_e, minlength=n_experts)
+    seg_offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return seg_offsets, pairs_t[o].astype(np.int32)
+
+
+class Routing:
+    """Grouped-expert tables with the empty segments dropped (segment s is
+    expert seg_expert[s]), as the grouped matmul takes them."""
+
+    def __init__(self, topk_ids, n_experts):
+        self.topk = np.asarray(topk_ids)
+        offs, self.row_index = group(self.topk, n_experts)
+        active = np.nonzero(np.diff(offs))[0]
+        self.seg_expert = active.astype(np.int32)
+        self.seg_offsets = np.concatenate([offs[active], [offs[-1]]]).astype(np.int32)
+
+    @property
+    def n_seg(self) -> int:
+        return int(self.seg_expert.shape[0])
+
+    @property
+    def m_total(self) -> int:
+        return int(self.row_index.shape[0])
+
+    @property
+    def max_seg_rows(self) -> int:
+        return int(np.diff(self.seg_offsets).max()) if self.n_seg else 0
+
+
+def route(x_bits, r_bits, bias, k=16):
+    """Top-k routing of every token, grouped by expert (compact segments)."""
+    scores, _ = route_scores(x_bits, r_bits, bias)
+    return Routing(topk(scores, k), np.asarray(r_bits).shape[0])
+
+
+def check_topk(topk_ids, scores, delta) -> dict:
+    """Is a computed top-k a correct top-k for scores known only within
+    ±delta?  Each row must hold k distinct experts, and every chosen expert e
+    and unchosen f must satisfy score[e] + delta[e] + delta[f] >= score[f]
+    (some scores within the error bounds rank e above f); consecutive picks
+    must be in non-increasing order within the same margin.  Where the k-th
+    and (k+1)-th scores are further apart than the margins, this leaves
+    exactly the fp64 choice.  `delta` is per element, shaped like `scores`."""
+    topk_ids = np.asarray(topk_ids, np.int64)
+    scores = np.asarray(scores, np.float64)
+    delta = np.broadcast_to(np.asarray(delta, np.float64), scores.shape)
+    t, k = topk_ids.shape
+    bad_rows = []
+    for i in range(t):
+        ids = topk_ids[i]
+        if len(set(ids.tolist())) != k or ids.min() < 0 or ids.max() >= scores.shape[1]:
+            bad_rows.append(i)
+            continue
+        chosen = np.zeros(scores.shape[1], bool)
+        chosen[ids] = True
+        lo_chosen = np.min(scores[i, ids] + delta[i, ids])
+        hi_other = np.max(scores[i, ~chosen] - delta[i, ~chosen]) if (~chosen).any() else -np.inf
+        ordered = np.all(scores[i, ids[:-1]] + delta[i, ids[:-1]] + delta[i, ids[1:]] >= scores[i, ids[1:]])
+        if lo_chosen < hi_other or not ordered:
+            bad_rows.append(i)
+    ref = topk(scores, k)
+    exact = int(np.sum(np.all(np.sort(ref, 1) == np.sort(topk_ids, 1), axis=1)))
+    return dict(ok=not bad_rows, bad_rows=bad_rows[:10], n_bad=len(bad_rows),
+                rows_equal_to_fp64_choice=exact, rows=t)
 
 
 # ---------------------------------------------------------------------------

@@ -208,59 +208,12 @@ def draw_experts(seed: int, count: int = 16, total: int = 896, sub: int = 0) -> 
     return perm[:count].copy()
 
 
-@dataclasses.dataclass
-class Routing:
-    """Tokens grouped by expert: segment s covers rows [seg_offsets[s],
-    seg_offsets[s+1]) of the grouped order; row r of that order reads token
-    row_index[r]; segments ascend by expert id, rows by token id."""
-    seg_expert: np.ndarray   # int32[S]
-    seg_offsets: np.ndarray  # int32[S + 1]
-    row_index: np.ndarray    # int32[m_total]
-    topk: np.ndarray         # int64[T, k], each token's experts by (score desc, id asc)
-
-    @property
-    def n_seg(self) -> int:
-        return int(self.seg_expert.shape[0])
-
-    @property
-    def m_total(self) -> int:
-        return int(self.row_index.shape[0])
-
-    @property
-    def max_seg_rows(self) -> int:
-        return int(np.diff(self.seg_offsets).max()) if self.n_seg else 0
-
-
 def router_inputs(seed: int, t: int = 512, d: int = 3584, experts: int = 896):
     """X bf16 ~N(0,1)[t, d]; R bf16 ~N(0, 0.02)[experts, d]; bias fp32 ~U[-0.1, 0.1]."""
     x = activations(seed, S_X, t, d)
     r = bf16_bits(0.02 * normal(seed, S_R, 0, experts * d)).reshape(experts, d)
     b = (-0.1 + 0.2 * uniform(seed, S_RBIAS, 0, experts)).astype(np.float32)
     return x, r, b
-
-
-def route(x_bits: np.ndarray, r_bits: np.ndarray, bias: np.ndarray, k: int = 16) -> Routing:
-    """Sigmoid router with a selection-only bias, top-k per token, grouped by expert.
-
-    score[t, e] = sigmoid(sum_j x[t, j] * R[e, j]) + bias[e], in fp64 from the
-    bf16/fp32 inputs; ties in score go to the lower expert id.  Computed once
-    here and handed to both sides as integers, so a near-tie can never route a
-    token differently on the two sides.
-    """
-    x = bf16_to_f32(x_bits).astype(np.float64)
-    r = bf16_to_f32(r_bits).astype(np.float64)
-    logits = x @ r.T
-    score = 1.0 / (1.0 + np.exp(-logits)) + bias.astype(np.float64)[None, :]
-    t, e = score.shape
-    order = np.lexsort((np.broadcast_to(np.arange(e), score.shape), -score), axis=1)
-    topk = order[:, :k]
-    pairs_e = topk.reshape(-1)
-    pairs_t = np.repeat(np.arange(t), k)
-    o = np.lexsort((pairs_t, pairs_e))
-    pairs_e, pairs_t = pairs_e[o], pairs_t[o]
-    seg_expert, counts = np.unique(pairs_e, return_counts=True)
-    seg_offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    return Routing(seg_expert.astype(np.int32), seg_offsets, pairs_t.astype(np.int32), topk)
 
 
 def sha256(*arrays: np.ndarray) -> str:

@@ -389,7 +389,7 @@ def test_moe_prefill_workload_sampled(expert_stacks):
     (gu, gsz), _ = expert_stacks
     seed = synth.seed_of(4)
     xb, rb, bias = synth.router_inputs(seed)
-    rt = synth.route(xb, rb, bias)
+    rt = oracle.route(xb, rb, bias)
     # config 4 reuses config 3's expert weights
     y = run_grouped(M, gu, gsz, 896, 6144, 3584, xb, rt.seg_expert, rt.seg_offsets, rt.row_index,
                     rt.max_seg_rows)

@@ -202,6 +202,83 @@ def pin_checker():
     assert oracle.check(np.array([0x4004], np.uint16), np.array([y_ex]), np.array([a_ex]))["ok"]   # 2.0625
 
 
+def pin_router_hand_worked():
+    """Scores and selections worked by hand.  Token 0 reads feature 0, token 1
+    feature 1; R's rows give logits (2, 0, -1, 2, 0) and (0, 2, -1, 2, 0), and
+    the bias (0, 0, 0, -1/4, 1/2) lifts expert 4 to sigmoid(0) + 1/2 = 1 and
+    pushes expert 3 to sigmoid(2) - 1/4 < sigmoid(2) but > 1/2."""
+    d = 8
+    x = np.zeros((2, d))
+    x[0, 0] = 1.0
+    x[1, 1] = 1.0
+    r = np.zeros((5, d))
+    r[0, 0] = 2.0
+    r[1, 1] = 2.0
+    r[2, :2] = -1.0
+    r[3, :2] = 2.0
+    bias = np.array([0.0, 0.0, 0.0, -0.25, 0.5], np.float32)
+    scores, a = oracle.route_scores(synth.bf16_bits(x), synth.bf16_bits(r), bias)
+    assert scores[0, 1] == 0.5 and scores[1, 0] == 0.5          # sigmoid(0) exactly
+    assert scores[0, 4] == 1.0 and scores[1, 4] == 1.0          # sigmoid(0) + 1/2
+    assert scores[0, 2] < 0.5 and scores[0, 0] > scores[0, 3] > 0.5
+    assert a[0, 3] == 2.0 and a[1, 2] == 1.0                      # Σ|x·r|
+    assert oracle.topk(scores, 3).tolist() == [[4, 0, 3], [4, 1, 3]]
+    # equal scores go to the lower expert id, in the choice and in the order
+    tie = np.array([[0.3, 0.7, 0.7, 0.1, 0.7]])
+    assert oracle.topk(tie, 2).tolist() == [[1, 2]]
+    assert oracle.topk(tie, 4).tolist() == [[1, 2, 4, 0]]
+
+
+def pin_router_full_sort():
+    """The vectorised routing against a naive per-token full sort in Python floats."""
+    import math
+    x, r, bias = synth.router_inputs(1004, t=24, d=256, experts=48)
+    rt = oracle.route(x, r, bias, k=8)
+    xf = [[float(v) for v in row] for row in oracle.bf16_to_f64(x)]
+    rf = [[float(v) for v in row] for row in oracle.bf16_to_f64(r)]
+    for tok in range(24):
+        sc = []
+        for e in range(48):
+            lg = math.fsum(xf[tok][j] * rf[e][j] for j in range(256))
+            sc.append((1.0 / (1.0 + math.exp(-lg)) + float(bias[e]), e))
+        sc.sort(key=lambda p: (-p[0], p[1]))
+        assert [e for _, e in sc[:8]] == rt.topk[tok].tolist()
+
+
+def pin_group_literal():
+    """Grouping written out by hand: token 0 picks experts (1, 0), token 1 (0, 3)."""
+    offs, rows = oracle.group(np.array([[1, 0], [0, 3]]), 4)
+    assert offs.tolist() == [0, 2, 3, 3, 4]         # expert 2 has an empty segment
+    assert rows.tolist() == [0, 1, 0, 1]            # tokens ascend inside a segment
+    rt = oracle.Routing(np.array([[1, 0], [0, 3]]), 4)
+    assert rt.seg_expert.tolist() == [0, 1, 3] and rt.seg_offsets.tolist() == [0, 2, 3, 4]
+    assert rt.max_seg_rows == 2 and rt.m_total == 4
+    # invariants on a routed workload: every token once per chosen expert, segments full
+    x, r, bias = synth.router_inputs(1005, t=40, d=128, experts=32)
+    rt = oracle.route(x, r, bias, k=6)
+    assert rt.m_total == 240 and rt.seg_offsets[-1] == 240
+    seen = {}
+    for s in range(rt.n_seg):
+        rows = rt.row_index[rt.seg_offsets[s]:rt.seg_offsets[s + 1]]
+        assert len(rows) > 0 and np.all(np.diff(rows) > 0)
+        for t in rows:
+            seen.setdefault(int(t), []).append(int(rt.seg_expert[s]))
+    for t in range(40):
+        assert sorted(seen[t]) == sorted(rt.topk[t].tolist())
+
+
+def pin_check_topk():
+    """The top-k acceptance: a clear gap leaves only the exact choice; scores
+    within the margins may come in either order."""
+    scores = np.array([[0.9, 0.5, 0.8, 0.1], [0.6, 0.60001, 0.2, 0.1]])
+    delta = np.full(scores.shape, 1e-4)
+    assert oracle.check_topk([[0, 2], [1, 0]], scores, delta)["ok"]
+    assert oracle.check_topk([[0, 2], [0, 1]], scores, delta)["ok"]      # near tie, swapped
+    assert not oracle.check_topk([[0, 1], [1, 0]], scores, delta)["ok"]  # 0.5 chosen over 0.8
+    assert not oracle.check_topk([[2, 0], [1, 0]], scores, delta)["ok"]  # out of order
+    assert not oracle.check_topk([[0, 0], [1, 0]], scores, delta)["ok"]  # repeated expert
+
+
 def all_pins(golden):
     pin_worked_example(golden)
     pin_nibble_order(golden)
@@ -211,6 +288,10 @@ def all_pins(golden):
     pin_integer_exact()
     pin_one_hot_and_row_sums()
     pin_checker()
+    pin_router_hand_worked()
+    pin_router_full_sort()
+    pin_group_literal()
+    pin_check_topk()
 
 
 # --- tests -----------------------------------------------------------------
@@ -286,6 +367,22 @@ def test_round_to_bf16_matches_scalar_rounding():
     assert np.array_equal(got, ref)
 
 
+def test_router_hand_worked():
+    pin_router_hand_worked()
+
+
+def test_router_full_sort():
+    pin_router_full_sort()
+
+
+def test_group_literal():
+    pin_group_literal()
+
+
+def test_check_topk():
+    pin_check_topk()
+
+
 def test_grouped_and_sampled(golden):
     rng = np.random.default_rng(RNG_SEED + 5)
     e_count, n, d, t = 4, 6, 64, 5
@@ -323,6 +420,16 @@ MUTATIONS = {
         lambda b: orig(b).reshape(-1, 2)[:, ::-1].reshape(orig(b).shape))),
     "checker_too_loose": ("check", lambda orig: (lambda *a, **k: dict(orig(*a, **k), ok=True))),
     "checker_rounds_wrong_way": ("round_to_bf16", lambda orig: (lambda v: orig(v) * (1 + 2.0 ** -6))),
+    "router_bias_ignored": ("route_scores", lambda orig: (lambda x, r, b: orig(x, r, None))),
+    "router_sigmoid_negated": ("route_scores", lambda orig: (
+        lambda x, r, b: (lambda sa: (1.0 - sa[0] + 2 * (0 if b is None else np.asarray(b, np.float64))[None, :], sa[1]))(orig(x, r, b)))),
+    "topk_ties_to_higher_id": ("topk", lambda orig: (
+        lambda s, k: np.lexsort((-np.broadcast_to(np.arange(np.shape(s)[1]), np.shape(s)), -np.asarray(s, np.float64)),
+                                axis=1)[:, :k])),
+    "topk_ascending": ("topk", lambda orig: (lambda s, k: orig(-np.asarray(s, np.float64), k))),
+    "group_tokens_descending": ("group", lambda orig: (
+        lambda tk, e: (lambda o: (o[0], np.concatenate([o[1][o[0][i]:o[0][i + 1]][::-1] for i in range(e)]).astype(np.int32)))(orig(tk, e)))),
+    "check_topk_too_loose": ("check_topk", lambda orig: (lambda *a, **k: dict(orig(*a, **k), ok=True))),
 }
 
 
