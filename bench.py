@@ -8,8 +8,8 @@ in HBM:
   prefill   affine GEMM, T=2048, D=5120, N=13824 (bf16 MFMA)
   moe_dec   MXFP4 grouped GEMV, 16 of 896 experts: gate_up 6144x3584, then
             down 3584x3072 (a fresh expert draw every step)
-  moe_pre   MXFP4 grouped GEMM, 512 tokens routed top-16 over 896 experts,
-            gate_up only
+  moe_pre   routing of 512 tokens, top-16 over 896 experts, on the GPU
+            (qmm_route), then the MXFP4 grouped GEMM (gate_up) on its tables
 Weights of the decode row rotate over enough packed copies (> 2x the 256 MB
 Infinity Cache) that every launch reads HBM, not the cache.  After the timed
 steps, a plain streaming read of the decode row's byte count (qmm_stream_read,
@@ -217,17 +217,29 @@ def main(argv=None) -> int:
              2.0 * 16 * dn_n * dn_d),
         ]
     if "moe_pre" in rows:
+        # routed on the GPU every step (qmm_route), its tables driving the grouped
+        # matmul directly: segments dense over all 896 experts, empty ones included
         seed4 = synth.seed_of(4)
         xb, rb, bias = synth.router_inputs(seed4)
-        rt = synth.route(xb, rb, bias)
-        x4 = T(xb)
-        ri, se, so = T(rt.row_index), T(rt.seg_expert), T(rt.seg_offsets)
-        y4 = torch.empty(rt.m_total, gu_n, dtype=torch.int16, device=dev)
-        b4 = rt.n_seg * (gsz - 256) + 2 * xb.size + 2 * rt.m_total * gu_n
-        moe_pre_info = dict(active_experts=rt.n_seg, routed_rows=rt.m_total, max_seg_rows=rt.max_seg_rows)
-        work["moe_pre"] = [(lambda s: qmm.qmm_grouped_gemm(M, gu, gsz, 896, gu_n, gu_d, x4, xb.shape[0], ri,
-                                                           se, so, rt.n_seg, rt.m_total, rt.max_seg_rows, y4),
-                            "grouped_gemm", b4, 2.0 * rt.m_total * gu_n * gu_d)]
+        t4, ne, k4 = xb.shape[0], rb.shape[0], 16
+        x4, r4, bias4 = T(xb), T(rb), torch.from_numpy(bias).to(dev)
+        scores4 = torch.empty(t4, ne, dtype=torch.float32, device=dev)
+        topk4 = torch.empty(t4, k4, dtype=torch.int32, device=dev)
+        se = torch.empty(ne, dtype=torch.int32, device=dev)
+        so = torch.empty(ne + 1, dtype=torch.int32, device=dev)
+        ri = torch.empty(t4 * k4, dtype=torch.int32, device=dev)
+        route = lambda s: qmm.qmm_route(x4, t4, gu_d, r4, ne, bias4, k4, scores4, topk4, se, so, ri)
+        route(0)
+        sizes = np.diff(so.cpu().numpy())        # setup only: the byte count needs the active experts
+        n_active = int(np.count_nonzero(sizes))
+        y4 = torch.empty(t4 * k4, gu_n, dtype=torch.int16, device=dev)
+        b4 = n_active * (gsz - 256) + 2 * xb.size + 2 * t4 * k4 * gu_n
+        br = 2 * xb.size + 2 * rb.size + 4 * ne + 4 * t4 * ne + 4 * t4 * k4 + 8 * t4 * k4 + 8 * ne
+        moe_pre_info = dict(active_experts=n_active, routed_rows=t4 * k4, max_seg_rows=int(sizes.max()))
+        work["moe_pre"] = [
+            (route, "route", br, 2.0 * t4 * ne * gu_d),
+            (lambda s: qmm.qmm_grouped_gemm(M, gu, gsz, 896, gu_n, gu_d, x4, t4, ri, se, so, ne, t4 * k4,
+                                            t4, y4), "grouped_gemm", b4, 2.0 * t4 * k4 * gu_n * gu_d)]
         log("moe_pre ready", moe_pre_info)
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
@@ -310,7 +322,7 @@ def main(argv=None) -> int:
         "dtype": "bf16", "data": "synthetic (seeded counter-based generator; no weights or datasets)",
         "config": {"workload": synth.CONFIGS[1]["name"], "t": 1, "d": d1, "n": n1,
                    "format": "affine4_g64", "rotation_copies": args.rotate,
-                   "step": "decode GEMV + prefill GEMM + MoE decode grouped GEMV x2 + MoE prefill grouped GEMM"
+                   "step": "decode GEMV + prefill GEMM + MoE decode grouped GEMV x2 + MoE prefill route + grouped GEMM"
                    if rows == ["decode", "prefill", "moe_dec", "moe_pre"] else ",".join(rows)},
     }
     if "gemv" in results:

@@ -16,7 +16,7 @@ __all__ = [
     "QMM_AFFINE4_G64", "QMM_MXFP4_G32", "QmmError", "lib_path", "load",
     "qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
     "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
-    "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "EXPORTS",
+    "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route", "EXPORTS",
 ]
 
 QMM_AFFINE4_G64 = 1
@@ -27,7 +27,7 @@ STATUS = {0: "QMM_OK", 1: "QMM_E_ARG", 2: "QMM_E_SHAPE", 3: "QMM_E_ALIGN", 4: "Q
 
 EXPORTS = ("qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
            "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
-           "qmm_layout_version", "qmm_profile_next", "qmm_stream_read")
+           "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -69,6 +69,7 @@ def load():
         "qmm_layout_version": (ctypes.c_uint32, []),
         "qmm_profile_next": (ctypes.c_int, [vp, vp]),
         "qmm_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
+        "qmm_route": (ctypes.c_int, [vp, i64, i64, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -139,6 +140,13 @@ def qmm_profile_next(start_event, stop_event):
 def qmm_stream_read(src, nbytes, sink, stream=None):
     """Read `nbytes` of device memory once (measurement of the HBM read ceiling)."""
     _check(load().qmm_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "qmm_stream_read")
+
+
+def qmm_route(x, t, d, r, n_experts, bias, k, scores, topk, seg_expert, seg_offsets, row_index,
+              stream=None):
+    _check(load().qmm_route(_ptr(x), t, d, _ptr(r), n_experts, _ptr(bias), k, _ptr(scores), _ptr(topk),
+                            _ptr(seg_expert), _ptr(seg_offsets), _ptr(row_index), _stream(stream)),
+           "qmm_route")
 
 
 def qmm_pack(fmt, n, d, codes, scales, biases, packed, stream=None):

@@ -65,6 +65,29 @@ size_t qmm_workspace_bytes(qmm_format, int64_t, int64_t, int64_t) { return 0; }
 
 uint32_t qmm_layout_version(void) { return qmm::kLayoutVersion; }
 
+qmm_status qmm_route(const qmm_bf16* x, int64_t t, int64_t d, const qmm_bf16* r, int32_t n_experts,
+                     const float* bias, int32_t k, float* scores, int32_t* topk,
+                     int32_t* seg_expert, int32_t* seg_offsets, int32_t* row_index, void* stream) {
+  g_last_error[0] = 0;
+  if (!x || !r || !scores || !topk || !seg_expert || !seg_offsets || !row_index)
+    return fail(QMM_E_ARG, "NULL pointer");
+  if (t < 1 || n_experts < 1 || k < 1) return fail(QMM_E_ARG, "t, n_experts and k must be >= 1");
+  if (n_experts > qmm::kRouteMaxExperts) return fail(QMM_E_SHAPE, "n_experts must be <= 1024");
+  if (k > qmm::kRouteMaxK || k > n_experts) return fail(QMM_E_SHAPE, "k must be <= min(64, n_experts)");
+  if (d < 8 || d % 8 || d > qmm::kMaxD) return fail(QMM_E_SHAPE, "d must be a multiple of 8 in [8, 65536]");
+  if (t * d * 2 >= (int64_t(1) << 31) || int64_t(n_experts) * d * 2 >= (int64_t(1) << 31))
+    return fail(QMM_E_SHAPE, "x and r must each be under 2 GiB");
+  if (t * k >= (int64_t(1) << 30)) return fail(QMM_E_SHAPE, "t*k must be below 2^30");
+  if (!aligned(x, 16) || !aligned(r, 16)) return fail(QMM_E_ALIGN, "x and r must be 16-byte aligned");
+  if (!aligned(scores, 4) || !aligned(topk, 4) || !aligned(seg_expert, 4) || !aligned(seg_offsets, 4) ||
+      !aligned(row_index, 4) || (bias && !aligned(bias, 4)))
+    return fail(QMM_E_ALIGN, "scores, bias and the tables must be 4-byte aligned");
+  qmm::RouteArgs a{x, int(t), int(d), r, n_experts, bias, k, scores, topk, seg_expert, seg_offsets, row_index};
+  int err = qmm::launch_route(a, stream);
+  if (err) return hip_fail(err, "qmm_route");
+  return QMM_OK;
+}
+
 qmm_status qmm_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
   g_last_error[0] = 0;
   if (!src || !sink) return fail(QMM_E_ARG, "NULL pointer");

@@ -198,6 +198,23 @@ struct GemmArgs {
 int launch_gemm(const GemmArgs& a, void* stream);
 int launch_grouped_gemm(const GemmArgs& a, void* stream);
 
+struct RouteArgs {
+  const uint16_t* x;   // [t, d] bf16
+  int t, d;
+  const uint16_t* r;   // [ne, d] bf16
+  int ne;
+  const float* bias;   // [ne] or NULL
+  int k;
+  float* scores;       // [t, ne]
+  int32_t* topk;       // [t, k]
+  int32_t* seg_expert;   // [ne]
+  int32_t* seg_offsets;  // [ne + 1]
+  int32_t* row_index;    // [t * k]
+};
+constexpr int kRouteMaxExperts = 1024;
+constexpr int kRouteMaxK = 64;
+int launch_route(const RouteArgs& a, void* stream);
+
 // read-only streaming kernel (measurement support): kStreamBlocks workgroups
 constexpr int kStreamBlocks = 2048;
 int launch_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);

@@ -143,9 +143,39 @@ qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expe
                             int32_t max_seg_rows, qmm_bf16* y, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* MoE router (the step before qmm_grouped_gemm for routed prefill): a sigmoid
+ * router with a selection-only bias, top-k per token, tokens grouped by expert
+ * ("Colibri Kimi K3 Metal 后端实现全解析", introduction: router with a
+ * score-correction bias; "Kimi K3 迁移到 Google TPU 的可行性评估（v2）", §2:
+ * sigmoid scoring, top-16 of 896 routed experts).
+ *   x        bf16 [t][d], row-major, device, 16-byte aligned
+ *   r        bf16 [n_experts][d], the router weights, device, 16-byte aligned
+ *   bias     fp32 [n_experts], device, or NULL for none; it changes which
+ *            experts are chosen, never a score's use elsewhere
+ *   scores   fp32 [t][n_experts], device, written: sigmoid(x·rᵀ) + bias,
+ *            products accumulated in fp32
+ *   topk     int32 [t][k], device, written: each token's experts, highest
+ *            score first, equal scores to the lower expert id; -inf scores
+ *            rank below every finite one and NaN below -inf (-0 equals +0)
+ *   seg_expert  int32 [n_experts], written 0 .. n_experts-1
+ *   seg_offsets int32 [n_experts + 1], written: segment e (expert e, possibly
+ *            empty) covers grouped rows [seg_offsets[e], seg_offsets[e+1])
+ *   row_index   int32 [t*k], written: the tokens of each segment, ascending
+ * The three tables feed qmm_grouped_gemm directly (n_seg = n_experts,
+ * m_total = t*k, max_seg_rows = t): no count has to come back to the host.
+ * Limits: t >= 1; 1 <= n_experts <= 1024; 1 <= k <= min(64, n_experts);
+ * d a multiple of 8, 8 <= d <= 65536; t*d*2 and n_experts*d*2 below 2^31;
+ * t*k below 2^30 (QMM_E_SHAPE / QMM_E_ARG / QMM_E_ALIGN otherwise, nothing
+ * launched).  Three kernel launches on `stream`, asynchronous; armed
+ * profiling events bracket all three.  The library allocates nothing. */
+qmm_status qmm_route(const qmm_bf16* x, int64_t t, int64_t d, const qmm_bf16* r, int32_t n_experts,
+                     const float* bias, int32_t k, float* scores, int32_t* topk,
+                     int32_t* seg_expert, int32_t* seg_offsets, int32_t* row_index, void* stream);
+
 /* Per-kernel GPU timing (per-op GPU timestamps, as in the op profiling of
  * "LLM Decode / Prefill 优化案例（Metal）", Step 1).  Arms two caller-owned
- * hipEvent_t handles for the next qmm_gemv / qmm_gemm / qmm_grouped_gemm call
+ * hipEvent_t handles for the next qmm_gemv / qmm_gemm / qmm_grouped_gemm /
+ * qmm_route / qmm_stream_read call
  * on this thread: its kernel is launched with hipExtLaunchKernel so `start`
  * and `stop` are stamped by the dispatch itself, and their elapsed time is
  * the kernel's execution time.  Either may be NULL.  The arming is consumed

@@ -105,6 +105,15 @@ def test_validation_errors_before_any_launch():
     expect(E_SHAPE, g, A, P, blob, 2, 16, 64, P, 4, P, P, P, 70000, 4, 4, P, None, 0)  # n_seg
     expect(E_ALIGN, g, A, P, blob, 2, 16, 64, P, 4, P + 2, P, P, 1, 4, 4, P, None, 0)
     assert "aligned" in qmm.qmm_last_error()
+    ro = qmm.qmm_route
+    expect(E_ARG, ro, None, 4, 64, P, 8, None, 2, P, P, P, P, P, 0)         # NULL x
+    expect(E_ARG, ro, P, 0, 64, P, 8, None, 2, P, P, P, P, P, 0)            # t = 0
+    expect(E_SHAPE, ro, P, 4, 64, P, 1025, None, 2, P, P, P, P, P, 0)       # too many experts
+    expect(E_SHAPE, ro, P, 4, 64, P, 8, None, 9, P, P, P, P, P, 0)          # k > n_experts
+    expect(E_SHAPE, ro, P, 4, 60, P, 8, None, 2, P, P, P, P, P, 0)          # d % 8
+    expect(E_SHAPE, ro, P, 1 << 24, 8, P, 64, None, 64, P, P, P, P, P, 0)   # t*k = 2^30
+    expect(E_ALIGN, ro, P + 8, 4, 64, P, 8, None, 2, P, P, P, P, P, 0)      # x 16-byte
+    expect(E_ALIGN, ro, P, 4, 64, P, 8, P + 2, 2, P, P, P, P, P, 0)         # bias 4-byte
     s = qmm.qmm_stream_read
     expect(E_ARG, s, None, 1024, P, 0)
     expect(E_ARG, s, P, 1024, None, 0)

@@ -447,3 +447,120 @@ def test_stream_read_reads_every_byte():
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(words)
+
+
+# ---------------------------------------------------------------------------
+# Router
+# ---------------------------------------------------------------------------
+
+def run_route(x_bits, r_bits, bias, k):
+    t, d = x_bits.shape
+    ne = r_bits.shape[0]
+    scores = torch.full((t, ne), float("nan"), device=DEV)
+    topk = torch.full((t, k), -1, dtype=torch.int32, device=DEV)
+    seg_e = torch.full((ne,), -1, dtype=torch.int32, device=DEV)
+    seg_o = torch.full((ne + 1,), -1, dtype=torch.int32, device=DEV)
+    rows = torch.full((t * k,), -1, dtype=torch.int32, device=DEV)
+    qmm.qmm_route(dev(x_bits), t, d, dev(r_bits), ne, None if bias is None else dev(bias), k,
+                  scores, topk, seg_e, seg_o, rows)
+    torch.cuda.synchronize()
+    return (scores.cpu().numpy().astype(np.float64), topk.cpu().numpy(), seg_e.cpu().numpy(),
+            seg_o.cpu().numpy(), rows.cpu().numpy())
+
+
+def score_bound(a_ref, d):
+    """Error bound of an fp32 score: the logit's products are exact in fp32 and
+    are summed in 32-wide MFMA blocks (a tree of at most 5 roundings), the
+    blocks accumulate in eight interleaved chains of at most d/32 steps in all,
+    and the eight chain sums are added in sequence (7 roundings), so
+    |logit error| <= n·u·Σ|x·r| with n = d/32 + 12 and u = 2^-24, doubled for
+    margin; the sigmoid's slope is at most 1/4, and its fp32 evaluation plus
+    the bias add cost a few ulps of 1."""
+    gamma = 2.0 * (d / 32 + 12) * 2.0 ** -24
+    return 0.25 * gamma * a_ref + 1e-6
+
+
+def check_route(x, r, bias, k, what):
+    s_gpu, tk, seg_e, seg_o, rows = run_route(x, r, bias, k)
+    s_ref, a_ref = oracle.route_scores(x, r, bias)
+    delta = score_bound(a_ref, x.shape[1])
+    err = np.abs(s_gpu - s_ref)
+    say(what, dict(max_err=float(err.max()), max_err_over_bound=float((err / delta).max())))
+    assert np.all(err <= delta), what
+    res = oracle.check_topk(tk, s_ref, delta)
+    say(what, {kk: res[kk] for kk in ("n_bad", "rows_equal_to_fp64_choice", "rows")})
+    assert res["ok"], (what, res)
+    offs, ridx = oracle.group(tk, r.shape[0])        # exact, given the GPU's own choice
+    assert np.array_equal(seg_e, np.arange(r.shape[0])), what
+    assert np.array_equal(seg_o, offs) and np.array_equal(rows, ridx), what
+    return tk, seg_o, rows
+
+
+@pytest.mark.parametrize("t,d,ne,k", [(48, 256, 96, 16), (70, 136, 100, 5), (1, 8, 1, 1),
+                                      (130, 512, 1024, 64), (9, 1024, 65, 64)])
+def test_route_small(t, d, ne, k):
+    say("route", t, d, ne, k)
+    x, r, bias = synth.router_inputs(7000 + t, t=t, d=d, experts=ne)
+    check_route(x, r, bias, k, f"route {t}x{d} over {ne} top-{k}")
+
+
+def test_route_ties_go_to_the_lower_id():
+    """Experts with identical router rows and bias score identically (same
+    arithmetic in every lane), so the choice among them is fixed by the id."""
+    say("route ties")
+    x, r, bias = synth.router_inputs(7100, t=20, d=128, experts=40)
+    r = r.copy()
+    bias = bias.copy()
+    for e in (7, 19, 33):                      # three copies of expert 3
+        r[e] = r[3]
+        bias[e] = bias[3]
+    s_gpu, tk, _, _, _ = run_route(x, r, bias, 12)
+    assert np.all(s_gpu[:, [7, 19, 33]] == s_gpu[:, [3]])
+    for row in tk:
+        picked = [e for e in row.tolist() if e in (3, 7, 19, 33)]
+        assert picked == sorted(picked)          # listed in id order
+        assert picked == [3, 7, 19, 33][:len(picked)]   # the lowest ids are the ones taken
+
+
+def test_route_non_finite_scores_rank_last():
+    """A bias of -inf or NaN: those experts come after every finite score, -inf
+    before NaN, each class in id order -- over 100 experts, so two keys per
+    lane, and k = 64 reaches into all three classes."""
+    say("route non-finite")
+    x, r, bias = synth.router_inputs(7200, t=24, d=256, experts=100)
+    ids = np.random.default_rng(7201).permutation(100)
+    fin, ninf, nan = ids[:44], ids[44:54], ids[54:]
+    bias = bias.copy()
+    bias[fin] = 2.0 * np.arange(44, 0, -1)         # spaced wider than the sigmoid's range
+    bias[ninf] = -np.inf
+    bias[nan] = np.nan
+    s_gpu, tk, seg_e, seg_o, rows = run_route(x, r, bias, 64)
+    assert np.all(np.isneginf(s_gpu[:, ninf])) and np.all(np.isnan(s_gpu[:, nan]))
+    assert np.all(np.isfinite(s_gpu[:, fin]))
+    want = fin.tolist() + sorted(ninf.tolist()) + sorted(nan.tolist())[:10]
+    assert all(row.tolist() == want for row in tk)
+    sref = oracle.route_scores(x, r, bias)[0]
+    assert all(row.tolist() == want for row in oracle.topk(sref, 64))
+    offs, rws = oracle.group(tk, 100)
+    assert np.array_equal(seg_e, np.arange(100))
+    assert np.array_equal(seg_o, offs) and np.array_equal(rows, rws)
+
+
+def test_route_prefill_workload_then_grouped_gemm(expert_stacks):
+    """512 tokens x 3584 routed top-16 over 896 experts on the GPU, every score
+    and choice checked; the tables then drive the grouped matmul directly
+    (dense segments, empty ones included), sampled against the oracle."""
+    say("route prefill workload")
+    (gu, gsz), _ = expert_stacks
+    xb, rb, bias = synth.router_inputs(synth.seed_of(4))
+    tk, seg_o, rows = check_route(xb, rb, bias, 16, "route 512x3584 over 896 top-16")
+    y = run_grouped(M, gu, gsz, 896, 6144, 3584, xb, np.arange(896), seg_o, rows, 512)
+    sizes = np.diff(seg_o)
+    assert not np.any(y == NAN16)
+    rng = np.random.default_rng(11)
+    active = np.nonzero(sizes)[0]
+    for e in sorted({int(active[np.argmax(sizes[active])]), *rng.choice(active, 5, replace=False).tolist()}):
+        r0, r1 = int(seg_o[e]), int(seg_o[e + 1])
+        g = synth.expert_gate_up(synth.seed_of(3), e)
+        yr, ar = oracle.gemm_mxfp4(xb[rows[r0:r1]], g.codes, g.e8m0)
+        assert_parity(y[r0:r1], yr, ar, f"routed expert {e} rows {r1 - r0}")

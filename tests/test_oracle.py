@@ -245,6 +245,15 @@ def pin_router_full_sort():
         assert [e for _, e in sc[:8]] == rt.topk[tok].tolist()
 
 
+def pin_topk_non_finite():
+    """Worked row: 2.0 first; the two 0.5 by id; -0 and +0 equal, by id; then
+    -1.0; -inf after every finite score; NaN last, by id."""
+    nan, inf = float("nan"), float("inf")
+    row = np.array([[0.5, -inf, nan, 0.5, -0.0, 0.0, -inf, 2.0, nan, -1.0]])
+    assert oracle.topk(row, 10)[0].tolist() == [7, 0, 3, 4, 5, 9, 1, 6, 2, 8]
+    assert oracle.topk(row, 3)[0].tolist() == [7, 0, 3]
+
+
 def pin_group_literal():
     """Grouping written out by hand: token 0 picks experts (1, 0), token 1 (0, 3)."""
     offs, rows = oracle.group(np.array([[1, 0], [0, 3]]), 4)
@@ -373,6 +382,10 @@ def test_router_hand_worked():
 
 def test_router_full_sort():
     pin_router_full_sort()
+
+
+def test_topk_non_finite():
+    pin_topk_non_finite()
 
 
 def test_group_literal():
