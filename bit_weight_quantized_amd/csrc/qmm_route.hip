@@ -6,17 +6,17 @@
 //
 // Three launches on the caller's stream, no workspace:
 //   1. scores[t, e] = sigmoid(Σ_j x[t,j]·R[e,j]) + bias[e] in fp32: one
-//      workgroup per 32 tokens × 32 experts, its four waves splitting d and
+//      workgroup per 32 tokens × 32 experts, its eight waves splitting d and
 //      staging their pieces through LDS, v_mfma_f32_16x16x32_bf16 with fp32
-//      accumulation;
+//      accumulation, tiles ordered so each XCD reads a slice of x and R;
 //   2. top-k per token: one wave per token holds the token's scores in
 //      registers (up to 16 per lane) as order-preserving integer keys and
 //      takes k rounds of a wave-wide maximum (DPP within rows of 16 lanes,
 //      then across rows in scalar registers), equal keys going to the lower
 //      expert id;
 //   3. grouping, one workgroup: per-expert counts with LDS atomics (order free),
-//      an exclusive scan into seg_offsets, then tokens in blocks of 256: each
-//      assignment sets its bit in an LDS bitmap [expert][256 tokens], and the
+//      an exclusive scan into seg_offsets, then tokens in blocks of 512: each
+//      assignment sets its bit in an LDS bitmap [expert][512 tokens], and the
 //      thread of expert e writes the set bits in ascending token order behind
 //      its cursor -- so row_index lists each expert's tokens ascending, with no
 //      dependence on thread timing.
@@ -36,39 +36,58 @@ namespace {
 constexpr uint32_t kOOBr = 0x80000000u;   // buffer offset past every range: reads zero
 
 // ---- 1. scores ----
-// One workgroup per 32 tokens × 32 experts (2 × 2 blocks of 16 × 16); its four
-// waves take interleaved 128-code pieces of d (wave w: pieces w, w + 4, ...).
-// The MFMA operand layout puts 16 different rows on adjacent lanes, which
-// global loads serve poorly (rows are d·2 bytes apart), so each wave stages
-// its pieces through a private LDS region: global loads with 16 lanes on
-// each row's 256 contiguous bytes, then ds_read_b128 in operand layout.  The
-// region is the wave's own, so no barrier is needed until the end, where
-// each wave adds the four partial sums of one block in wave order through
-// LDS -- the result does not depend on timing.
+// One workgroup per 32 tokens × 32 experts (2 × 2 blocks of 16 × 16); its
+// eight waves take interleaved 64-code pieces of d (wave w: pieces w, w + 8,
+// ...).  The MFMA operand layout puts 16 different rows on adjacent lanes,
+// which global loads serve poorly (rows are d·2 bytes apart), so each wave
+// stages its pieces through a private LDS region: global loads with 8 lanes
+// on each row's 128 contiguous bytes, then ds_read_b128 in operand layout.
+// The region is the wave's own, so no barrier is needed until the end, where
+// waves 0-3 each add the eight partial sums of one block in wave order
+// through LDS -- the result does not depend on timing.
+//
+// Tile order: workgroups are dealt round-robin to the 8 XCDs, and XCD k
+// takes one cell of an a × (8/a) split of the token-tile × expert-tile grid
+// (a chosen on the host), so each XCD's L2 holds a slice of x and of R
+// instead of every XCD streaming all of R.
 constexpr int kRT = 32;                 // tokens and experts per workgroup
-constexpr int kRPiece = 128;            // codes per piece
+constexpr int kRWaves = 8;
+constexpr int kRPiece = 64;             // codes per piece
 constexpr int kRRows = 2 * kRT;         // staged rows per piece: tokens, then experts
-constexpr int kRLoads = kRRows / 4;     // b128 loads per lane per piece (4 rows each)
-constexpr int kRRowLds = 2 * kRPiece + 16;  // padded LDS row (bytes)
+constexpr int kRLanesRow = kRPiece * 2 / 16;   // lanes per staged row (16 B each)
+constexpr int kRRowsLoad = 64 / kRLanesRow;    // rows per b128 load instruction
+constexpr int kRLoads = kRRows / kRRowsLoad;   // b128 loads per lane per piece
+constexpr int kRRowLds = 2 * kRPiece + 16;     // padded LDS row (bytes)
 constexpr int kRWaveLds = kRRows * kRRowLds;
 
-__global__ __launch_bounds__(256) void route_scores_kernel(const uint16_t* __restrict__ x, int t,
-                                                           int d, const uint16_t* __restrict__ r,
-                                                           int ne, const float* __restrict__ bias,
-                                                           float* __restrict__ scores) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * kRWaveLds];
+__global__ __launch_bounds__(64 * kRWaves) void route_scores_kernel(
+    const uint16_t* __restrict__ x, int t, int d, const uint16_t* __restrict__ r, int ne,
+    const float* __restrict__ bias, float* __restrict__ scores, int tiles_t, int tiles_e,
+    int split_t) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kRWaves * kRWaveLds];
+  // this workgroup's tile: XCD k = id mod 8 owns cell (k mod a, k / a)
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int split_e = 8 / split_t;
+  const int ct = xcd % split_t, ce = xcd / split_t;
+  const int ts = ct * tiles_t / split_t, te_ = (ct + 1) * tiles_t / split_t;
+  const int es = ce * tiles_e / split_e, ee_ = (ce + 1) * tiles_e / split_e;
+  const int nt = te_ - ts;
+  if (local >= nt * (ee_ - es)) return;   // whole workgroup, before any barrier
+  const int t0 = (ts + local % nt) * kRT, e0 = (es + local / nt) * kRT;
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: loop control stays scalar
   const int col = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * kRT, e0 = blockIdx.y * kRT;
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(x, uint32_t(t) * uint32_t(d) * 2u);
   const __amdgpu_buffer_rsrc_t rr = make_rsrc(r, uint32_t(ne) * uint32_t(d) * 2u);
-  // staging: load i covers rows 4i + g (g = lane >> 4), bytes 16·col .. +15 of
-  // the row's piece; rows 0-31 are tokens t0.., rows 32-63 experts e0..
+  // staging: load i covers row kRRowsLoad·i + (lane / kRLanesRow), bytes
+  // 16·(lane mod kRLanesRow) .. +15 of the row's piece; rows 0-31 are tokens
+  // t0 .., rows 32-63 experts e0 ..
+  const int srow = lane / kRLanesRow, sc = lane % kRLanesRow;
   uint32_t rowoff[kRLoads];
 #pragma unroll
   for (int i = 0; i < kRLoads; ++i) {
-    const int row = 4 * i + g;
+    const int row = kRRowsLoad * i + srow;
     if (i < kRLoads / 2) {
       const int tt = t0 + row;
       rowoff[i] = tt < t ? uint32_t(tt) * uint32_t(d) * 2u : kOOBr;
@@ -78,12 +97,12 @@ __global__ __launch_bounds__(256) void route_scores_kernel(const uint16_t* __res
     }
   }
   auto load_piece = [&](u32x4_t (&v)[kRLoads], int piece) {
-    const int k = piece * kRPiece + 8 * col;
+    const int k = piece * kRPiece + 8 * sc;
     const bool kin = k < d;
 #pragma unroll
     for (int i = 0; i < kRLoads; ++i) {
       const uint32_t off = (kin ? rowoff[i] + 2u * uint32_t(k) : kOOBr) | (rowoff[i] & kOOBr);
-      v[i] = buf_load16(i < kRLoads / 2 ? xr : rr, off);   // rows 4i + g < 32: tokens
+      v[i] = buf_load16(i < kRLoads / 2 ? xr : rr, off);   // first half: token rows
     }
   };
   unsigned char* my = lds + wave * kRWaveLds;
@@ -94,7 +113,7 @@ __global__ __launch_bounds__(256) void route_scores_kernel(const uint16_t* __res
   auto stage_and_compute = [&](const u32x4_t (&v)[kRLoads]) {
 #pragma unroll
     for (int i = 0; i < kRLoads; ++i)
-      *reinterpret_cast<u32x4_t*>(my + (4 * i + g) * kRRowLds + 16 * col) = v[i];
+      *reinterpret_cast<u32x4_t*>(my + (kRRowsLoad * i + srow) * kRRowLds + 16 * sc) = v[i];
 #pragma unroll
     for (int u = 0; u < kRPiece / 32; ++u) {
       bf16x8_t a[2], b[2];
@@ -110,20 +129,20 @@ __global__ __launch_bounds__(256) void route_scores_kernel(const uint16_t* __res
           acc[2 * bi + bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[bi], b[bj], acc[2 * bi + bj], 0, 0, 0);
     }
   };
-  // two pieces in flight, one loop shape: a piece past the end loads zeros,
-  // which add nothing (at most one such piece is staged per wave)
+  // Two pieces in flight, one loop shape: a piece past the end loads zeros,
+  // which add nothing (at most one such piece is staged per wave).  Loads
+  // complete in issue order, so they are issued in the order they are staged
+  // (the scheduling barriers keep the scheduler from swapping batches).
   u32x4_t v0[kRLoads], v1[kRLoads];
-  // loads complete in issue order, so they are issued in the order they are
-  // staged (the scheduling barriers keep the scheduler from swapping batches)
   load_piece(v0, wave);
   __builtin_amdgcn_sched_barrier(0);
-  load_piece(v1, wave + 4);
-  for (int p = wave; p < npieces; p += 8) {
+  load_piece(v1, wave + kRWaves);
+  for (int p = wave; p < npieces; p += 2 * kRWaves) {
     stage_and_compute(v0);
-    load_piece(v0, p + 8);
+    load_piece(v0, p + 2 * kRWaves);
     __builtin_amdgcn_sched_barrier(0);
     stage_and_compute(v1);
-    load_piece(v1, p + 12);
+    load_piece(v1, p + 3 * kRWaves);
     __builtin_amdgcn_sched_barrier(0);
   }
   __syncthreads();   // every wave is done with its staging region
@@ -131,10 +150,11 @@ __global__ __launch_bounds__(256) void route_scores_kernel(const uint16_t* __res
 #pragma unroll
   for (int b = 0; b < 4; ++b) part[(wave * 4 + b) * 64 + lane] = acc[b];
   __syncthreads();
+  if (wave >= 4) return;
   // wave w finishes block w: tokens t0 + 16 (w >> 1) + 4g + i, expert e0 + 16 (w & 1) + col
   f32x4_t sum = part[wave * 64 + lane];
 #pragma unroll
-  for (int w = 1; w < 4; ++w) {
+  for (int w = 1; w < kRWaves; ++w) {
     const f32x4_t q = part[(w * 4 + wave) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sum[i] += q[i];
@@ -221,7 +241,8 @@ __global__ __launch_bounds__(64) void route_topk_kernel(const float* __restrict_
 }
 
 // ---- 3. grouping ----
-constexpr int kGroupBlock = 256;   // tokens per bitmap pass
+constexpr int kGroupBlock = 512;   // tokens per bitmap pass
+constexpr int kGroupCache = 16;    // top-k entries a thread holds when t·k <= 1024·16
 
 __global__ __launch_bounds__(1024) void route_group_kernel(const int32_t* __restrict__ topk, int t,
                                                            int ne, int k,
@@ -233,19 +254,33 @@ __global__ __launch_bounds__(1024) void route_group_kernel(const int32_t* __rest
   __shared__ int32_t wsum[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int na = t * k;   // below 2^30
+  // Small tables (the usual case) are read once, all loads in flight together,
+  // and kept in registers for both passes; larger ones are streamed per pass
+  // with four loads in flight.  Loads past the end re-read the last entry and
+  // are not used.  Ids outside [0, ne) are skipped in the counts and the
+  // bitmaps alike, so no cursor can pass its segment's end.
+  const bool cached = na <= 1024 * kGroupCache;
+  int32_t ent[kGroupCache];
+  if (cached) {
+#pragma unroll
+    for (int u = 0; u < kGroupCache; ++u) ent[u] = topk[min(tid + 1024 * u, na - 1)];
+  }
   cnt[tid] = 0;
   __syncthreads();
-  const int na = t * k;   // below 2^30
-  // four loads in flight per thread; the ones past the end re-read the last
-  // entry and are not counted.  Ids outside [0, ne) are skipped here and in
-  // the bitmap alike, so no cursor can pass its segment's end.
-  for (int i0 = tid; i0 < na; i0 += 4096) {
-    int32_t e[4];
+  if (cached) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) e[u] = topk[min(i0 + 1024 * u, na - 1)];
+    for (int u = 0; u < kGroupCache; ++u)
+      if (tid + 1024 * u < na && uint32_t(ent[u]) < uint32_t(ne)) atomicAdd(&cnt[ent[u]], 1);
+  } else {
+    for (int i0 = tid; i0 < na; i0 += 4096) {
+      int32_t e[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (i0 + 1024 * u < na && uint32_t(e[u]) < uint32_t(ne)) atomicAdd(&cnt[e[u]], 1);
+      for (int u = 0; u < 4; ++u) e[u] = topk[min(i0 + 1024 * u, na - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (i0 + 1024 * u < na && uint32_t(e[u]) < uint32_t(ne)) atomicAdd(&cnt[e[u]], 1);
+    }
   }
   __syncthreads();
   // exclusive scan of cnt[0 .. 1024): within waves, then across the 16 waves
@@ -274,16 +309,27 @@ __global__ __launch_bounds__(1024) void route_group_kernel(const int32_t* __rest
     __syncthreads();
     const int nb = min(kGroupBlock, t - b0);
     const int nab = nb * k, base = b0 * k;
-    for (int i0 = tid; i0 < nab; i0 += 4096) {
-      int32_t e[4];
+    if (cached) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) e[u] = topk[base + min(i0 + 1024 * u, nab - 1)];
+      for (int u = 0; u < kGroupCache; ++u) {
+        const int il = tid + 1024 * u - base;   // entry index inside this block
+        if (il >= 0 && il < nab && uint32_t(ent[u]) < uint32_t(ne)) {
+          const int tl = il / k;
+          atomicOr(&bits[ent[u]][tl >> 5], 1u << (tl & 31));
+        }
+      }
+    } else {
+      for (int i0 = tid; i0 < nab; i0 += 4096) {
+        int32_t e[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + 1024 * u;
-        if (i < nab && uint32_t(e[u]) < uint32_t(ne)) {
-          const int tl = i / k;
-          atomicOr(&bits[e[u]][tl >> 5], 1u << (tl & 31));
+        for (int u = 0; u < 4; ++u) e[u] = topk[base + min(i0 + 1024 * u, nab - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int il = i0 + 1024 * u;
+          if (il < nab && uint32_t(e[u]) < uint32_t(ne)) {
+            const int tl = il / k;
+            atomicOr(&bits[e[u]][tl >> 5], 1u << (tl & 31));
+          }
         }
       }
     }
@@ -311,8 +357,21 @@ int launch_route(const RouteArgs& a, void* stream) {
   // first dispatch, stop by the last
   const ProfileEvents pe = take_profile_events();
   const hipEvent_t ev0 = static_cast<hipEvent_t>(pe.start), ev1 = static_cast<hipEvent_t>(pe.stop);
-  hipExtLaunchKernelGGL(route_scores_kernel, dim3(unsigned((a.t + kRT - 1) / kRT), unsigned((a.ne + kRT - 1) / kRT)),
-                        dim3(256), 0, s, ev0, nullptr, 0, a.x, a.t, a.d, a.r, a.ne, a.bias, a.scores);
+  // XCD split: the a × (8/a) cell grid with the fewest workgroups per XCD,
+  // then the fewest rows (bytes of x and R) per XCD
+  const int tiles_t = (a.t + kRT - 1) / kRT, tiles_e = (a.ne + kRT - 1) / kRT;
+  int split_t = 1;
+  int64_t best_cells = -1, best_rows = 0;
+  for (int st = 1; st <= 8; st *= 2) {
+    const int64_t ct = (tiles_t + st - 1) / st, ce = (tiles_e + 8 / st - 1) / (8 / st);
+    if (best_cells < 0 || ct * ce < best_cells || (ct * ce == best_cells && ct + ce < best_rows)) {
+      best_cells = ct * ce;
+      best_rows = ct + ce;
+      split_t = st;
+    }
+  }
+  hipExtLaunchKernelGGL(route_scores_kernel, dim3(unsigned(8 * best_cells)), dim3(64 * kRWaves), 0, s, ev0,
+                        nullptr, 0, a.x, a.t, a.d, a.r, a.ne, a.bias, a.scores, tiles_t, tiles_e, split_t);
   int err = int(hipGetLastError());
   if (err) return err;
   hipLaunchKernelGGL(route_topk_kernel, dim3(unsigned(a.t)), dim3(64), 0, s,

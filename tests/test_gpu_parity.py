@@ -497,7 +497,9 @@ def check_route(x, r, bias, k, what):
 
 
 @pytest.mark.parametrize("t,d,ne,k", [(48, 256, 96, 16), (70, 136, 100, 5), (1, 8, 1, 1),
-                                      (130, 512, 1024, 64), (9, 1024, 65, 64)])
+                                      (130, 512, 1024, 64), (9, 1024, 65, 64),
+                                      (1000, 64, 96, 16),     # t*k = 16000: tables held in registers, 2 passes
+                                      (1100, 64, 120, 16)])   # t*k = 17600: tables streamed, 3 passes
 def test_route_small(t, d, ne, k):
     say("route", t, d, ne, k)
     x, r, bias = synth.router_inputs(7000 + t, t=t, d=d, experts=ne)
