@@ -391,7 +391,7 @@ constexpr int kGCols = 4 * 16 * kGCB;   // columns per workgroup
 constexpr int kGXs = 136;   // LDS row stride in bf16 for a 128-wide K step
 
 template <int FMT>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(
+__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
     const uint8_t* __restrict__ base, int64_t expert_stride, int n_experts, int64_t codes_off,
     int64_t meta_off, int n, int d, const uint16_t* __restrict__ x, int64_t t_x,
     const int32_t* __restrict__ row_index, const int32_t* __restrict__ seg_expert,
@@ -458,12 +458,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x4_t*>(&xs[buf][xr * kGXs + 8 * (4 * xq + i)]) = xreg[i];
     };
-    u32x4_t wreg[kGCB];
-    auto load_w = [&](int k0) {
+    auto load_w = [&](u32x4_t (&wr)[kGCB], int k0) {
       const int k = k0 + 32 * g;
 #pragma unroll
       for (int cb = 0; cb < kGCB; ++cb)
-        wreg[cb] = (col_ok[cb] && k < d) ? load16(codes + L.code_byte(col[cb], k)) : u32x4_t{0, 0, 0, 0};
+        wr[cb] = (col_ok[cb] && k < d) ? load16(codes + L.code_byte(col[cb], k)) : u32x4_t{0, 0, 0, 0};
     };
     // metadata of the slab starting at code k0 for the wave's column `lane`
     uint32_t mslab[MW];
@@ -489,11 +488,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
 #pragma unroll
       for (int cb = 0; cb < kGCB; ++cb) acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // Two weight register slots: step s waits for W(s) and at once issues the
+    // loads of step s + 1 (activations, then weights into the other slot,
+    // then the metadata of a slab that opens), so the next step's latency
+    // runs under this step's dequantisation, barrier and MFMAs.  Loads are
+    // issued in the order they are used: X(s + 1) is stored to LDS at the end
+    // of step s, W(s + 1) is consumed at the start of step s + 1.
+    u32x4_t wreg[2][kGCB];
     load_x(0);
-    load_w(0);
+    load_w(wreg[0], 0);
     load_meta(0);
     store_x(0);
-    for (int ks = 0; ks < nk; ++ks) {
+    auto gstep = [&](int ks, auto P) {
+      constexpr int p = decltype(P)::value;
       const int buf = ks & 1;
       const int k0 = ks * 128;
       // this step's group metadata for each column block: dword q of the slab
@@ -519,18 +526,20 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
           }
         }
       }
+      // W(s) has arrived (its metadata with it): start step s + 1's loads
+      // before the dequantisation
+      if (ks + 1 < nk) {
+        load_x(k0 + 128);
+        load_w(wreg[p ^ 1], k0 + 128);
+        if (((k0 + 128) & (kSlabCodes - 1)) == 0) load_meta(k0 + 128);
+      }
       u32x4_t bfrag[kGCB][4];
 #pragma unroll
       for (int cb = 0; cb < kGCB; ++cb) {
-        dequant_chunk<FMT>(wreg[cb], mreg[cb], bfrag[cb]);
+        dequant_chunk<FMT>(wreg[p][cb], mreg[cb], bfrag[cb]);
         if (!(col_ok[cb] && k0 + 32 * g < d))
 #pragma unroll
           for (int j = 0; j < 4; ++j) bfrag[cb][j] = u32x4_t{0, 0, 0, 0};
-      }
-      if (ks + 1 < nk) {
-        load_x(k0 + 128);
-        load_w(k0 + 128);
-        if (((k0 + 128) & (kSlabCodes - 1)) == 0) load_meta(k0 + 128);
       }
       __syncthreads();
 #pragma unroll
@@ -548,6 +557,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(
         }
       }
       if (ks + 1 < nk) store_x(buf ^ 1);
+    };
+    for (int ks = 0; ks < nk; ks += 2) {
+      gstep(ks, std::integral_constant<int, 0>{});
+      if (ks + 1 < nk) gstep(ks + 1, std::integral_constant<int, 1>{});
     }
 
     // epilogue: lane holds column col_l, rows 4g + r of each 16x16 block
