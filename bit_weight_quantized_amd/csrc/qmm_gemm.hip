@@ -425,7 +425,10 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
     col_ok[cb] = col[cb] < n;
   }
 
-  const int xr = tid >> 2, xq = tid & 3;  // activation loader: row tid/4, slots 4xq..4xq+3
+  // activation loader: copy i of wave w covers rows 16i + 4w + (lane >> 4),
+  // 16 lanes on each row's 256 contiguous bytes (chunk lane & 15); a short
+  // segment's rows (< 16) are spread over all four waves
+  const int xc = lane & 15;
   constexpr int MW = FMT == QMM_AFFINE4_G64 ? 8 : 4;   // metadata dwords per row per full slab
   const int64_t mcol = min(int64_t(n0 + 16 * kGCB * wave + lane), int64_t(n) - 1);
   const __amdgpu_buffer_rsrc_t mrs =
@@ -443,20 +446,21 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
       src_row[tid] = src;
     }
     __syncthreads();
-    const int my_src = src_row[xr];
+    int my_src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) my_src[i] = src_row[16 * i + 4 * wave + (lane >> 4)];
 
     u32x4_t xreg[4];
     auto load_x = [&](int k0) {
+      const int k = k0 + 8 * xc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = k0 + 8 * (4 * xq + i);
-        xreg[i] = (my_src >= 0 && k < d) ? load16(x + int64_t(my_src) * d + k) : u32x4_t{0, 0, 0, 0};
-      }
+      for (int i = 0; i < 4; ++i)
+        xreg[i] = (my_src[i] >= 0 && k < d) ? load16(x + int64_t(my_src[i]) * d + k) : u32x4_t{0, 0, 0, 0};
     };
     auto store_x = [&](int buf) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4_t*>(&xs[buf][xr * kGXs + 8 * (4 * xq + i)]) = xreg[i];
+        *reinterpret_cast<u32x4_t*>(&xs[buf][(16 * i + 4 * wave + (lane >> 4)) * kGXs + 8 * xc]) = xreg[i];
     };
     auto load_w = [&](u32x4_t (&wr)[kGCB], int k0) {
       const int k = k0 + 32 * g;
@@ -533,14 +537,12 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
         load_w(wreg[p ^ 1], k0 + 128);
         if (((k0 + 128) & (kSlabCodes - 1)) == 0) load_meta(k0 + 128);
       }
+      // No masking: past d the activations are zero and the weights finite
+      // (affine scale and bias and E8M0 < 255 are checked at pack time), so
+      // those products are exact zeros; columns past n are never stored.
       u32x4_t bfrag[kGCB][4];
 #pragma unroll
-      for (int cb = 0; cb < kGCB; ++cb) {
-        dequant_chunk<FMT>(wreg[p][cb], mreg[cb], bfrag[cb]);
-        if (!(col_ok[cb] && k0 + 32 * g < d))
-#pragma unroll
-          for (int j = 0; j < 4; ++j) bfrag[cb][j] = u32x4_t{0, 0, 0, 0};
-      }
+      for (int cb = 0; cb < kGCB; ++cb) dequant_chunk<FMT>(wreg[p][cb], mreg[cb], bfrag[cb]);
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
