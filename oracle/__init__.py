@@ -19,8 +19,9 @@ the E2M1 value set, exact-rational brute force on tiny shapes, integer-exact
 cases, one-hot columns, row sums and the tolerance checker's self-test; for the
 router, hand-worked scores and selections on tiny inputs (bias that changes the
 choice, ties to the lower id), a naive per-token full sort, the grouping's
-invariants and literal tables, and the top-k checker's self-test.  No function
-here is parity-unpinned.
+invariants and literal tables, and the top-k checker's self-test; for the expert
+FFN, hand-worked SiLU values and identities, a literal SwiGLU split and a
+hand-worked renormalised combine.  No function here is parity-unpinned.
 """
 from __future__ import annotations
 
@@ -306,6 +307,72 @@ def route(x_bits, r_bits, bias, k=16):
     """Top-k routing of every token, grouped by expert (compact segments)."""
     scores, _ = route_scores(x_bits, r_bits, bias)
     return Routing(topk(scores, k), np.asarray(r_bits).shape[0])
+
+
+# ---------------------------------------------------------------------------
+# Expert FFN after the gate_up matmul: SwiGLU, then the weighted combine
+# ---------------------------------------------------------------------------
+
+def silu(v):
+    """SiLU: v·σ(v) = v / (1 + e^(−v)), fp64.  The activation of the per-expert
+    SwiGLU ("Colibri Kimi K3 Metal 后端实现全解析", the silu_mul operation of the
+    Metal API table and Phase 6's per-expert activation)."""
+    v = np.asarray(v, np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def swiglu(y, n_inter):
+    """h[r, j] = silu(g[r, j])·u[r, j] with g = y[:, :n_inter] (the gate) and
+    u = y[:, n_inter:2·n_inter] (the up projection) of a gate_up output y."""
+    y = np.asarray(y, np.float64)
+    return silu(y[:, :n_inter]) * y[:, n_inter:2 * n_inter]
+
+
+SILU_SLOPE_MAX = 1.1   # bound on |d silu / dv| over the reals (the maximum is 1.09984 at v ≈ 2.40)
+
+
+def swiglu_tolerance(y, tol_y, n_inter):
+    """Bound on |h_gpu − h| before the output rounding when each gate and up
+    value the GPU used is within tol_y of the exact one: silu moves by at most
+    SILU_SLOPE_MAX·tol_g, so |Δh| <= SILU_SLOPE_MAX·tol_g·(|u| + tol_u) +
+    |silu(g)|·tol_u, plus 1e-6·|h| + 1e-30 for the fp32 evaluation of silu·u."""
+    y = np.asarray(y, np.float64)
+    tol_y = np.broadcast_to(np.asarray(tol_y, np.float64), y.shape)
+    g, u = y[:, :n_inter], y[:, n_inter:2 * n_inter]
+    tg, tu = tol_y[:, :n_inter], tol_y[:, n_inter:2 * n_inter]
+    h = silu(g) * u
+    return SILU_SLOPE_MAX * tg * (np.abs(u) + tu) + np.abs(silu(g)) * tu + 1e-6 * np.abs(h) + 1e-30
+
+
+def combine(o, topk_ids, weights_src, seg_offsets, row_index):
+    """Weighted scatter-add of the expert outputs back to the tokens
+    ("Colibri Kimi K3 Metal 后端实现全解析", Phase 6: output accumulation by
+    weighted scatter-add into token space).  For token t and its slot j
+    (expert e = topk[t, j]): w[t, j] = weights_src[t, e] / Σ_j' weights_src[t,
+    topk[t, j']] -- the chosen experts' sigmoid weights renormalised to sum to
+    one ("Kimi K3 迁移到 Google TPU 的可行性评估（v2）", §2: sigmoid + renormalize)
+    -- and out[t] = Σ_j w[t, j]·o[r(t, j)], where r(t, j) is the row of token t
+    in expert e's segment of the grouped order.  Returns (out, A) with
+    A[t, c] = Σ_j |w[t, j]·o[r(t, j), c]|, fp64."""
+    o = np.asarray(o, np.float64)
+    topk_ids = np.asarray(topk_ids, np.int64)
+    src = np.asarray(weights_src, np.float64)
+    t, k = topk_ids.shape
+    where = {}
+    for e in range(len(seg_offsets) - 1):
+        for r in range(int(seg_offsets[e]), int(seg_offsets[e + 1])):
+            where[(e, int(row_index[r]))] = r
+    out = np.zeros((t, o.shape[1]))
+    a = np.zeros((t, o.shape[1]))
+    for i in range(t):
+        sel = src[i, topk_ids[i]]
+        w = sel / sel.sum()
+        for j in range(k):
+            term = w[j] * o[where[(int(topk_ids[i, j]), i)]]
+            out[i] += term
+            a[i] += np.abs(term)
+    return out, a
 
 
 def check_topk(topk_ids, scores, delta) -> dict:

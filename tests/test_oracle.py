@@ -254,6 +254,42 @@ def pin_topk_non_finite():
     assert oracle.topk(row, 3)[0].tolist() == [7, 0, 3]
 
 
+def pin_silu():
+    """SiLU written out: σ(1) = 1/(1 + e^−1) = 0.7310585786300049, so
+    silu(1) = 0.7310585786300049 and silu(−1) = −0.2689414213699951; silu(0) = 0;
+    silu(v) − silu(−v) = v for every v; silu(v) -> v for large v."""
+    assert oracle.silu(0.0) == 0.0
+    assert abs(oracle.silu(1.0) - 0.7310585786300049) <= 1e-15
+    assert abs(oracle.silu(-1.0) + 0.2689414213699951) <= 1e-15
+    v = np.linspace(-30.0, 30.0, 121)
+    assert np.max(np.abs(oracle.silu(v) - oracle.silu(-v) - v)) <= 1e-13
+    assert abs(oracle.silu(40.0) - 40.0) <= 1e-12 and abs(oracle.silu(-40.0)) <= 1e-15
+    # the slope bound the SwiGLU tolerance uses holds on a fine grid
+    grid = np.linspace(-20.0, 20.0, 400001)
+    assert np.max(np.abs(np.diff(oracle.silu(grid)) / np.diff(grid))) <= oracle.SILU_SLOPE_MAX
+
+
+def pin_swiglu_literal():
+    """Gate first, up second: y = [1, −1 | 2, 3] -> [silu(1)·2, silu(−1)·3]."""
+    h = oracle.swiglu(np.array([[1.0, -1.0, 2.0, 3.0]]), 2)
+    assert np.allclose(h, [[1.4621171572600098, -0.8068242641099853]], rtol=0, atol=1e-15)
+
+
+def pin_combine_hand_worked():
+    """Two tokens, top-2 of three experts.  Token 0 picks experts 2 (weight 0.6)
+    and 0 (0.2): renormalised 0.75 and 0.25; token 1 picks 0 (0.5) and 1 (0.25):
+    2/3 and 1/3.  Grouped rows: expert 0 -> tokens 0, 1 (rows 0, 1), expert 1 ->
+    token 1 (row 2), expert 2 -> token 0 (row 3)."""
+    topk_ids = np.array([[2, 0], [0, 1]])
+    src = np.array([[0.2, 0.9, 0.6], [0.5, 0.25, 0.1]])
+    offs, rows = oracle.group(topk_ids, 3)
+    assert offs.tolist() == [0, 2, 3, 4] and rows.tolist() == [0, 1, 1, 0]
+    o = np.array([[1.0, 2.0], [3.0, 4.0], [5.0, 6.0], [7.0, 8.0]])
+    out, a = oracle.combine(o, topk_ids, src, offs, rows)
+    assert np.allclose(out, [[5.5, 6.5], [11.0 / 3.0, 14.0 / 3.0]], rtol=0, atol=1e-14)
+    assert np.allclose(a, out, rtol=0, atol=1e-14)   # all terms positive
+
+
 def pin_group_literal():
     """Grouping written out by hand: token 0 picks experts (1, 0), token 1 (0, 3)."""
     offs, rows = oracle.group(np.array([[1, 0], [0, 3]]), 4)
@@ -299,8 +335,12 @@ def all_pins(golden):
     pin_checker()
     pin_router_hand_worked()
     pin_router_full_sort()
+    pin_topk_non_finite()
     pin_group_literal()
     pin_check_topk()
+    pin_silu()
+    pin_swiglu_literal()
+    pin_combine_hand_worked()
 
 
 # --- tests -----------------------------------------------------------------
@@ -388,6 +428,18 @@ def test_topk_non_finite():
     pin_topk_non_finite()
 
 
+def test_silu():
+    pin_silu()
+
+
+def test_swiglu_literal():
+    pin_swiglu_literal()
+
+
+def test_combine_hand_worked():
+    pin_combine_hand_worked()
+
+
 def test_group_literal():
     pin_group_literal()
 
@@ -443,6 +495,14 @@ MUTATIONS = {
     "group_tokens_descending": ("group", lambda orig: (
         lambda tk, e: (lambda o: (o[0], np.concatenate([o[1][o[0][i]:o[0][i + 1]][::-1] for i in range(e)]).astype(np.int32)))(orig(tk, e)))),
     "check_topk_too_loose": ("check_topk", lambda orig: (lambda *a, **k: dict(orig(*a, **k), ok=True))),
+    "silu_is_sigmoid": ("silu", lambda orig: (lambda v: 1.0 / (1.0 + np.exp(-np.asarray(v, np.float64))))),
+    "silu_sign_flipped": ("silu", lambda orig: (lambda v: np.asarray(v, np.float64) / (1.0 + np.exp(np.asarray(v, np.float64))))),
+    "swiglu_halves_swapped": ("swiglu", lambda orig: (
+        lambda y, n: orig(np.concatenate([np.asarray(y)[:, n:2 * n], np.asarray(y)[:, :n]], axis=1), n))),
+    "combine_not_renormalised": ("combine", lambda orig: (
+        lambda o, tk, src, so, ri: (lambda res, sums: (res[0] * sums, res[1] * sums))(
+            orig(o, tk, src, so, ri),
+            np.asarray(src, np.float64)[np.arange(np.shape(tk)[0])[:, None], np.asarray(tk)].sum(1)[:, None]))),
 }
 
 
