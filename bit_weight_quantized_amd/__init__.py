@@ -16,7 +16,8 @@ __all__ = [
     "QMM_AFFINE4_G64", "QMM_MXFP4_G32", "QmmError", "lib_path", "load",
     "qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
     "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
-    "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route", "EXPORTS",
+    "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route",
+    "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "EXPORTS",
 ]
 
 QMM_AFFINE4_G64 = 1
@@ -27,7 +28,8 @@ STATUS = {0: "QMM_OK", 1: "QMM_E_ARG", 2: "QMM_E_SHAPE", 3: "QMM_E_ALIGN", 4: "Q
 
 EXPORTS = ("qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
            "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
-           "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route")
+           "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route",
+           "qmm_grouped_gemm_swiglu", "qmm_moe_combine")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -70,6 +72,9 @@ def load():
         "qmm_profile_next": (ctypes.c_int, [vp, vp]),
         "qmm_stream_read": (ctypes.c_int, [vp, sz, vp, vp]),
         "qmm_route": (ctypes.c_int, [vp, i64, i64, vp, i32, vp, i32, vp, vp, vp, vp, vp, vp]),
+        "qmm_grouped_gemm_swiglu": (ctypes.c_int, [ctypes.c_int, vp, i64, i32, i64, i64, vp, i64, vp, vp,
+                                                   vp, i32, i32, i32, vp, vp, sz, vp]),
+        "qmm_moe_combine": (ctypes.c_int, [vp, i32, i64, i64, i32, vp, vp, i32, vp, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -176,3 +181,19 @@ def qmm_grouped_gemm(fmt, packed_stack, expert_stride_bytes, n_experts, n, d, x,
                                    _ptr(x), t_x, _ptr(row_index), _ptr(seg_expert),
                                    _ptr(seg_offsets), n_seg, m_total, max_seg_rows, _ptr(y),
                                    _ptr(ws), _nbytes(ws), _stream(stream)), "qmm_grouped_gemm")
+
+
+def qmm_grouped_gemm_swiglu(fmt, packed_stack, expert_stride_bytes, n_experts, n, d, x, t_x, row_index,
+                            seg_expert, seg_offsets, n_seg, m_total, max_seg_rows, h, ws=None,
+                            stream=None):
+    _check(load().qmm_grouped_gemm_swiglu(fmt, _ptr(packed_stack), expert_stride_bytes, n_experts, n, d,
+                                          _ptr(x), t_x, _ptr(row_index), _ptr(seg_expert),
+                                          _ptr(seg_offsets), n_seg, m_total, max_seg_rows, _ptr(h),
+                                          _ptr(ws), _nbytes(ws), _stream(stream)), "qmm_grouped_gemm_swiglu")
+
+
+def qmm_moe_combine(o, m_total, d, t, k, topk, weights, n_experts, seg_offsets, row_index, out,
+                    stream=None):
+    _check(load().qmm_moe_combine(_ptr(o), m_total, d, t, k, _ptr(topk), _ptr(weights), n_experts,
+                                  _ptr(seg_offsets), _ptr(row_index), _ptr(out), _stream(stream)),
+           "qmm_moe_combine")

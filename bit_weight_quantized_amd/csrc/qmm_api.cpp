@@ -212,24 +212,26 @@ qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int6
   return QMM_OK;
 }
 
-qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expert_stride_bytes,
-                            int32_t n_experts, int64_t n, int64_t d, const qmm_bf16* x,
-                            int64_t t_x, const int32_t* row_index, const int32_t* seg_expert,
-                            const int32_t* seg_offsets, int32_t n_seg, int32_t m_total,
-                            int32_t max_seg_rows, qmm_bf16* y, void* ws, size_t ws_bytes,
-                            void* stream) {
+namespace {
+
+qmm_status grouped(const char* name, bool swiglu, qmm_format f, const void* packed_stack,
+                   int64_t expert_stride_bytes, int32_t n_experts, int64_t n, int64_t d,
+                   const qmm_bf16* x, int64_t t_x, const int32_t* row_index,
+                   const int32_t* seg_expert, const int32_t* seg_offsets, int32_t n_seg,
+                   int32_t m_total, int32_t max_seg_rows, qmm_bf16* y, void* ws, size_t ws_bytes,
+                   void* stream) {
   g_last_error[0] = 0;
   qmm::Layout l;
   qmm_status st = check_shape(f, n, d, &l);
   if (st) return st;
+  if (swiglu && n % 2) return fail(QMM_E_SHAPE, "a gate_up stack needs an even n (gate rows, then up rows)");
   if (n_experts < 1) return fail(QMM_E_ARG, "n_experts must be >= 1");
   if (expert_stride_bytes < l.total_bytes || expert_stride_bytes % 256)
     return fail(QMM_E_ARG, "expert_stride_bytes must be a multiple of 256 and >= qmm_packed_bytes");
   if (n_seg < 0 || m_total < 0 || t_x < 1) return fail(QMM_E_ARG, "n_seg, m_total >= 0 and t_x >= 1 required");
   if (n_seg > 65535) return fail(QMM_E_SHAPE, "n_seg must be <= 65535");
   if (!packed_stack || !x || !y) return fail(QMM_E_ARG, "NULL pointer");
-  if (n_seg > 0 && (!row_index || !seg_expert || !seg_offsets))
-    return fail(QMM_E_ARG, "NULL routing table");
+  if (n_seg > 0 && (!seg_expert || !seg_offsets)) return fail(QMM_E_ARG, "NULL routing table");
   if (n_seg > 0 && max_seg_rows < 1) return fail(QMM_E_ARG, "max_seg_rows must be >= 1");
   if (!aligned(packed_stack, 256)) return fail(QMM_E_ALIGN, "packed_stack must be 256-byte aligned");
   if (!aligned(x, 16)) return fail(QMM_E_ALIGN, "x must be 16-byte aligned");
@@ -239,7 +241,9 @@ qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expe
   if ((st = check_ws(f, m_total, n, d, ws, ws_bytes))) return st;
   if (n_seg == 0 || m_total == 0) return QMM_OK;
   int err;
-  if (max_seg_rows == 1) {
+  // one row per segment takes the decode GEMV, unless the activation is
+  // fused or the rows are taken in order (the matmul kernel does both)
+  if (max_seg_rows == 1 && !swiglu && row_index) {
     qmm::GemvArgs a{};
     a.f = f;
     a.packed = static_cast<const uint8_t*>(packed_stack);
@@ -273,9 +277,54 @@ qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expe
     a.m_total = m_total;
     a.max_seg_rows = max_seg_rows;
     a.y = y;
+    a.swiglu = swiglu;
     err = qmm::launch_grouped_gemm(a, stream);
   }
-  if (err) return hip_fail(err, "qmm_grouped_gemm");
+  if (err) return hip_fail(err, name);
+  return QMM_OK;
+}
+
+}  // namespace
+
+qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expert_stride_bytes,
+                            int32_t n_experts, int64_t n, int64_t d, const qmm_bf16* x,
+                            int64_t t_x, const int32_t* row_index, const int32_t* seg_expert,
+                            const int32_t* seg_offsets, int32_t n_seg, int32_t m_total,
+                            int32_t max_seg_rows, qmm_bf16* y, void* ws, size_t ws_bytes,
+                            void* stream) {
+  return grouped("qmm_grouped_gemm", false, f, packed_stack, expert_stride_bytes, n_experts, n, d, x,
+                 t_x, row_index, seg_expert, seg_offsets, n_seg, m_total, max_seg_rows, y, ws,
+                 ws_bytes, stream);
+}
+
+qmm_status qmm_grouped_gemm_swiglu(qmm_format f, const void* packed_stack,
+                                   int64_t expert_stride_bytes, int32_t n_experts, int64_t n,
+                                   int64_t d, const qmm_bf16* x, int64_t t_x,
+                                   const int32_t* row_index, const int32_t* seg_expert,
+                                   const int32_t* seg_offsets, int32_t n_seg, int32_t m_total,
+                                   int32_t max_seg_rows, qmm_bf16* h, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  return grouped("qmm_grouped_gemm_swiglu", true, f, packed_stack, expert_stride_bytes, n_experts, n,
+                 d, x, t_x, row_index, seg_expert, seg_offsets, n_seg, m_total, max_seg_rows, h, ws,
+                 ws_bytes, stream);
+}
+
+qmm_status qmm_moe_combine(const qmm_bf16* o, int32_t m_total, int64_t d, int64_t t, int32_t k,
+                           const int32_t* topk, const float* weights, int32_t n_experts,
+                           const int32_t* seg_offsets, const int32_t* row_index, qmm_bf16* out,
+                           void* stream) {
+  g_last_error[0] = 0;
+  if (!o || !topk || !weights || !seg_offsets || !row_index || !out) return fail(QMM_E_ARG, "NULL pointer");
+  if (t < 1 || k < 1 || n_experts < 1 || m_total < 0) return fail(QMM_E_ARG, "t, k, n_experts >= 1 and m_total >= 0 required");
+  if (k > qmm::kCombineMaxK) return fail(QMM_E_SHAPE, "k must be <= 64");
+  if (d < 8 || d % 8 || d > qmm::kMaxD) return fail(QMM_E_SHAPE, "d must be a multiple of 8 in [8, 65536]");
+  if (t * k >= (int64_t(1) << 31) || t > (int64_t(1) << 31) - 1) return fail(QMM_E_SHAPE, "t*k must be below 2^31");
+  if (!aligned(o, 16) || !aligned(out, 16)) return fail(QMM_E_ALIGN, "o and out must be 16-byte aligned");
+  if (!aligned(topk, 4) || !aligned(weights, 4) || !aligned(seg_offsets, 4) || !aligned(row_index, 4))
+    return fail(QMM_E_ALIGN, "tables and weights must be 4-byte aligned");
+  qmm::CombineArgs a{o, m_total, int(d), int(t), k, topk, weights, n_experts, seg_offsets, row_index, out};
+  const int err = qmm::launch_combine(a, stream);
+  if (err) return hip_fail(err, "qmm_moe_combine");
   return QMM_OK;
 }
 

@@ -390,7 +390,14 @@ constexpr int kGCB = 4;     // 16-column blocks per wave
 constexpr int kGCols = 4 * 16 * kGCB;   // columns per workgroup
 constexpr int kGXs = 136;   // LDS row stride in bf16 for a 128-wide K step
 
-template <int FMT>
+// GLU: the weights are a gate_up stack (rows [0, n/2) the gate, [n/2, n) the
+// up projection) and the output is h = silu(gate)·up, [m_total][n/2]: a
+// workgroup takes 128 output columns, waves 0-1 the gate rows and waves 2-3
+// the matching up rows, and after the K loop the up waves hand their fp32
+// accumulators to the gate waves through LDS (the activation buffers), which
+// apply the activation before the one bf16 rounding.  row_index NULL: row r
+// of the grouped order reads row r of x.
+template <int FMT, bool GLU>
 __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
     const uint8_t* __restrict__ base, int64_t expert_stride, int n_experts, int64_t codes_off,
     int64_t meta_off, int n, int d, const uint16_t* __restrict__ x, int64_t t_x,
@@ -398,12 +405,18 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
     const int32_t* __restrict__ seg_offsets, int m_total, uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][kGBM * kGXs];
   __shared__ int32_t src_row[kGBM];
+  static_assert(sizeof(xs) >= 2 * 16 * 64 * sizeof(f32x4_t), "the up accumulators fit the activation buffers");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col_l = lane & 15, g = lane >> 4;
   const int s = blockIdx.y;
-  const int n0 = blockIdx.x * kGCols;
+  const int nh = n / 2;                                   // GLU output columns
+  const int n0 = blockIdx.x * (GLU ? kGCols / 2 : kGCols); // first output column of the tile
+  // packed row of this wave's first column, and that column's output index
+  const int wout = GLU ? n0 + 64 * (wave & 1) : n0 + 64 * wave;
+  const int64_t wrow = GLU ? int64_t(wave >> 1) * nh + wout : int64_t(wout);
+  const int nout = GLU ? nh : n;                           // output columns
 
   const int r_begin = min(max(seg_offsets[s], 0), m_total);
   const int r_end = min(max(seg_offsets[s + 1], r_begin), m_total);
@@ -417,12 +430,12 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
   const Slabs L{n, d, FMT};
   const int nk = (d + 127) / 128;
 
-  int64_t col[kGCB];
+  int64_t col[kGCB];   // packed row of column block cb
   bool col_ok[kGCB];
 #pragma unroll
   for (int cb = 0; cb < kGCB; ++cb) {
-    col[cb] = n0 + 16 * kGCB * wave + 16 * cb + col_l;
-    col_ok[cb] = col[cb] < n;
+    col[cb] = wrow + 16 * cb + col_l;
+    col_ok[cb] = wout + 16 * cb + col_l < nout;
   }
 
   // activation loader: copy i of wave w covers rows 16i + 4w + (lane >> 4),
@@ -430,7 +443,9 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
   // segment's rows (< 16) are spread over all four waves
   const int xc = lane & 15;
   constexpr int MW = FMT == QMM_AFFINE4_G64 ? 8 : 4;   // metadata dwords per row per full slab
-  const int64_t mcol = min(int64_t(n0 + 16 * kGCB * wave + lane), int64_t(n) - 1);
+  // packed row of the column whose slab metadata lane `lane` loads (clamped
+  // into the wave's half of the stack)
+  const int64_t mcol = (GLU ? int64_t(wave >> 1) * nh : 0) + min(wout + lane, nout - 1);
   const __amdgpu_buffer_rsrc_t mrs =
       make_rsrc(meta, uint32_t(L.meta_quad() * ((int64_t(n) + 3) / 4)));
 
@@ -440,7 +455,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
     if (tid < kGBM) {
       int src = -1;
       if (tid < nrows) {
-        src = row_index[mb + tid];
+        src = row_index ? row_index[mb + tid] : mb + tid;
         if (bad_expert || src < 0 || src >= t_x) src = -2;
       }
       src_row[tid] = src;
@@ -566,18 +581,51 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
     }
 
     // epilogue: lane holds column col_l, rows 4g + r of each 16x16 block
+    if (GLU) {
+      f32x4_t* up = reinterpret_cast<f32x4_t*>(&xs[0][0]);   // [wave - 2][i][cb][lane]
+      __syncthreads();   // every wave is done reading the activation buffers
+      if (wave >= 2) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= nrb) continue;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int cb = 0; cb < kGCB; ++cb) {
-        if (!col_ok[cb]) continue;
+          for (int cb = 0; cb < kGCB; ++cb) up[((wave - 2) * 16 + 4 * i + cb) * 64 + lane] = acc[i][cb];
+      }
+      __syncthreads();
+      if (wave < 2) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int lr = 16 * i + 4 * g + r;
-          if (lr < nrows) {
-            const float v = src_row[lr] == -2 ? __builtin_nanf("") : acc[i][cb][r];
-            y[int64_t(mb + lr) * n + col[cb]] = f32_to_bf16(v);
+        for (int i = 0; i < 4; ++i) {
+          if (i >= nrb) continue;
+#pragma unroll
+          for (int cb = 0; cb < kGCB; ++cb) {
+            if (!col_ok[cb]) continue;
+            const f32x4_t u = up[(wave * 16 + 4 * i + cb) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int lr = 16 * i + 4 * g + r;
+              if (lr < nrows) {
+                const float gv = acc[i][cb][r];
+                const float h = gv / (1.0f + expf(-gv)) * u[r];
+                const float v = src_row[lr] == -2 ? __builtin_nanf("") : h;
+                y[int64_t(mb + lr) * nh + wout + 16 * cb + col_l] = f32_to_bf16(v);
+              }
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nrb) continue;
+#pragma unroll
+        for (int cb = 0; cb < kGCB; ++cb) {
+          if (!col_ok[cb]) continue;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int lr = 16 * i + 4 * g + r;
+            if (lr < nrows) {
+              const float v = src_row[lr] == -2 ? __builtin_nanf("") : acc[i][cb][r];
+              y[int64_t(mb + lr) * n + col[cb]] = f32_to_bf16(v);
+            }
           }
         }
       }
@@ -622,15 +670,18 @@ int launch_grouped_gemm(const GemmArgs& a, void* stream) {
   Layout l;
   if (!layout_of(a.f, a.n, a.d, &l)) return int(hipErrorInvalidValue);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid(unsigned((a.n + kGCols - 1) / kGCols), unsigned(a.n_seg));
+  const int per_tile = a.swiglu ? kGCols / 2 : kGCols;
+  const int64_t outs = a.swiglu ? a.n / 2 : a.n;
+  dim3 grid(unsigned((outs + per_tile - 1) / per_tile), unsigned(a.n_seg));
+  auto go = [&](auto kernel) {
+    launch_kernel(kernel, grid, dim3(256), s, a.packed, a.expert_stride, a.n_experts, l.codes_offset,
+                  l.meta_offset, a.n, a.d, a.x, a.t_x, a.row_index, a.seg_expert, a.seg_offsets,
+                  a.m_total, a.y);
+  };
   if (a.f == QMM_AFFINE4_G64)
-    launch_kernel(grouped_gemm_kernel<QMM_AFFINE4_G64>, grid, dim3(256), s, a.packed,
-                       a.expert_stride, a.n_experts, l.codes_offset, l.meta_offset, a.n, a.d, a.x,
-                       a.t_x, a.row_index, a.seg_expert, a.seg_offsets, a.m_total, a.y);
+    a.swiglu ? go(grouped_gemm_kernel<QMM_AFFINE4_G64, true>) : go(grouped_gemm_kernel<QMM_AFFINE4_G64, false>);
   else
-    launch_kernel(grouped_gemm_kernel<QMM_MXFP4_G32>, grid, dim3(256), s, a.packed,
-                       a.expert_stride, a.n_experts, l.codes_offset, l.meta_offset, a.n, a.d, a.x,
-                       a.t_x, a.row_index, a.seg_expert, a.seg_offsets, a.m_total, a.y);
+    a.swiglu ? go(grouped_gemm_kernel<QMM_MXFP4_G32, true>) : go(grouped_gemm_kernel<QMM_MXFP4_G32, false>);
   return int(hipGetLastError());
 }
 

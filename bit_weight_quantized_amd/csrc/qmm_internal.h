@@ -194,9 +194,23 @@ struct GemmArgs {
   int m_total;
   int max_seg_rows;
   uint16_t* y;
+  bool swiglu = false;   // grouped: y = silu(gate)·up of a gate_up stack, [m_total][n/2]
 };
 int launch_gemm(const GemmArgs& a, void* stream);
 int launch_grouped_gemm(const GemmArgs& a, void* stream);
+
+constexpr int kCombineMaxK = 64;
+struct CombineArgs {
+  const uint16_t* o;   // [m_total, d] bf16, grouped order
+  int m_total, d, t, k;
+  const int32_t* topk;       // [t, k]
+  const float* weights;      // [t, ne] routing weights
+  int ne;
+  const int32_t* seg_offsets;   // [ne + 1], dense per expert
+  const int32_t* row_index;     // [m_total], tokens ascending within a segment
+  uint16_t* out;             // [t, d] bf16
+};
+int launch_combine(const CombineArgs& a, void* stream);
 
 struct RouteArgs {
   const uint16_t* x;   // [t, d] bf16

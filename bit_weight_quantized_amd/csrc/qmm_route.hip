@@ -5,12 +5,13 @@
 // 迁移到 Google TPU 的可行性评估（v2）" (§2 模型解剖).
 //
 // Three launches on the caller's stream, no workspace:
-//   1. scores[t, e] = sigmoid(Σ_j x[t,j]·R[e,j]) + bias[e] in fp32: one
+//   1. scores[t, e] = sigmoid(Σ_j x[t,j]·R[e,j]) in fp32 (the routing weight): one
 //      workgroup per 32 tokens × 32 experts, its eight waves splitting d and
 //      staging their pieces through LDS, v_mfma_f32_16x16x32_bf16 with fp32
 //      accumulation, tiles ordered so each XCD reads a slice of x and R;
-//   2. top-k per token: one wave per token holds the token's scores in
-//      registers (up to 16 per lane) as order-preserving integer keys and
+//   2. top-k per token by the selection score fp32(score + bias[e]): one wave
+//      per token holds them in registers (up to 16 per lane) as
+//      order-preserving integer keys and
 //      takes k rounds of a wave-wide maximum (DPP within rows of 16 lanes,
 //      then across rows in scalar registers), equal keys going to the lower
 //      expert id;
@@ -62,8 +63,7 @@ constexpr int kRWaveLds = kRRows * kRRowLds;
 
 __global__ __launch_bounds__(64 * kRWaves) void route_scores_kernel(
     const uint16_t* __restrict__ x, int t, int d, const uint16_t* __restrict__ r, int ne,
-    const float* __restrict__ bias, float* __restrict__ scores, int tiles_t, int tiles_e,
-    int split_t) {
+    float* __restrict__ scores, int tiles_t, int tiles_e, int split_t) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[kRWaves * kRWaveLds];
   // this workgroup's tile: XCD k = id mod 8 owns cell (k mod a, k / a)
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
@@ -161,11 +161,10 @@ __global__ __launch_bounds__(64 * kRWaves) void route_scores_kernel(
   }
   const int e = e0 + 16 * (wave & 1) + col;
   if (e >= ne) return;
-  const float be = bias ? bias[e] : 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tt = t0 + 16 * (wave >> 1) + 4 * g + i;
-    if (tt < t) scores[int64_t(tt) * ne + e] = 1.0f / (1.0f + expf(-sum[i])) + be;
+    if (tt < t) scores[int64_t(tt) * ne + e] = 1.0f / (1.0f + expf(-sum[i]));
   }
 }
 
@@ -204,18 +203,23 @@ __device__ __forceinline__ uint32_t dpp_min(uint32_t v) {
   return min(min(r0, r1), min(r2, r3));
 }
 
-// One wave per token; lane l holds the keys of experts l, l + 64, ...  Each of
-// the k rounds takes the largest key, the lowest expert id among equal keys,
-// and zeroes the winner's key.  Branch-free: every lane runs every step.
-__global__ __launch_bounds__(64) void route_topk_kernel(const float* __restrict__ scores, int t,
+// One wave per token; lane l holds the keys of experts l, l + 64, ...: the
+// selection score fp32(sigmoid + bias) of each.  Each of the k rounds takes
+// the largest key, the lowest expert id among equal keys, and zeroes the
+// winner's key.  Branch-free: every lane runs every step.
+__global__ __launch_bounds__(64) void route_topk_kernel(const float* __restrict__ scores,
+                                                        const float* __restrict__ bias, int t,
                                                         int ne, int k, int32_t* __restrict__ topk) {
   const int lane = threadIdx.x;
   const int tok = blockIdx.x;
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(scores + int64_t(tok) * ne, uint32_t(ne) * 4u);
+  // no bias: a descriptor of size zero, every load reads zero
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(bias ? bias : scores, bias ? uint32_t(ne) * 4u : 0u);
   float v[kEJ];
 #pragma unroll
   for (int j = 0; j < kEJ; ++j)   // past the row's end reads zero
-    v[j] = __uint_as_float(buf_load4(sr, uint32_t(lane + 64 * j) * 4u));
+    v[j] = __uint_as_float(buf_load4(sr, uint32_t(lane + 64 * j) * 4u)) +
+           __uint_as_float(buf_load4(br, uint32_t(lane + 64 * j) * 4u));
   uint32_t key[kEJ];
 #pragma unroll
   for (int j = 0; j < kEJ; ++j) {
@@ -371,11 +375,11 @@ int launch_route(const RouteArgs& a, void* stream) {
     }
   }
   hipExtLaunchKernelGGL(route_scores_kernel, dim3(unsigned(8 * best_cells)), dim3(64 * kRWaves), 0, s, ev0,
-                        nullptr, 0, a.x, a.t, a.d, a.r, a.ne, a.bias, a.scores, tiles_t, tiles_e, split_t);
+                        nullptr, 0, a.x, a.t, a.d, a.r, a.ne, a.scores, tiles_t, tiles_e, split_t);
   int err = int(hipGetLastError());
   if (err) return err;
   hipLaunchKernelGGL(route_topk_kernel, dim3(unsigned(a.t)), dim3(64), 0, s,
-                     static_cast<const float*>(a.scores), a.t, a.ne, a.k, a.topk);
+                     static_cast<const float*>(a.scores), a.bias, a.t, a.ne, a.k, a.topk);
   err = int(hipGetLastError());
   if (err) return err;
   hipExtLaunchKernelGGL(route_group_kernel, dim3(1), dim3(1024), 0, s, nullptr, ev1, 0,

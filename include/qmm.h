@@ -124,7 +124,10 @@ qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int6
  *                       blob e at packed_stack + e·expert_stride_bytes
  *                       (stride a multiple of 256, >= the blob size)
  *   x                   bf16[t_x][d] activation rows
- *   row_index           int32[m_total]: grouped row r reads x row row_index[r]
+ *   row_index           int32[m_total]: grouped row r reads x row row_index[r];
+ *                       or NULL: row r reads x row r (x already in grouped
+ *                       order, e.g. the activated rows of the expert FFN;
+ *                       this always takes the matmul kernel)
  *   seg_expert          int32[n_seg]: expert of segment s
  *   seg_offsets         int32[n_seg + 1]: segment s owns grouped rows
  *                       [seg_offsets[s], seg_offsets[s+1])
@@ -143,6 +146,49 @@ qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expe
                             int32_t max_seg_rows, qmm_bf16* y, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* Routed-expert gate_up matmul with the SwiGLU activation fused into its
+ * epilogue (the per-expert SwiGLU of "Colibri Kimi K3 Metal 后端实现全解析":
+ * the silu_mul operation of its Metal API table, fused into the MoE block in
+ * Phase 6).  Arguments as for qmm_grouped_gemm, with the stack's n rows read
+ * as the gate (rows [0, n/2)) followed by the up projection (rows [n/2, n)):
+ *   h   bf16[m_total][n/2]: h[r][j] = silu(g)·u, g = (x_r·Ŵ_eᵀ)[j],
+ *       u = (x_r·Ŵ_eᵀ)[n/2 + j], silu(v) = v / (1 + e^-v); g and u are the
+ *       fp32 accumulations (never rounded), h is rounded once to bf16.
+ * n must be even (QMM_E_SHAPE).  Always the matmul kernel, whatever
+ * max_seg_rows says.  Error rows are NaN as for qmm_grouped_gemm. */
+qmm_status qmm_grouped_gemm_swiglu(qmm_format f, const void* packed_stack,
+                                   int64_t expert_stride_bytes, int32_t n_experts, int64_t n,
+                                   int64_t d, const qmm_bf16* x, int64_t t_x,
+                                   const int32_t* row_index, const int32_t* seg_expert,
+                                   const int32_t* seg_offsets, int32_t n_seg, int32_t m_total,
+                                   int32_t max_seg_rows, qmm_bf16* h, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* MoE combine: each token's expert outputs weighted and summed back into
+ * token space (the weighted scatter-add of "Colibri Kimi K3 Metal 后端实现全解析",
+ * Phase 6), the weights being the chosen experts' routing weights
+ * renormalised to sum to one ("Kimi K3 迁移到 Google TPU 的可行性评估（v2）", §2:
+ * sigmoid + renormalize).
+ *   o            bf16[m_total][d], device: expert outputs in the grouped order
+ *   topk         int32[t][k], device: each token's experts (qmm_route)
+ *   weights      fp32[t][n_experts], device: routing weights (qmm_route's scores)
+ *   seg_offsets  int32[n_experts + 1], device: dense per-expert segments
+ *   row_index    int32[m_total], device: the token of each grouped row,
+ *                ascending inside a segment (qmm_route's tables)
+ *   out          bf16[t][d], device, written:
+ *                out[t] = Σ_j w_j·o[r_j] with w_j = weights[t][e_j] /
+ *                Σ_j' weights[t][e_j'] (summed in slot order), r_j the row of
+ *                token t in expert e_j's segment; fp32, rounded once to bf16.
+ * One workgroup per token; the sums run in slot order, so results do not
+ * depend on timing.  A slot whose expert is out of range or whose token is
+ * missing from that expert's segment makes the token's outputs NaN.
+ * Limits: 1 <= k <= 64, d a multiple of 8 in [8, 65536], t·k < 2^31; o and
+ * out 16-byte aligned, the tables 4-byte aligned (QMM_E_* otherwise). */
+qmm_status qmm_moe_combine(const qmm_bf16* o, int32_t m_total, int64_t d, int64_t t, int32_t k,
+                           const int32_t* topk, const float* weights, int32_t n_experts,
+                           const int32_t* seg_offsets, const int32_t* row_index, qmm_bf16* out,
+                           void* stream);
+
 /* MoE router (the step before qmm_grouped_gemm for routed prefill): a sigmoid
  * router with a selection-only bias, top-k per token, tokens grouped by expert
  * ("Colibri Kimi K3 Metal 后端实现全解析", introduction: router with a
@@ -151,12 +197,14 @@ qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expe
  *   x        bf16 [t][d], row-major, device, 16-byte aligned
  *   r        bf16 [n_experts][d], the router weights, device, 16-byte aligned
  *   bias     fp32 [n_experts], device, or NULL for none; it changes which
- *            experts are chosen, never a score's use elsewhere
- *   scores   fp32 [t][n_experts], device, written: sigmoid(x·rᵀ) + bias,
- *            products accumulated in fp32
- *   topk     int32 [t][k], device, written: each token's experts, highest
- *            score first, equal scores to the lower expert id; -inf scores
- *            rank below every finite one and NaN below -inf (-0 equals +0)
+ *            experts are chosen and nothing else
+ *   scores   fp32 [t][n_experts], device, written: sigmoid(x·rᵀ), products
+ *            accumulated in fp32 -- the routing weights (qmm_moe_combine
+ *            renormalises the chosen ones)
+ *   topk     int32 [t][k], device, written: each token's experts by the
+ *            selection score fp32(scores + bias), highest first, equal
+ *            selection scores to the lower expert id; -inf ranks below every
+ *            finite value and NaN below -inf (-0 equals +0)
  *   seg_expert  int32 [n_experts], written 0 .. n_experts-1
  *   seg_offsets int32 [n_experts + 1], written: segment e (expert e, possibly
  *            empty) covers grouped rows [seg_offsets[e], seg_offsets[e+1])

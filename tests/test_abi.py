@@ -99,7 +99,7 @@ def test_validation_errors_before_any_launch():
     expect(E_ARG, g, A, P, blob, 0, 16, 64, P, 4, P, P, P, 1, 4, 4, P, None, 0)      # n_experts
     expect(E_ARG, g, A, P, blob - 256, 2, 16, 64, P, 4, P, P, P, 1, 4, 4, P, None, 0)  # stride < blob
     expect(E_ARG, g, A, P, blob + 8, 2, 16, 64, P, 4, P, P, P, 1, 4, 4, P, None, 0)    # stride % 256
-    expect(E_ARG, g, A, P, blob, 2, 16, 64, P, 4, None, P, P, 1, 4, 4, P, None, 0)     # NULL table
+    expect(E_ARG, g, A, P, blob, 2, 16, 64, P, 4, P, None, P, 1, 4, 4, P, None, 0)     # NULL seg_expert
     expect(E_ARG, g, A, P, blob, 2, 16, 64, P, 4, P, P, P, 1, 4, 0, P, None, 0)        # max_seg_rows
     expect(E_ARG, g, A, P, blob, 2, 16, 64, P, 0, P, P, P, 1, 4, 4, P, None, 0)        # t_x
     expect(E_SHAPE, g, A, P, blob, 2, 16, 64, P, 4, P, P, P, 70000, 4, 4, P, None, 0)  # n_seg
@@ -114,6 +114,15 @@ def test_validation_errors_before_any_launch():
     expect(E_SHAPE, ro, P, 1 << 24, 8, P, 64, None, 64, P, P, P, P, P, 0)   # t*k = 2^30
     expect(E_ALIGN, ro, P + 8, 4, 64, P, 8, None, 2, P, P, P, P, P, 0)      # x 16-byte
     expect(E_ALIGN, ro, P, 4, 64, P, 8, P + 2, 2, P, P, P, P, P, 0)         # bias 4-byte
+    gs = qmm.qmm_grouped_gemm_swiglu
+    expect(E_SHAPE, gs, A, P, blob, 2, 15, 64, P, 4, P, P, P, 1, 4, 4, P, None, 0)      # odd n
+    expect(E_ARG, gs, A, P, blob, 2, 16, 64, P, 4, P, None, P, 1, 4, 4, P, None, 0)     # NULL table
+    c = qmm.qmm_moe_combine
+    expect(E_ARG, c, None, 8, 64, 4, 2, P, P, 8, P, P, P, 0)      # NULL o
+    expect(E_SHAPE, c, P, 8, 64, 4, 65, P, P, 8, P, P, P, 0)      # k > 64
+    expect(E_SHAPE, c, P, 8, 60, 4, 2, P, P, 8, P, P, P, 0)       # d % 8
+    expect(E_ALIGN, c, P + 8, 8, 64, 4, 2, P, P, 8, P, P, P, 0)   # o 16-byte
+    expect(E_ARG, c, P, 8, 64, 0, 2, P, P, 8, P, P, P, 0)         # t = 0
     s = qmm.qmm_stream_read
     expect(E_ARG, s, None, 1024, P, 0)
     expect(E_ARG, s, P, 1024, None, 0)

@@ -324,6 +324,114 @@ def test_grouped_gemm_small(fmt, d):
         assert_parity(y, yr, ar, f"grouped fmt={fmt} d={d} max_rows={max_rows}")
 
 
+# ---------------------------------------------------------------------------
+# expert FFN: gate_up with the SwiGLU activation, down on the activated rows,
+# weighted combine back to the tokens
+# ---------------------------------------------------------------------------
+
+def run_grouped_swiglu(fmt, stk, stride, n_exp, n, d, x_bits, seg_expert, seg_offsets, row_index, max_rows):
+    m_total = int(seg_offsets[-1])
+    h = nan_out(m_total, n // 2)
+    qmm.qmm_grouped_gemm_swiglu(fmt, stk, stride, n_exp, n, d, dev(x_bits), x_bits.shape[0],
+                                dev(np.asarray(row_index, np.int32)), dev(np.asarray(seg_expert, np.int32)),
+                                dev(np.asarray(seg_offsets, np.int32)), len(seg_expert), m_total, max_rows, h)
+    torch.cuda.synchronize()
+    return host_u16(h)
+
+
+def assert_swiglu(h_bits, y_ref, a_ref, n_inter, what):
+    """h = silu(g)·u checked against the fp64 SwiGLU of the fp64 gate_up
+    result, within the bound that the gate and up values' own acceptance
+    (2e-3·A + 1e-5 each) carries through silu and the product, then the one
+    bf16 rounding."""
+    tol_y = oracle.REL_TOL * np.asarray(a_ref, np.float64) + oracle.ABS_TOL
+    h_ref = oracle.swiglu(y_ref, n_inter)
+    tol_h = oracle.swiglu_tolerance(y_ref, tol_y, n_inter)
+    r = oracle.check(h_bits, h_ref, tol_h, rel=1.0, abs_=0.0)
+    say(what, {k: r[k] for k in ("n", "n_fail", "max_ratio", "max_abs")})
+    assert r["ok"], (what, r)
+
+
+@pytest.mark.parametrize("fmt,d", [(A, 256), (M, 256), (A, 576), (M, 1056)])
+def test_grouped_swiglu_small(fmt, d):
+    """gate_up stacks of 600 rows (300 gate, 300 up: the last 128-column tile
+    is partial), segments of 0 .. 130 rows, narrow last slabs."""
+    say("grouped swiglu small", fmt, d)
+    n, n_exp, t = 600, 5, 140
+    ws = [synth.affine_weights(960 + e, n, d) if fmt == A else rand_mxfp4(960 + e, n, d) for e in range(n_exp)]
+    stk, size = stack(fmt, ws)
+    x = synth.activations(961, synth.S_X, t, d)
+    sizes = [0, 1, 17, 64, 65, 130]
+    seg_expert = [4, 0, 2, 1, 3, 2]
+    seg_offsets = np.concatenate([[0], np.cumsum(sizes)])
+    rng = np.random.default_rng(9)
+    row_index = np.concatenate([np.sort(rng.choice(t, s, replace=False)) for s in sizes]).astype(np.int32)
+    deq = (lambda e: oracle.dequant_affine(ws[e].codes, ws[e].scale, ws[e].bias)) if fmt == A else \
+          (lambda e: oracle.dequant_mxfp4(ws[e].codes, ws[e].e8m0))
+    yr, ar = oracle.grouped(x, row_index, seg_expert, seg_offsets, deq)
+    for max_rows in (max(sizes), 1):      # one kernel whatever the bound says
+        h = run_grouped_swiglu(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, max_rows)
+        assert_swiglu(h, yr, ar, n // 2, f"swiglu fmt={fmt} d={d} max_rows={max_rows}")
+
+
+def test_grouped_rows_in_order():
+    """row_index NULL: grouped row r reads x row r, also with one row per
+    segment (which then takes the matmul kernel)."""
+    say("grouped rows in order")
+    n, d, n_exp = 200, 1056, 3
+    ws = [rand_mxfp4(970 + e, n, d) for e in range(n_exp)]
+    stk, size = stack(M, ws)
+    sizes = [3, 0, 40, 1]
+    seg_expert = [2, 1, 0, 2]
+    seg_offsets = np.concatenate([[0], np.cumsum(sizes)])
+    m_total = int(seg_offsets[-1])
+    x = synth.activations(971, synth.S_X, m_total, d)
+    deq = lambda e: oracle.dequant_mxfp4(ws[e].codes, ws[e].e8m0)
+    yr, ar = oracle.grouped(x, np.arange(m_total), seg_expert, seg_offsets, deq)
+    for max_rows in (40, 1):
+        y = nan_out(m_total, n)
+        qmm.qmm_grouped_gemm(M, stk, size, n_exp, n, d, dev(x), m_total, None, dev(np.asarray(seg_expert, np.int32)),
+                             dev(np.asarray(seg_offsets, np.int32)), len(seg_expert), m_total, max_rows, y)
+        torch.cuda.synchronize()
+        assert_parity(host_u16(y), yr, ar, f"grouped rows in order max_rows={max_rows}")
+
+
+def run_combine(o_bits, topk, weights, seg_offsets, row_index, d):
+    t, k = topk.shape
+    out = nan_out(t, d)
+    qmm.qmm_moe_combine(dev(o_bits), o_bits.shape[0], d, t, k, dev(np.asarray(topk, np.int32)),
+                        dev(np.asarray(weights, np.float32)), weights.shape[1],
+                        dev(np.asarray(seg_offsets, np.int32)), dev(np.asarray(row_index, np.int32)), out)
+    torch.cuda.synchronize()
+    return host_u16(out)
+
+
+@pytest.mark.parametrize("t,ne,k,d", [(40, 20, 4, 96), (7, 65, 64, 8), (130, 300, 16, 1032)])
+def test_combine_small(t, ne, k, d):
+    """The combine against the oracle's on the same inputs: the fp64 routing's
+    tables and fp32 weights, random bf16 expert outputs."""
+    say("combine", t, ne, k, d)
+    x, r, bias = synth.router_inputs(7300 + t, t=t, d=64, experts=ne)
+    sig = oracle.route_scores(x, r, None)[0].astype(np.float32)
+    tk = oracle.topk(oracle.route_scores(x, r, bias)[0], k)
+    offs, rows = oracle.group(tk, ne)
+    o = synth.activations(7301 + t, synth.S_X, t * k, d)
+    out = run_combine(o, tk, sig, offs, rows, d)
+    yr, ar = oracle.combine(oracle.bf16_to_f64(o), tk, sig.astype(np.float64), offs, rows)
+    assert_parity(out, yr, ar, f"combine t={t} ne={ne} k={k} d={d}")
+
+
+def test_combine_missing_row_gives_nan():
+    say("combine missing row")
+    tk = np.array([[0, 1], [1, 0]])
+    offs = np.array([0, 1, 3])               # expert 0 lists token 0 only
+    rows = np.array([0, 0, 1])
+    w = np.full((2, 2), 0.5, np.float32)
+    o = synth.activations(7400, synth.S_X, 3, 16)
+    out = oracle.bf16_to_f64(run_combine(o, tk, w, offs, rows, 16))
+    assert np.all(np.isfinite(out[0])) and np.all(np.isnan(out[1]))
+
+
 def test_grouped_invalid_entries_give_nan():
     say("grouped invalid entries")
     n, d, n_exp, t = 40, 128, 2, 8
@@ -481,13 +589,17 @@ def score_bound(a_ref, d):
 
 
 def check_route(x, r, bias, k, what):
+    """Scores are the bare sigmoid (the routing weights); the choice is made on
+    sigmoid + bias, whose fp32 sum adds one rounding of at most 2^-24·|sum| to
+    the score's bound, well inside its 1e-6 absolute term."""
     s_gpu, tk, seg_e, seg_o, rows = run_route(x, r, bias, k)
-    s_ref, a_ref = oracle.route_scores(x, r, bias)
+    sig_ref, a_ref = oracle.route_scores(x, r, None)
+    sel_ref, _ = oracle.route_scores(x, r, bias)
     delta = score_bound(a_ref, x.shape[1])
-    err = np.abs(s_gpu - s_ref)
+    err = np.abs(s_gpu - sig_ref)
     say(what, dict(max_err=float(err.max()), max_err_over_bound=float((err / delta).max())))
     assert np.all(err <= delta), what
-    res = oracle.check_topk(tk, s_ref, delta)
+    res = oracle.check_topk(tk, sel_ref, delta)
     say(what, {kk: res[kk] for kk in ("n_bad", "rows_equal_to_fp64_choice", "rows")})
     assert res["ok"], (what, res)
     offs, ridx = oracle.group(tk, r.shape[0])        # exact, given the GPU's own choice
@@ -537,8 +649,7 @@ def test_route_non_finite_scores_rank_last():
     bias[ninf] = -np.inf
     bias[nan] = np.nan
     s_gpu, tk, seg_e, seg_o, rows = run_route(x, r, bias, 64)
-    assert np.all(np.isneginf(s_gpu[:, ninf])) and np.all(np.isnan(s_gpu[:, nan]))
-    assert np.all(np.isfinite(s_gpu[:, fin]))
+    assert np.all(np.isfinite(s_gpu))   # the weights are the bare sigmoid; the bias only selects
     want = fin.tolist() + sorted(ninf.tolist()) + sorted(nan.tolist())[:10]
     assert all(row.tolist() == want for row in tk)
     sref = oracle.route_scores(x, r, bias)[0]
@@ -546,6 +657,39 @@ def test_route_non_finite_scores_rank_last():
     offs, rws = oracle.group(tk, 100)
     assert np.array_equal(seg_e, np.arange(100))
     assert np.array_equal(seg_o, offs) and np.array_equal(rows, rws)
+
+
+def test_moe_prefill_expert_ffn(expert_stacks):
+    """The routed prefill workload through the whole expert FFN on the GPU:
+    route -> gate_up with SwiGLU -> down on the activated rows -> combine.
+    Each stage is checked against the oracle on the GPU's own inputs to that
+    stage (sampled experts for the matmuls, every output of the combine)."""
+    say("moe prefill expert ffn")
+    (gu, gsz), (dn, dsz) = expert_stacks
+    xb, rb, bias = synth.router_inputs(synth.seed_of(4))
+    t, ne, k = 512, 896, 16
+    s_gpu, tk, seg_e, seg_o, rows = run_route(xb, rb, bias, k)
+    m_total = t * k
+    h = run_grouped_swiglu(M, gu, gsz, ne, 6144, 3584, xb, seg_e, seg_o, rows, 512)
+    o = nan_out(m_total, 3584)
+    qmm.qmm_grouped_gemm(M, dn, dsz, ne, 3584, 3072, dev(h), m_total, None, dev(seg_e), dev(seg_o), ne,
+                         m_total, 512, o)
+    torch.cuda.synchronize()
+    o = host_u16(o)
+    out = run_combine(o, tk, s_gpu.astype(np.float32), seg_o, rows, 3584)
+    sizes = np.diff(seg_o)
+    active = np.nonzero(sizes)[0]
+    rng = np.random.default_rng(12)
+    for e in sorted({int(active[np.argmax(sizes[active])]), *rng.choice(active, 3, replace=False).tolist()}):
+        r0, r1 = int(seg_o[e]), int(seg_o[e + 1])
+        g = synth.expert_gate_up(synth.seed_of(3), e)
+        yr, ar = oracle.gemm_mxfp4(xb[rows[r0:r1]], g.codes, g.e8m0)
+        assert_swiglu(h[r0:r1], yr, ar, 3072, f"ffn gate_up+swiglu expert {e} rows {r1 - r0}")
+        dw = synth.expert_down(synth.seed_of(3), e)
+        yr, ar = oracle.gemm_mxfp4(h[r0:r1], dw.codes, dw.e8m0)
+        assert_parity(o[r0:r1], yr, ar, f"ffn down expert {e} rows {r1 - r0}")
+    yr, ar = oracle.combine(oracle.bf16_to_f64(o), tk, s_gpu, seg_o, rows)
+    assert_parity(out, yr, ar, "ffn combine 512x3584")
 
 
 def test_route_prefill_workload_then_grouped_gemm(expert_stacks):
