@@ -10,6 +10,9 @@ in HBM:
             down 3584x3072 (a fresh expert draw every step)
   moe_pre   routing of 512 tokens, top-16 over 896 experts, on the GPU
             (qmm_route), then the MXFP4 grouped GEMM (gate_up) on its tables
+  moe_ffn   the rest of the expert FFN on the same routed rows: gate_up with
+            the SwiGLU activation fused, down on the activated rows, and the
+            renormalised weighted combine back to the 512 tokens
 Weights of the decode row rotate over enough packed copies (> 2x the 256 MB
 Infinity Cache) that every launch reads HBM, not the cache.  After the timed
 steps, a plain streaming read of the decode row's byte count (qmm_stream_read,
@@ -115,9 +118,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotate", type=int, default=24, help="packed copies of the decode weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rows", default="decode,prefill,moe_dec,moe_pre",
-                    help="comma list of decode, prefill, moe_dec, moe_pre; 'copy' adds a plain "
-                         "256 MiB device copy used to calibrate HBM byte counters")
+    ap.add_argument("--rows", default="decode,prefill,moe_dec,moe_pre,moe_ffn",
+                    help="comma list of decode, prefill, moe_dec, moe_pre, moe_ffn (needs moe_pre); "
+                         "'copy' adds a plain 256 MiB device copy used to calibrate HBM byte counters")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -190,12 +193,15 @@ def main(argv=None) -> int:
         sg.expert_stack(synth.seed_of(3), "gate_up", 896,
                         lambda c, e, ptr: qmm.qmm_pack(M, gu_n, gu_d, c, e, None, ptr), gsz, gsz, gu)
         log("gate_up stack ready", gu.numel() / 1e9, "GB")
-    if "moe_dec" in rows:
+    if "moe_ffn" in rows and "moe_pre" not in rows:
+        raise SystemExit("the moe_ffn rows run on moe_pre's routing tables: ask for moe_pre too")
+    if "moe_dec" in rows or "moe_ffn" in rows:
         dsz = qmm.qmm_packed_bytes(M, dn_n, dn_d)
         dn = torch.empty(dsz * 896, dtype=torch.uint8, device=dev)
         sg.expert_stack(synth.seed_of(3), "down", 896,
                         lambda c, e, ptr: qmm.qmm_pack(M, dn_n, dn_d, c, e, None, ptr), dsz, dsz, dn)
         log("down stack ready")
+    if "moe_dec" in rows:
         seed3 = synth.seed_of(3)
         x3 = T(synth.activations(seed3, synth.S_X, 1, gu_d))
         z3 = T(synth.activations(seed3, synth.S_Z, 16, dn_d))
@@ -241,6 +247,27 @@ def main(argv=None) -> int:
             (lambda s: qmm.qmm_grouped_gemm(M, gu, gsz, 896, gu_n, gu_d, x4, t4, ri, se, so, ne, t4 * k4,
                                             t4, y4), "grouped_gemm", b4, 2.0 * t4 * k4 * gu_n * gu_d)]
         log("moe_pre ready", moe_pre_info)
+    if "moe_ffn" in rows:
+        # the rest of the expert FFN on the same routed rows: gate_up with the
+        # SwiGLU activation fused, down on the activated rows (already in grouped
+        # order), the renormalised weighted combine back to the 512 tokens
+        m4 = t4 * k4
+        h4 = torch.empty(m4, gu_n // 2, dtype=torch.int16, device=dev)
+        o4 = torch.empty(m4, dn_n, dtype=torch.int16, device=dev)
+        out4 = torch.empty(t4, dn_n, dtype=torch.int16, device=dev)
+        bsw = n_active * (gsz - 256) + 2 * xb.size + 2 * m4 * (gu_n // 2)
+        bdn = n_active * (dsz - 256) + 2 * m4 * dn_d + 2 * m4 * dn_n
+        bcb = 2 * m4 * dn_n + 2 * t4 * dn_n + 4 * t4 * k4 * 2 + 4 * m4 + 4 * (ne + 1)
+        work["moe_ffn"] = [
+            (lambda s: qmm.qmm_grouped_gemm_swiglu(M, gu, gsz, 896, gu_n, gu_d, x4, t4, ri, se, so, ne, m4,
+                                                   t4, h4), "grouped_gemm_swiglu", bsw,
+             2.0 * m4 * gu_n * gu_d),
+            (lambda s: qmm.qmm_grouped_gemm(M, dn, dsz, 896, dn_n, dn_d, h4, m4, None, se, so, ne, m4, t4, o4),
+             "grouped_gemm_down", bdn, 2.0 * m4 * dn_n * dn_d),
+            (lambda s: qmm.qmm_moe_combine(o4, m4, dn_n, t4, k4, topk4, scores4, ne, so, ri, out4),
+             "moe_combine", bcb, 2.0 * m4 * dn_n),
+        ]
+        log("moe_ffn ready")
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
 
@@ -323,7 +350,8 @@ def main(argv=None) -> int:
         "config": {"workload": synth.CONFIGS[1]["name"], "t": 1, "d": d1, "n": n1,
                    "format": "affine4_g64", "rotation_copies": args.rotate,
                    "step": "decode GEMV + prefill GEMM + MoE decode grouped GEMV x2 + MoE prefill route + grouped GEMM"
-                   if rows == ["decode", "prefill", "moe_dec", "moe_pre"] else ",".join(rows)},
+                           " + expert FFN (gate_up with SwiGLU, down, combine)"
+                   if rows == ["decode", "prefill", "moe_dec", "moe_pre", "moe_ffn"] else ",".join(rows)},
     }
     if "gemv" in results:
         g = results["gemv"]

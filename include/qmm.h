@@ -223,7 +223,7 @@ qmm_status qmm_route(const qmm_bf16* x, int64_t t, int64_t d, const qmm_bf16* r,
 /* Per-kernel GPU timing (per-op GPU timestamps, as in the op profiling of
  * "LLM Decode / Prefill 优化案例（Metal）", Step 1).  Arms two caller-owned
  * hipEvent_t handles for the next qmm_gemv / qmm_gemm / qmm_grouped_gemm /
- * qmm_route / qmm_stream_read call
+ * qmm_grouped_gemm_swiglu / qmm_moe_combine / qmm_route / qmm_stream_read call
  * on this thread: its kernel is launched with hipExtLaunchKernel so `start`
  * and `stop` are stamped by the dispatch itself, and their elapsed time is
  * the kernel's execution time.  Either may be NULL.  The arming is consumed
