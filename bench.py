@@ -5,6 +5,8 @@
 One step runs every row of the hot path once, each on inputs already resident
 in HBM:
   decode    affine GEMV, T=1, D=5120, N=13824 (the headline)
+  qkv       a Q/K/V triple (5120, 1024, 1024 rows of D=5120) sharing one x: one
+            GEMV over the matrices packed as one, then the three separately
   prefill   affine GEMM, T=2048, D=5120, N=13824 (bf16 MFMA)
   moe_dec   MXFP4 grouped GEMV, 16 of 896 experts: gate_up 6144x3584, then
             down 3584x3072 (a fresh expert draw every step)
@@ -118,8 +120,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotate", type=int, default=24, help="packed copies of the decode weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rows", default="decode,prefill,moe_dec,moe_pre,moe_ffn",
-                    help="comma list of decode, prefill, moe_dec, moe_pre, moe_ffn (needs moe_pre); "
+    ap.add_argument("--rows", default="decode,qkv,prefill,moe_dec,moe_pre,moe_ffn",
+                    help="comma list of decode, qkv, prefill, moe_dec, moe_pre, moe_ffn (needs moe_pre); "
                          "'copy' adds a plain 256 MiB device copy used to calibrate HBM byte counters")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -168,6 +170,32 @@ def main(argv=None) -> int:
         work["decode"] = [(lambda s: qmm.qmm_gemv(A, copies[s % len(copies)], n1, d1, x1, y1),
                            "gemv", b1, 2.0 * n1 * d1)]
         log("decode ready", len(copies), "copies")
+
+    # ---- fused projections: a Q/K/V triple sharing x as one GEMV, against three ----------
+    if "qkv" in rows:
+        dq = 5120
+        shapes = (5120, 1024, 1024)   # a GQA split of the 5120 hidden size
+        qw = [synth.affine_weights(synth.seed_of(1) + 100 + i, nq, dq) for i, nq in enumerate(shapes)]
+        fw = synth.Affine(np.concatenate([w.codes for w in qw]), np.concatenate([w.scale for w in qw]),
+                          np.concatenate([w.bias for w in qw]))
+
+        def packed_copies(w, count=16):
+            pk = torch.empty(qmm.qmm_packed_bytes(A, w.n, w.d), dtype=torch.uint8, device=dev)
+            qmm.qmm_pack(A, w.n, w.d, T(w.codes), T(w.scale), T(w.bias), pk)
+            return [pk] + [pk.clone() for _ in range(count - 1)]
+
+        fcopies = packed_copies(fw)
+        scopies = [packed_copies(w) for w in qw]
+        xq = T(synth.activations(synth.seed_of(1) + 100, synth.S_X, 1, dq))
+        yq = torch.empty(fw.n, dtype=torch.int16, device=dev)
+        ys = [torch.empty(w.n, dtype=torch.int16, device=dev) for w in qw]
+        nb = lambda nn: nn * dq * 36 // 64 + 2 * dq + 2 * nn
+        work["qkv"] = [(lambda s: qmm.qmm_gemv(A, fcopies[s % 16], fw.n, dq, xq, yq), "gemv_qkv_fused",
+                        nb(fw.n), 2.0 * fw.n * dq)]
+        for i, (w, nm) in enumerate(zip(qw, ("q", "k", "v"))):
+            work["qkv"].append(((lambda i, w: lambda s: qmm.qmm_gemv(A, scopies[i][s % 16], w.n, dq, xq, ys[i]))(i, w),
+                                f"gemv_{nm}", nb(w.n), 2.0 * w.n * dq))
+        log("qkv ready")
 
     # ---- prefill: affine GEMM 2048 x 5120 x 13824 ------------------------------------------
     if "prefill" in rows:
@@ -349,9 +377,10 @@ def main(argv=None) -> int:
         "dtype": "bf16", "data": "synthetic (seeded counter-based generator; no weights or datasets)",
         "config": {"workload": synth.CONFIGS[1]["name"], "t": 1, "d": d1, "n": n1,
                    "format": "affine4_g64", "rotation_copies": args.rotate,
-                   "step": "decode GEMV + prefill GEMM + MoE decode grouped GEMV x2 + MoE prefill route + grouped GEMM"
+                   "step": "decode GEMV + fused Q/K/V GEMV (and the three separately) + prefill GEMM"
+                           " + MoE decode grouped GEMV x2 + MoE prefill route + grouped GEMM"
                            " + expert FFN (gate_up with SwiGLU, down, combine)"
-                   if rows == ["decode", "prefill", "moe_dec", "moe_pre", "moe_ffn"] else ",".join(rows)},
+                   if rows == ["decode", "qkv", "prefill", "moe_dec", "moe_pre", "moe_ffn"] else ",".join(rows)},
     }
     if "gemv" in results:
         g = results["gemv"]

@@ -107,7 +107,12 @@ qmm_status qmm_unpack(qmm_format f, int64_t n, int64_t d, const void* packed, vo
 
 /* Decode GEMV: y[n] = Σ_k x[k]·ŵ[n,k] for one activation row.
  *   packed  blob from qmm_pack(f, n, d); x bf16[d]; y bf16[n] (written whole).
- * fp32 accumulation, bf16 round-to-nearest-even output. */
+ * fp32 accumulation, bf16 round-to-nearest-even output.  Several matrices
+ * that share x (a Q/K/V triple, a gate/up pair: the fused dispatches of
+ * "LLM Decode / Prefill 优化案例（Metal）", Steps 8-9) run as one launch when
+ * packed as one matrix with their rows concatenated: y then holds their
+ * outputs back to back, each bit-identical to its own call.  The same holds
+ * for qmm_gemm. */
 qmm_status qmm_gemv(qmm_format f, const void* packed, int64_t n, int64_t d, const qmm_bf16* x,
                     qmm_bf16* y, void* ws, size_t ws_bytes, void* stream);
 

@@ -187,6 +187,28 @@ def test_gemv_mxfp4(n, d, elo, ecount):
     assert_parity(y, yr[0], ar[0], f"gemv mxfp4 {n}x{d} E in [{elo}, {elo + ecount})")
 
 
+@pytest.mark.parametrize("shapes,d", [((512, 128, 128), 512), ((300, 300), 1088), ((5120, 1024, 1024), 5120)])
+def test_gemv_fused_projections(shapes, d):
+    """Matrices that share one activation row -- a GQA Q/K/V triple, a gate/up
+    pair ("LLM Decode / Prefill 优化案例（Metal）", Steps 8 and 9) -- run as one
+    launch when packed as one matrix, their rows concatenated.  Each block of
+    the fused output equals its own GEMV bit for bit (a row's result depends
+    only on that row) and the oracle."""
+    say("gemv fused projections", shapes, d)
+    ws = [synth.affine_weights(5000 + i, n, d) for i, n in enumerate(shapes)]
+    fused = synth.Affine(np.concatenate([w.codes for w in ws]), np.concatenate([w.scale for w in ws]),
+                         np.concatenate([w.bias for w in ws]))
+    x = synth.activations(5100 + d, synth.S_X, 1, d)
+    yf = run_gemv(A, pack_affine(fused), fused, x[0])
+    off = 0
+    for i, w in enumerate(ws):
+        ys = run_gemv(A, pack_affine(w), w, x[0])
+        assert np.array_equal(yf[off:off + w.n], ys)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+        assert_parity(yf[off:off + w.n], yr[0], ar[0], f"fused projection {i}: {w.n}x{d}")
+        off += w.n
+
+
 def integer_affine(seed, n, d):
     w = synth.affine_weights(seed, n, d)
     w.scale[:] = 0x3F80      # 1.0
