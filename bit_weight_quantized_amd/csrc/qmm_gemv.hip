@@ -47,7 +47,7 @@ namespace {
 
 constexpr int kWaves = 4;                 // quads per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRing = 2;                  // code slabs in flight per lane
+constexpr int kRing = 3;                  // code slabs in flight per lane (3 KiB per wave)
 constexpr int kPassSlabs = 12;            // slabs staged in LDS per pass
 constexpr int kChunkBytes = 80;           // LDS activation chunk: 64 B of x, sum at +64
 constexpr int kXL = kPassSlabs * 64 / kThreads;   // 16-byte activation pieces per thread
