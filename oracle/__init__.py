@@ -21,7 +21,9 @@ router, hand-worked scores and selections on tiny inputs (bias that changes the
 choice, ties to the lower id), a naive per-token full sort, the grouping's
 invariants and literal tables, and the top-k checker's self-test; for the expert
 FFN, hand-worked SiLU values and identities, a literal SwiGLU split and a
-hand-worked renormalised combine.  No function here is parity-unpinned.
+hand-worked renormalised combine; for the deferred-dequantisation GEMV, a
+hand-worked quantisation (half-even ties, the absmax scale), an integer-exact
+case and a per-element brute force.  No function here is parity-unpinned.
 """
 from __future__ import annotations
 
@@ -186,6 +188,53 @@ def gemm_affine(x_bits, codes_u32, scale_bits, bias_bits):
 def gemm_mxfp4(x_bits, codes_u8, e8m0):
     """MXFP4 GEMV/GEMM: Y = X·Ŵᵀ."""
     return matmul(x_bits, dequant_mxfp4(codes_u8, e8m0))
+
+
+# ---------------------------------------------------------------------------
+# Deferred dequantisation (approximate: the activations are quantised to int8)
+# ---------------------------------------------------------------------------
+
+def quantize_rows_int8(x_bits):
+    """Per-row absmax quantisation of bf16 activations to int8 ("LLM Decode /
+    Prefill 优化案例（Metal）", Step 2: the input is quantised per row by its
+    absolute maximum before the integer GEMV).  Readings where the page is
+    silent: s = fp32(absmax)/127 and x_q = round-half-even(x/s), both in fp32
+    (the GPU takes the same decision in the same precision, so the codes match
+    exactly); an all-zero row has s = 0 and x_q = 0.  Returns (x_q int64[T, D],
+    s float32[T])."""
+    x = bf16_to_f64(x_bits).astype(np.float32)
+    x = x.reshape(-1, x.shape[-1])
+    amax = np.max(np.abs(x), axis=1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = np.rint((x / safe[:, None]).astype(np.float32))
+    q = np.where(s[:, None] > 0, q, 0.0)
+    return q.astype(np.int64), s
+
+
+def gemv_affine_deferred(x_bits, codes_u32, scale_bits, bias_bits):
+    """The deferred-dequantisation decode GEMV of "LLM Decode / Prefill 优化案例
+    （Metal）", Step 2, for one activation row: the weights' 4-bit codes meet the
+    int8 activations in an exact integer sum per group of 64,
+    isum[n, g] = Σ_{k∈g} x_q[k]·q[n, k], and the scales are applied once per
+    group afterwards, with the bias corrected through the sum of the quantised
+    inputs: y[n] = s_x·Σ_g (scale[n, g]·isum[n, g] + bias[n, g]·Σ_{k∈g} x_q[k]).
+    Integer parts exact (int64), the rest in fp64.  Returns (y[N], A[N]) with
+    A = s_x·Σ_g (|scale·isum| + |bias·xsum|), the size of the terms."""
+    xq, sx = quantize_rows_int8(x_bits)
+    xq, sx = xq[0], float(sx[0])
+    q = affine_codes(codes_u32)
+    n, d = q.shape
+    g = d // 64
+    isum = (q.reshape(n, g, 64) * xq.reshape(1, g, 64)).sum(axis=2)
+    xsum = xq.reshape(g, 64).sum(axis=1)
+    sc = bf16_to_f64(scale_bits).reshape(n, g)
+    bi = bf16_to_f64(bias_bits).reshape(n, g)
+    t1 = sc * isum.astype(np.float64)
+    t2 = bi * xsum[None, :].astype(np.float64)
+    y = sx * (t1 + t2).sum(axis=1)
+    a = sx * (np.abs(t1) + np.abs(t2)).sum(axis=1)
+    return y, a
 
 
 def grouped(x_bits, row_index, seg_expert, seg_offsets, expert_weights, segments=None):

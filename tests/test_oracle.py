@@ -290,6 +290,50 @@ def pin_combine_hand_worked():
     assert np.allclose(a, out, rtol=0, atol=1e-14)   # all terms positive
 
 
+def pin_quantize_int8():
+    """absmax 127 gives s = 1 exactly, so x_q = round-half-even(x): 2.5 -> 2,
+    -2.5 -> -2, 100.5 -> 100, 101.5 -> 102, 0.375 -> 0; absmax 254 halves
+    everything; an all-zero row quantises to zeros with s = 0."""
+    vals = np.array([[127.0, -3.0, 2.5, -2.5, 0.375, 100.5, 101.5]])
+    q, s = oracle.quantize_rows_int8(oracle.f64_to_bf16_bits(vals))
+    assert s.tolist() == [1.0] and q.tolist() == [[127, -3, 2, -2, 0, 100, 102]]
+    q, s = oracle.quantize_rows_int8(oracle.f64_to_bf16_bits(np.array([[254.0, 5.0, -7.0, 3.0]])))
+    assert s.tolist() == [2.0] and q.tolist() == [[127, 2, -4, 2]]   # 2.5 -> 2, -3.5 -> -4, 1.5 -> 2
+    q, s = oracle.quantize_rows_int8(np.zeros((1, 64), np.uint16))
+    assert s.tolist() == [0.0] and not q.any()
+
+
+def pin_deferred_brute():
+    """The deferred GEMV written out element by element from its definition on
+    small shapes (Python ints and floats), and the integer-exact case: scale
+    1, bias 0 and integer x with absmax 127 make y = Σ x·q exactly."""
+    rng = np.random.default_rng(RNG_SEED + 21)
+    for n, d in ((3, 64), (5, 192)):
+        w = rand_affine(rng, n, d)
+        x = oracle.f64_to_bf16_bits(rng.standard_normal((1, d)))
+        y, a = oracle.gemv_affine_deferred(x, *w)
+        xf = [float(v) for v in oracle.bf16_to_f64(x)[0]]
+        amax = np.float32(max(abs(v) for v in xf))
+        sx = np.float32(amax / np.float32(127.0))
+        xq = [int(np.rint(np.float32(np.float32(v) / sx))) for v in xf]
+        codes = oracle.affine_codes(w[0])
+        for r in range(n):
+            total = 0.0
+            for gi in range(d // 64):
+                isum = sum(xq[k] * int(codes[r, k]) for k in range(64 * gi, 64 * gi + 64))
+                xsum = sum(xq[64 * gi:64 * gi + 64])
+                total += float(oracle.bf16_to_f64(w[1][r, gi])) * isum + float(oracle.bf16_to_f64(w[2][r, gi])) * xsum
+            assert abs(float(sx) * total - y[r]) <= 1e-12 * max(a[r], 1e-30)
+    n, d = 4, 128
+    codes = rng.integers(0, 2 ** 32, (n, d // 8), dtype=np.uint64).astype(np.uint32)
+    ones = np.full((n, d // 64), 0x3F80, np.uint16)
+    zeros = np.zeros((n, d // 64), np.uint16)
+    xi = rng.integers(-127, 128, (1, d)).astype(np.float64)
+    xi[0, 0] = 127.0
+    y, _ = oracle.gemv_affine_deferred(oracle.f64_to_bf16_bits(xi), codes, ones, zeros)
+    assert np.array_equal(y, (oracle.affine_codes(codes) * xi.astype(np.int64)).sum(axis=1).astype(np.float64))
+
+
 def pin_group_literal():
     """Grouping written out by hand: token 0 picks experts (1, 0), token 1 (0, 3)."""
     offs, rows = oracle.group(np.array([[1, 0], [0, 3]]), 4)
@@ -341,6 +385,8 @@ def all_pins(golden):
     pin_silu()
     pin_swiglu_literal()
     pin_combine_hand_worked()
+    pin_quantize_int8()
+    pin_deferred_brute()
 
 
 # --- tests -----------------------------------------------------------------
@@ -440,6 +486,14 @@ def test_combine_hand_worked():
     pin_combine_hand_worked()
 
 
+def test_quantize_int8():
+    pin_quantize_int8()
+
+
+def test_deferred_brute():
+    pin_deferred_brute()
+
+
 def test_group_literal():
     pin_group_literal()
 
@@ -468,6 +522,15 @@ def test_grouped_and_sampled(golden):
     yf, af = oracle.gemm_affine(x, *ws[1])
     for i, (tt, j) in enumerate(pairs):
         assert abs(ys[i] - yf[tt, j]) <= 1e-12 * af[tt, j]
+
+
+def _quantize_half_away(x_bits):
+    """A plausible mistake: ties rounded away from zero instead of to even."""
+    x = oracle.bf16_to_f64(x_bits).astype(np.float32).reshape(-1, np.shape(x_bits)[-1])
+    s = (np.max(np.abs(x), axis=1) / np.float32(127.0)).astype(np.float32)
+    v = x / np.where(s > 0, s, np.float32(1.0))[:, None]
+    q = np.trunc(v + np.float32(0.5) * np.sign(v))
+    return np.where(s[:, None] > 0, q, 0).astype(np.int64), s
 
 
 MUTATIONS = {
@@ -499,6 +562,9 @@ MUTATIONS = {
     "silu_sign_flipped": ("silu", lambda orig: (lambda v: np.asarray(v, np.float64) / (1.0 + np.exp(np.asarray(v, np.float64))))),
     "swiglu_halves_swapped": ("swiglu", lambda orig: (
         lambda y, n: orig(np.concatenate([np.asarray(y)[:, n:2 * n], np.asarray(y)[:, :n]], axis=1), n))),
+    "quantize_half_away": ("quantize_rows_int8", lambda orig: _quantize_half_away),
+    "deferred_no_bias_correction": ("gemv_affine_deferred", lambda orig: (
+        lambda x, c, s, b: orig(x, c, s, np.zeros_like(b)))),
     "combine_not_renormalised": ("combine", lambda orig: (
         lambda o, tk, src, so, ri: (lambda res, sums: (res[0] * sums, res[1] * sums))(
             orig(o, tk, src, so, ri),
