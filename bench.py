@@ -4,7 +4,8 @@
 
 One step runs every row of the hot path once, each on inputs already resident
 in HBM:
-  decode    affine GEMV, T=1, D=5120, N=13824 (the headline)
+  decode    affine GEMV, T=1, D=5120, N=13824 (the headline), then its
+            deferred-dequantisation variant (int8 activations) on the same weights
   qkv       a Q/K/V triple (5120, 1024, 1024 rows of D=5120) sharing one x: one
             GEMV over the matrices packed as one, then the three separately
   prefill   affine GEMM, T=2048, D=5120, N=13824 (bf16 MFMA)
@@ -167,8 +168,12 @@ def main(argv=None) -> int:
         x1 = T(synth.activations(synth.seed_of(1), synth.S_X, 1, d1))
         y1 = torch.empty(n1, dtype=torch.int16, device=dev)
         b1 = n1 * d1 * 36 // 64 + 2 * d1 + 2 * n1
+        y1i = torch.empty(n1, dtype=torch.int16, device=dev)
         work["decode"] = [(lambda s: qmm.qmm_gemv(A, copies[s % len(copies)], n1, d1, x1, y1),
-                           "gemv", b1, 2.0 * n1 * d1)]
+                           "gemv", b1, 2.0 * n1 * d1),
+                          # the deferred-dequantisation variant (int8 activations) on the same weights
+                          (lambda s: qmm.qmm_gemv_int8(A, copies[(s + 12) % len(copies)], n1, d1, x1, y1i),
+                           "gemv_int8", b1, 2.0 * n1 * d1)]
         log("decode ready", len(copies), "copies")
 
     # ---- fused projections: a Q/K/V triple sharing x as one GEMV, against three ----------

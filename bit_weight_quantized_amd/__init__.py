@@ -17,7 +17,7 @@ __all__ = [
     "qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
     "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
     "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route",
-    "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "EXPORTS",
+    "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "qmm_gemv_int8", "EXPORTS",
 ]
 
 QMM_AFFINE4_G64 = 1
@@ -29,7 +29,7 @@ STATUS = {0: "QMM_OK", 1: "QMM_E_ARG", 2: "QMM_E_SHAPE", 3: "QMM_E_ALIGN", 4: "Q
 EXPORTS = ("qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
            "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
            "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route",
-           "qmm_grouped_gemm_swiglu", "qmm_moe_combine")
+           "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "qmm_gemv_int8")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -75,6 +75,7 @@ def load():
         "qmm_grouped_gemm_swiglu": (ctypes.c_int, [ctypes.c_int, vp, i64, i32, i64, i64, vp, i64, vp, vp,
                                                    vp, i32, i32, i32, vp, vp, sz, vp]),
         "qmm_moe_combine": (ctypes.c_int, [vp, i32, i64, i64, i32, vp, vp, i32, vp, vp, vp, vp]),
+        "qmm_gemv_int8": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -197,3 +198,7 @@ def qmm_moe_combine(o, m_total, d, t, k, topk, weights, n_experts, seg_offsets, 
     _check(load().qmm_moe_combine(_ptr(o), m_total, d, t, k, _ptr(topk), _ptr(weights), n_experts,
                                   _ptr(seg_offsets), _ptr(row_index), _ptr(out), _stream(stream)),
            "qmm_moe_combine")
+
+
+def qmm_gemv_int8(fmt, packed, n, d, x, y, stream=None):
+    _check(load().qmm_gemv_int8(fmt, _ptr(packed), n, d, _ptr(x), _ptr(y), _stream(stream)), "qmm_gemv_int8")

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "qmm_deferred.h"
 #include "qmm_internal.h"
 
 namespace {
@@ -32,6 +33,12 @@ qmm_status check_shape(int f, int64_t n, int64_t d, qmm::Layout* l) {
   if (n < 1 || d < 1) return fail(QMM_E_ARG, "n and d must be >= 1");
   if (!qmm::layout_of(f, n, d, l)) return fail(QMM_E_SHAPE, "d must be a multiple of the group size, n <= 2^28, d <= 65536");
   return QMM_OK;
+}
+
+// The GEMV kernels address one matrix's codes and metadata through 32-bit
+// buffer offsets, with 2^31 reserved as the out-of-range marker.
+bool gemv_fits(int64_t n, int64_t d, const qmm::Layout& l) {
+  return n * (d / 2) < (int64_t(1) << 31) && l.meta_bytes < (int64_t(1) << 31);
 }
 
 qmm_status check_ws(int f, int64_t t, int64_t n, int64_t d, const void* ws, size_t ws_bytes) {
@@ -168,6 +175,7 @@ qmm_status qmm_gemv(qmm_format f, const void* packed, int64_t n, int64_t d, cons
   qmm::Layout l;
   qmm_status st = check_shape(f, n, d, &l);
   if (st) return st;
+  if (!gemv_fits(n, d, l)) return fail(QMM_E_SHAPE, "the GEMV addresses codes and metadata with 32-bit offsets: n*d/2 must be below 2^31");
   if (!packed || !x || !y) return fail(QMM_E_ARG, "NULL pointer");
   if (!aligned(packed, 256)) return fail(QMM_E_ALIGN, "packed must be 256-byte aligned");
   if (!aligned(x, 16)) return fail(QMM_E_ALIGN, "x must be 16-byte aligned");
@@ -243,7 +251,7 @@ qmm_status grouped(const char* name, bool swiglu, qmm_format f, const void* pack
   int err;
   // one row per segment takes the decode GEMV, unless the activation is
   // fused or the rows are taken in order (the matmul kernel does both)
-  if (max_seg_rows == 1 && !swiglu && row_index) {
+  if (max_seg_rows == 1 && !swiglu && row_index && gemv_fits(n, d, l)) {
     qmm::GemvArgs a{};
     a.f = f;
     a.packed = static_cast<const uint8_t*>(packed_stack);
@@ -307,6 +315,32 @@ qmm_status qmm_grouped_gemm_swiglu(qmm_format f, const void* packed_stack,
   return grouped("qmm_grouped_gemm_swiglu", true, f, packed_stack, expert_stride_bytes, n_experts, n,
                  d, x, t_x, row_index, seg_expert, seg_offsets, n_seg, m_total, max_seg_rows, h, ws,
                  ws_bytes, stream);
+}
+
+qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d, const qmm_bf16* x,
+                         qmm_bf16* y, void* stream) {
+  g_last_error[0] = 0;
+  if (f != QMM_AFFINE4_G64) return fail(f == QMM_MXFP4_G32 ? QMM_E_UNSUPPORTED : QMM_E_ARG,
+                                        "the deferred-dequantisation GEMV takes affine weights");
+  qmm::Layout l;
+  qmm_status st = check_shape(f, n, d, &l);
+  if (st) return st;
+  if (d > qmm::kI8MaxD) return fail(QMM_E_SHAPE, "d must be <= 57344 (the row's int8 codes live in LDS)");
+  if (!gemv_fits(n, d, l)) return fail(QMM_E_SHAPE, "n*d/2 must be below 2^31");
+  if (!packed || !x || !y) return fail(QMM_E_ARG, "NULL pointer");
+  if (!aligned(packed, 256)) return fail(QMM_E_ALIGN, "packed must be 256-byte aligned");
+  if (!aligned(x, 16)) return fail(QMM_E_ALIGN, "x must be 16-byte aligned");
+  if (!aligned(y, 2)) return fail(QMM_E_ALIGN, "y must be 2-byte aligned");
+  qmm::GemvArgs a{};
+  a.f = f;
+  a.packed = static_cast<const uint8_t*>(packed);
+  a.n = int(n);
+  a.d = int(d);
+  a.x = x;
+  a.y = y;
+  const int err = qmm::launch_gemv_i8(a, stream);
+  if (err) return hip_fail(err, "qmm_gemv_int8");
+  return QMM_OK;
 }
 
 qmm_status qmm_moe_combine(const qmm_bf16* o, int32_t m_total, int64_t d, int64_t t, int32_t k,

@@ -107,7 +107,8 @@ qmm_status qmm_unpack(qmm_format f, int64_t n, int64_t d, const void* packed, vo
 
 /* Decode GEMV: y[n] = Σ_k x[k]·ŵ[n,k] for one activation row.
  *   packed  blob from qmm_pack(f, n, d); x bf16[d]; y bf16[n] (written whole).
- * fp32 accumulation, bf16 round-to-nearest-even output.  Several matrices
+ * fp32 accumulation, bf16 round-to-nearest-even output.  n·d/2 must be
+ * below 2^31 (32-bit addressing; QMM_E_SHAPE).  Several matrices
  * that share x (a Q/K/V triple, a gate/up pair: the fused dispatches of
  * "LLM Decode / Prefill 优化案例（Metal）", Steps 8-9) run as one launch when
  * packed as one matrix with their rows concatenated: y then holds their
@@ -115,6 +116,19 @@ qmm_status qmm_unpack(qmm_format f, int64_t n, int64_t d, const void* packed, vo
  * for qmm_gemm. */
 qmm_status qmm_gemv(qmm_format f, const void* packed, int64_t n, int64_t d, const qmm_bf16* x,
                     qmm_bf16* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Deferred-dequantisation decode GEMV (an approximation; affine weights
+ * only): the deferred dequantisation of "LLM Decode / Prefill 优化案例（Metal）",
+ * Step 2.  The activation row is quantised to int8 by its absolute maximum
+ * (s = absmax/127 and x_q = round-half-even(x/s), both in fp32), the 4-bit
+ * codes meet it in exact int32 sums per 32-code chunk, and
+ *   y[n] = s·Σ_chunks (scale·Σ x_q·q + bias·Σ x_q),
+ * fp32 from the integer sums on, rounded once to bf16.  The loss of the
+ * activations' low bits makes it differ from qmm_gemv by up to ~s/2 per
+ * activation.  Limits as for qmm_gemv, plus d <= 57344 and n·d/2 < 2^31;
+ * MXFP4 returns QMM_E_UNSUPPORTED.  No workspace. */
+qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d, const qmm_bf16* x,
+                         qmm_bf16* y, void* stream);
 
 /* Prefill GEMM: Y[t][n] = Σ_k X[t][k]·ŵ[n,k].
  *   x bf16[t][d] row-major; y bf16[t][n] row-major (written whole).

@@ -13,14 +13,14 @@ HAVE_LIB = os.path.exists(qmm.lib_path())
 pytestmark = pytest.mark.skipif(not HAVE_LIB, reason="libqmm.so not built (run __graft_entry__.build())")
 
 A, M = qmm.QMM_AFFINE4_G64, qmm.QMM_MXFP4_G32
-OK, E_ARG, E_SHAPE, E_ALIGN, E_WS = 0, 1, 2, 3, 5
+OK, E_ARG, E_SHAPE, E_ALIGN, E_UNSUPPORTED, E_WS = 0, 1, 2, 3, 4, 5
 
 
 def declared_functions():
     with open(os.path.join(ROOT, "include", "qmm.h"), encoding="utf-8") as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qmm_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -117,6 +117,12 @@ def test_validation_errors_before_any_launch():
     gs = qmm.qmm_grouped_gemm_swiglu
     expect(E_SHAPE, gs, A, P, blob, 2, 15, 64, P, 4, P, P, P, 1, 4, 4, P, None, 0)      # odd n
     expect(E_ARG, gs, A, P, blob, 2, 16, 64, P, 4, P, None, P, 1, 4, 4, P, None, 0)     # NULL table
+    g8 = qmm.qmm_gemv_int8
+    expect(E_UNSUPPORTED, g8, M, P, 16, 64, P, P, 0)            # MXFP4
+    expect(E_SHAPE, g8, A, P, 16, 57408, P, P, 0)               # d > 57344
+    expect(E_ARG, g8, A, None, 16, 64, P, P, 0)                 # NULL packed
+    expect(E_ALIGN, g8, A, P, 16, 64, P + 8, P, 0)              # x 16-byte
+    expect(E_SHAPE, qmm.qmm_gemv, A, P, 1 << 27, 65536, P, P, None, 0)   # n*d/2 >= 2^31
     c = qmm.qmm_moe_combine
     expect(E_ARG, c, None, 8, 64, 4, 2, P, P, 8, P, P, P, 0)      # NULL o
     expect(E_SHAPE, c, P, 8, 64, 4, 65, P, P, 8, P, P, P, 0)      # k > 64

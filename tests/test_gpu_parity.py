@@ -209,6 +209,49 @@ def test_gemv_fused_projections(shapes, d):
         off += w.n
 
 
+def run_gemv_int8(packed, n, d, x_bits):
+    y = nan_out(n)
+    qmm.qmm_gemv_int8(A, packed, n, d, dev(x_bits), y)
+    torch.cuda.synchronize()
+    return host_u16(y)
+
+
+@pytest.mark.parametrize("n,d", [(512, 256), (37, 192), (300, 1088), (1000, 5120), (13824, 5120), (5, 57344)])
+def test_gemv_int8(n, d):
+    """The deferred-dequantisation GEMV against the oracle of the same method
+    (int8 activations decided in fp32 on both sides, exact integer sums);
+    its distance from the exact bf16 GEMV is reported, not asserted."""
+    say("gemv int8", n, d)
+    w = synth.affine_weights(6000 + n, n, d)
+    x = synth.activations(6100 + d, synth.S_X, 1, d)
+    y = run_gemv_int8(pack_affine(w), n, d, x[0])
+    yr, ar = oracle.gemv_affine_deferred(x, w.codes, w.scale, w.bias)
+    assert_parity(y, yr, ar, f"gemv int8 {n}x{d}")
+    ye, ae = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    dev_exact = np.abs(oracle.bf16_to_f64(y) - ye[0]) / ae[0]
+    say("gemv int8 vs exact", {"max_err_over_A": float(dev_exact.max()), "mean": float(dev_exact.mean())})
+
+
+def test_gemv_int8_integer_exact_and_zero_row():
+    """Scale 1, bias 0 and integer activations with absmax 127 make the
+    quantisation the identity, so every sum is an exact integer below 2^24 in
+    fp32 and the output is its one bf16 rounding, bit for bit; a zero row
+    gives zeros."""
+    say("gemv int8 integer exact")
+    rng = np.random.default_rng(61)
+    n, d = 64, 1088
+    w = integer_affine(6200, n, d)
+    xi = rng.integers(-8, 9, (1, d)).astype(np.float64)
+    xi[0, 5] = 127.0
+    x = oracle.f64_to_bf16_bits(xi)
+    y = run_gemv_int8(pack_affine(w), n, d, x[0])
+    exact = (oracle.affine_codes(w.codes) * xi.astype(np.int64)).sum(axis=1)
+    assert np.all(np.abs(exact) < 2 ** 24)
+    assert np.array_equal(oracle.bf16_to_f64(y), oracle.round_to_bf16(exact.astype(np.float64)))
+    z = run_gemv_int8(pack_affine(w), n, d, np.zeros(d, np.uint16))
+    assert not np.any(oracle.bf16_to_f64(z))
+
+
 def integer_affine(seed, n, d):
     w = synth.affine_weights(seed, n, d)
     w.scale[:] = 0x3F80      # 1.0
