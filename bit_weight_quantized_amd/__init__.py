@@ -51,6 +51,12 @@ def load():
     global _lib
     if _lib is not None:
         return _lib
+    # torch first: it ships its own libamdhip64.so.7, and whichever copy of
+    # that soname a process loads first is the one every library binds to.
+    # Loaded after torch, libqmm shares torch's HIP runtime (its streams and
+    # allocations); loaded before, it would pull in the system copy and leave
+    # torch on a runtime it was not built against.
+    import torch  # noqa: F401
     path = lib_path()
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "

@@ -16,6 +16,7 @@ _lib = None
 def load():
     global _lib
     if _lib is None:
+        import torch  # noqa: F401  (torch's HIP runtime is the process's; see bit_weight_quantized_amd.load)
         path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsynth.so")
         if not os.path.exists(path):
             raise ImportError(f"{path} is missing: build with `python -m bit_weight_quantized_amd.build`")
