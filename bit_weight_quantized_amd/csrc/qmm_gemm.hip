@@ -145,12 +145,20 @@ constexpr int gemm_lds_bytes() {
   return kXSlots * WM * 128 + kWSlots * kWSlotBytes;
 }
 
-template <int FMT, int WM>
+// FAST (d a multiple of 512, so every slab is full, and the codes and the
+// metadata each below 2^31 bytes): the two weight descriptors span the whole
+// codes and metadata regions for the whole kernel, each lane keeps the
+// constant part of its offsets, and a step adds one scalar (or 2^31 once the
+// step is past d, which reads zeros); columns past n fall past the regions or
+// into other slabs' codes, which only feed output columns that are never
+// stored.  Otherwise each step builds descriptors bounded to its slab and tile.
+template <int FMT, int WM, bool FAST>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ meta, int t, int n,
                                                    int d, const uint16_t* __restrict__ x,
                                                    uint16_t* __restrict__ y, int tiles_m,
-                                                   int tiles_n) {
+                                                   int tiles_n, uint32_t codes_bytes,
+                                                   uint32_t meta_bytes) {
   constexpr int RB = WM / 32;
   constexpr int XSLOT = WM * 128;
   constexpr int WBASE = kXSlots * XSLOT;
@@ -184,7 +192,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   const uint32_t xstep = 64u * uint32_t(d);  // bytes between instruction i and i + 1 (32 rows)
   auto copy_x = [&](int ks, int slot, int i) {
     const int k0 = 64 * ks;
-    const uint32_t o = (xlane + 2u * uint32_t(k0) + uint32_t(i) * xstep) | oob_bit(k0 + 8 * xchunk, d);
+    uint32_t o;
+    if constexpr (FAST)   // past d: 2^31 plus at most 7 row strides, still past the range
+      o = xlane + ((ks < nk ? 2u * uint32_t(k0) : 0x80000000u) + uint32_t(i) * xstep);
+    else
+      o = (xlane + 2u * uint32_t(k0) + uint32_t(i) * xstep) | oob_bit(k0 + 8 * xchunk, d);
     copy16_to_lds(xrs, o, lds_base + slot * XSLOT + 1024 * (wave + 4 * i));
   };
 
@@ -196,7 +208,27 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   const uint32_t mcol = uint32_t(64 * wave + lane);
   const uint32_t mquad = uint32_t(L.meta_quad());
   const int64_t meta_total = L.meta_quad() * ((int64_t(n) + 3) / 4);
+  // FAST: whole-region descriptors and the lanes' constant offsets
+  const auto crs_all = make_rsrc(codes, codes_bytes);
+  const auto mrs_all = make_rsrc(meta, meta_bytes);
+  const uint32_t slab_bytes = uint32_t(n) * uint32_t(kSlabCodes / 2);
+  uint32_t vcode[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) vcode[cb] = (uint32_t(n0) + ccol + 32u * cb) * uint32_t(kSlabCodes / 2) + 16u * chalf;
+  const uint32_t vmeta = ((uint32_t(n0) + mcol) >> 2) * mquad + (mcol & 3) * uint32_t(L.meta_full());
   auto copy_w = [&](int ks, int slot) {
+    const uint32_t dst = lds_base + WBASE + slot * kWSlotBytes;
+    if constexpr (FAST) {
+      const int sl = ks >> 3, j = ks & 7;   // 8 steps per slab
+      const bool in = ks < nk;
+      const uint32_t sc = in ? uint32_t(sl) * slab_bytes + 32u * j : 0x80000000u;
+      const uint32_t mk = FMT == QMM_AFFINE4_G64 ? 4u * j : 4u * (j >> 1);
+      const uint32_t sm = in ? 4u * uint32_t(sl) * uint32_t(L.meta_full()) + mk : 0x80000000u;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) copy16_to_lds(crs_all, vcode[cb] + sc, dst + 1024 * (2 * wave + cb));
+      copy4_to_lds(mrs_all, vmeta + sm, dst + 8192 + 256 * wave);
+      return;
+    }
     const int k0 = 64 * ks;
     const bool any = k0 < d;
     const int sl = (any ? k0 : 0) >> 9;
@@ -209,7 +241,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
     // quad-major metadata: column c of the tile at (c / 4)·meta_quad + (c % 4)·mrow
     const int64_t mo = L.meta(sl, n0) + mk;
     const auto mrs = make_rsrc(meta + mo, any ? uint32_t(meta_total - mo) : 0u);
-    const uint32_t dst = lds_base + WBASE + slot * kWSlotBytes;
     const uint32_t koob = oob_bit(k0 + 32 * int(chalf), d);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb)
@@ -643,25 +674,29 @@ int launch_gemm(const GemmArgs& a, void* stream) {
   const uint8_t* codes = a.packed + l.codes_offset;
   const uint8_t* meta = a.packed + l.meta_offset;
   const int tiles_n = (a.n + 255) / 256;
+  // whole-region descriptors: offsets up to a region plus one 256-column
+  // tile past it, and 2^31 as the out-of-range marker, must fit in 32 bits
+  const int64_t code_bytes = int64_t(a.n) * (a.d / 2);
+  const bool fast = a.d % kSlabCodes == 0 && code_bytes + (int64_t(1) << 16) < (int64_t(1) << 31) &&
+                    l.meta_bytes + (int64_t(1) << 20) < (int64_t(1) << 31);
+  const uint32_t cb = fast ? uint32_t(code_bytes) : 0u, mb = fast ? uint32_t(l.meta_bytes) : 0u;
+  auto go = [&](auto kernel, int wm) {
+    const int tiles_m = (a.t + wm - 1) / wm;
+    launch_kernel(kernel, dim3(unsigned(tiles_m * tiles_n)), dim3(256), s, codes, meta, a.t, a.n, a.d,
+                  a.x, a.y, tiles_m, tiles_n, cb, mb);
+  };
   // 256-row tiles for tall X, 128-row tiles otherwise
+  const bool aff = a.f == QMM_AFFINE4_G64;
   if (a.t > 128) {
-    const int tiles_m = (a.t + 255) / 256;
-    dim3 grid(unsigned(tiles_m * tiles_n));
-    if (a.f == QMM_AFFINE4_G64)
-      launch_kernel((gemm_kernel<QMM_AFFINE4_G64, 256>), grid, dim3(256), s, codes, meta,
-                         a.t, a.n, a.d, a.x, a.y, tiles_m, tiles_n);
+    if (aff)
+      fast ? go(gemm_kernel<QMM_AFFINE4_G64, 256, true>, 256) : go(gemm_kernel<QMM_AFFINE4_G64, 256, false>, 256);
     else
-      launch_kernel((gemm_kernel<QMM_MXFP4_G32, 256>), grid, dim3(256), s, codes, meta,
-                         a.t, a.n, a.d, a.x, a.y, tiles_m, tiles_n);
+      fast ? go(gemm_kernel<QMM_MXFP4_G32, 256, true>, 256) : go(gemm_kernel<QMM_MXFP4_G32, 256, false>, 256);
   } else {
-    const int tiles_m = (a.t + 127) / 128;
-    dim3 grid(unsigned(tiles_m * tiles_n));
-    if (a.f == QMM_AFFINE4_G64)
-      launch_kernel((gemm_kernel<QMM_AFFINE4_G64, 128>), grid, dim3(256), s, codes, meta,
-                         a.t, a.n, a.d, a.x, a.y, tiles_m, tiles_n);
+    if (aff)
+      fast ? go(gemm_kernel<QMM_AFFINE4_G64, 128, true>, 128) : go(gemm_kernel<QMM_AFFINE4_G64, 128, false>, 128);
     else
-      launch_kernel((gemm_kernel<QMM_MXFP4_G32, 128>), grid, dim3(256), s, codes, meta,
-                         a.t, a.n, a.d, a.x, a.y, tiles_m, tiles_n);
+      fast ? go(gemm_kernel<QMM_MXFP4_G32, 128, true>, 128) : go(gemm_kernel<QMM_MXFP4_G32, 128, false>, 128);
   }
   return int(hipGetLastError());
 }

@@ -287,7 +287,10 @@ def run_gemm(fmt, packed, n, d, x_bits):
 
 
 @pytest.mark.parametrize("t,n,d", [(2, 5, 64), (3, 300, 320), (130, 257, 576), (129, 512, 1024),
-                                   (300, 520, 640), (257, 256, 256), (513, 100, 5120)])
+                                   (300, 520, 640), (257, 256, 256), (513, 100, 5120),
+                                   # d a multiple of 512 (whole-region weight descriptors), both
+                                   # tile heights, n not a multiple of 4 or of 256, ragged t
+                                   (200, 301, 512), (70, 259, 1024), (3, 1, 1536), (600, 517, 2048)])
 def test_gemm_affine(t, n, d):
     say("gemm affine", t, n, d)
     w = synth.affine_weights(5000 + n, n, d)
@@ -299,7 +302,8 @@ def test_gemm_affine(t, n, d):
 
 @pytest.mark.parametrize("t,n,d,elo,ecount", [(2, 5, 32, 118, 9), (3, 300, 96, 118, 9),
                                               (130, 257, 3584, 118, 9), (257, 300, 3072, 118, 9),
-                                              (64, 70, 1056, 100, 50)])
+                                              (64, 70, 1056, 100, 50), (33, 130, 2048, 118, 9),
+                                              (300, 259, 1024, 100, 50)])
 def test_gemm_mxfp4(t, n, d, elo, ecount):
     say("gemm mxfp4", t, n, d)
     w = rand_mxfp4(7000 + n, n, d, elo, ecount)
