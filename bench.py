@@ -20,7 +20,9 @@ Weights of the decode row rotate over enough packed copies (> 2x the 256 MB
 Infinity Cache) that every launch reads HBM, not the cache.  After the timed
 steps, a plain streaming read of the decode row's byte count (qmm_stream_read,
 rotated the same way, timed the same way) is reported as the achievable read
-ceiling at that size (`stream_ceiling`).
+ceiling at that size (`stream_ceiling`), and when the prefill row runs, a
+dense bf16 GEMM of its shape through the vendor library (torch.matmul, no
+dequantisation) is timed beside it (`prefill_gemm.bf16_library_gemm`).
 
 Each kernel launch gets HIP start/stop events stamped by its own dispatch
 (qmm_profile_next -> hipExtLaunchKernel, on the stream it runs on); their
@@ -372,6 +374,29 @@ def main(argv=None) -> int:
                           "frac": round(sbytes / float(sus.mean()) / 1e3 / HBM_PEAK_GBPS, 4)}
         del sbufs
 
+    # dense bf16 GEMM of the prefill shape through the vendor library (torch.matmul,
+    # hipBLASLt), no dequantisation: what the matrix cores sustain on this machine for
+    # this shape with full-entropy operands; context beside the prefill row, not
+    # part of a step
+    library_gemm = None
+    if "prefill" in rows:
+        xb = x2.view(torch.bfloat16)
+        wt = torch.randn(d2, n2, device=dev, dtype=torch.float32).to(torch.bfloat16)   # [D, N] contiguous
+        for _ in range(3):
+            torch.matmul(xb, wt)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            torch.matmul(xb, wt)
+        e1.record()
+        torch.cuda.synchronize()
+        lus = e0.elapsed_time(e1) * 1e3 / 20
+        library_gemm = {"what": "torch.matmul bf16 [2048,5120]x[5120,13824] (hipBLASLt), no dequantisation",
+                        "us_mean": round(lus, 2), "TFLOPs": round(2.0 * t2 * n2 * d2 / lus / 1e6, 1),
+                        "frac": round(2.0 * t2 * n2 * d2 / lus / 1e6 / BF16_PEAK_TFLOPS, 4)}
+        del wt
+
     hev.close()
     out = {
         "metric": METRIC,
@@ -404,6 +429,9 @@ def main(argv=None) -> int:
         out["prefill_gemm"] = {"value": g["TFLOPs"], "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
                                "frac": g["mfma_frac"], "us_mean": g["us_mean"],
                                "workload": synth.CONFIGS[2]["name"]}
+        if library_gemm is not None:
+            out["prefill_gemm"]["bf16_library_gemm"] = library_gemm
+            out["prefill_gemm"]["vs_bf16_library"] = round(library_gemm["us_mean"] / g["us_mean"], 3)
     out["rows"] = results
     if "moe_pre" in rows:
         out["rows"]["grouped_gemm"].update(moe_pre_info)
