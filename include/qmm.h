@@ -44,6 +44,12 @@
  *     repeated calls give bitwise identical results (no float atomics).
  *   - Calls on different streams may run concurrently; the only process
  *     state is a per-device cache of device properties.
+ *   - The matmul, routing and combine calls only enqueue kernels on `stream`
+ *     (no allocation, copy, memset or synchronization), so a sequence of them
+ *     can be recorded into a HIP graph by stream capture and replayed; the
+ *     buffers are then fixed at capture and the host scalars (sizes,
+ *     max_seg_rows) with them.  qmm_pack and qmm_unpack synchronize and
+ *     cannot be captured.
  */
 #ifndef QMM_H
 #define QMM_H

@@ -1,0 +1,153 @@
+"""HIP graph capture of the hot path (needs an MI355X).
+
+A decode GEMV, a prefill GEMM and a whole routed MoE layer (route -> gate_up
+with SwiGLU -> down -> combine) are recorded once into a HIP graph through
+torch.cuda.CUDAGraph and replayed: the matmul, routing and combine calls only
+enqueue kernels on the caller's stream (no allocation, copy, memset or
+synchronization), so a replay must reproduce an eager run on the same inputs
+bit for bit (summation order is fixed per launch configuration).  Replays run
+with new inputs copied into the captured buffers, with eager work and
+synchronizations between them, and every output is reset to a sentinel before
+each replay so an output the graph did not write is caught.  Numerical
+correctness of each call is the parity suite's subject; this file checks only
+that the recorded launches behave as the eager ones.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import bit_weight_quantized_amd as qmm  # noqa: E402
+
+A, M = qmm.QMM_AFFINE4_G64, qmm.QMM_MXFP4_G32
+DEV = "cuda"
+
+
+def say(*a):
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to(DEV)
+
+
+def test_graph_replay_matches_eager():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qmm.load()
+    say("graph capture: gemv + gemm + routed MoE layer")
+
+    # weights: affine decode matrix and prefill matrix, MXFP4 expert stacks
+    nd, dd = 1000, 1024
+    tg, ng, dg = 70, 300, 1024
+    ne, k, t, dm, ni = 12, 4, 40, 256, 96
+    wd = synth.affine_weights(901, nd, dd)
+    wg = synth.affine_weights(902, ng, dg)
+    pd = torch.empty(qmm.qmm_packed_bytes(A, nd, dd), dtype=torch.uint8, device=DEV)
+    qmm.qmm_pack(A, nd, dd, dev(wd.codes), dev(wd.scale), dev(wd.bias), pd)
+    pg = torch.empty(qmm.qmm_packed_bytes(A, ng, dg), dtype=torch.uint8, device=DEV)
+    qmm.qmm_pack(A, ng, dg, dev(wg.codes), dev(wg.scale), dev(wg.bias), pg)
+    gsz, dsz = qmm.qmm_packed_bytes(M, 2 * ni, dm), qmm.qmm_packed_bytes(M, dm, ni)
+    gu = torch.empty(gsz * ne, dtype=torch.uint8, device=DEV)
+    dn = torch.empty(dsz * ne, dtype=torch.uint8, device=DEV)
+    for e in range(ne):
+        g = synth.mxfp4_weights(903, 2 * ni, dm, synth.S_GU_CODES, synth.S_GU_E8M0, e)
+        qmm.qmm_pack(M, 2 * ni, dm, dev(g.codes), dev(g.e8m0), None, gu.data_ptr() + e * gsz)
+        w = synth.mxfp4_weights(903, dm, ni, synth.S_DN_CODES, synth.S_DN_E8M0, e)
+        qmm.qmm_pack(M, dm, ni, dev(w.codes), dev(w.e8m0), None, dn.data_ptr() + e * dsz)
+    _, r, bias = synth.router_inputs(904, t=t, d=dm, experts=ne)
+    r_d, bias_d = dev(r), torch.from_numpy(np.asarray(bias, np.float32)).to(DEV)
+
+    # the captured buffers: inputs, then outputs (with the sentinel each is reset to)
+    xd = torch.empty(dd, dtype=torch.int16, device=DEV)
+    xg = torch.empty(tg, dg, dtype=torch.int16, device=DEV)
+    xm = torch.empty(t, dm, dtype=torch.int16, device=DEV)
+    outs = {
+        "gemv": (torch.empty(nd, dtype=torch.int16, device=DEV), 0x7FC0),
+        "gemm": (torch.empty(tg, ng, dtype=torch.int16, device=DEV), 0x7FC0),
+        "scores": (torch.empty(t, ne, dtype=torch.float32, device=DEV), float("nan")),
+        "topk": (torch.empty(t, k, dtype=torch.int32, device=DEV), -7),
+        "seg_expert": (torch.empty(ne, dtype=torch.int32, device=DEV), -7),
+        "seg_offsets": (torch.empty(ne + 1, dtype=torch.int32, device=DEV), -7),
+        "row_index": (torch.empty(t * k, dtype=torch.int32, device=DEV), -7),
+        "h": (torch.empty(t * k, ni, dtype=torch.int16, device=DEV), 0x7FC0),
+        "o": (torch.empty(t * k, dm, dtype=torch.int16, device=DEV), 0x7FC0),
+        "out": (torch.empty(t, dm, dtype=torch.int16, device=DEV), 0x7FC0),
+    }
+    O = {name: buf for name, (buf, _) in outs.items()}
+
+    def inputs(seed):
+        xd.copy_(dev(synth.activations(seed, synth.S_X, 1, dd)[0]))
+        xg.copy_(dev(synth.activations(seed, synth.S_X, tg, dg, sub=1)))
+        xm.copy_(dev(synth.activations(seed, synth.S_X, t, dm, sub=2)))
+
+    def reset():
+        for buf, fill in outs.values():
+            buf.fill_(fill)
+
+    def layer():
+        qmm.qmm_gemv(A, pd, nd, dd, xd, O["gemv"])
+        qmm.qmm_gemm(A, pg, tg, ng, dg, xg, O["gemm"])
+        qmm.qmm_route(xm, t, dm, r_d, ne, bias_d, k, O["scores"], O["topk"], O["seg_expert"],
+                      O["seg_offsets"], O["row_index"])
+        qmm.qmm_grouped_gemm_swiglu(M, gu, gsz, ne, 2 * ni, dm, xm, t, O["row_index"], O["seg_expert"],
+                                    O["seg_offsets"], ne, t * k, t, O["h"])
+        qmm.qmm_grouped_gemm(M, dn, dsz, ne, dm, ni, O["h"], t * k, None, O["seg_expert"],
+                             O["seg_offsets"], ne, t * k, t, O["o"])
+        qmm.qmm_moe_combine(O["o"], t * k, dm, t, k, O["topk"], O["scores"], ne, O["seg_offsets"],
+                            O["row_index"], O["out"])
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return {name: (buf.view(torch.int32) if buf.dtype == torch.float32 else buf).cpu().numpy().copy()
+                for name, buf in O.items()}
+
+    def check(got, want, what):
+        for name in want:
+            assert np.array_equal(got[name], want[name]), f"{what}: {name} differs from the eager run"
+
+    # eager references for two input sets
+    reset()
+    sentinel = snapshot()
+    eager = {}
+    for seed in (905, 906):
+        inputs(seed)
+        reset()
+        layer()
+        eager[seed] = snapshot()
+    for name in O:   # every output was written, and the two input sets differ
+        assert not np.array_equal(eager[905][name], sentinel[name]), name
+    assert not np.array_equal(eager[905]["out"], eager[906]["out"])
+
+    # record once (inputs of the first set in place; nothing runs during capture)
+    inputs(905)
+    reset()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer()
+    torch.cuda.synchronize()
+
+    busy = torch.randn(1 << 20, device=DEV)
+    for rep, seed in enumerate((905, 906, 905, 906)):
+        inputs(seed)
+        reset()
+        graph.replay()
+        got = snapshot()
+        check(got, eager[seed], f"replay {rep} (inputs {seed})")
+        # eager work between replays, then a synchronization
+        busy.mul_(0.5).add_(1.0)
+        float(busy.sum().item())
+        torch.cuda.synchronize()
+    say("graph replays match eager", 4)
