@@ -100,7 +100,10 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // inline asm so the compiler does not track them: it cannot tell the LDS
 // slots apart and would wait for every copy in flight before each LDS read.
 // The kernels order them with explicit vmcnt waits instead, and issue no
-// other vector-memory loads while copies are in flight.
+// other vector-memory loads while copies are in flight.  Each copy sets m0
+// itself; the compiler warns that it may not preserve m0 across the asm,
+// which is sound only while no compiler-generated instruction in these
+// kernels keeps a value in m0 (a CPU test compiles this file and checks).
 __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
@@ -558,12 +561,13 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
       const int q = ks & 3;
       uint32_t mreg[kGCB];
       {
-        const uint32_t v0 = FMT == QMM_AFFINE4_G64
-                                ? (q == 0 ? mslab[0] : q == 1 ? mslab[2] : q == 2 ? mslab[4] : mslab[6])
-                                : (q == 0 ? mslab[0] : q == 1 ? mslab[1] : q == 2 ? mslab[2] : mslab[3]);
-        const uint32_t v1 = FMT == QMM_AFFINE4_G64
-                                ? (q == 0 ? mslab[1] : q == 1 ? mslab[3] : q == 2 ? mslab[5] : mslab[7])
-                                : 0u;
+        uint32_t v0, v1 = 0u;
+        if constexpr (FMT == QMM_AFFINE4_G64) {
+          v0 = q == 0 ? mslab[0] : q == 1 ? mslab[2] : q == 2 ? mslab[4] : mslab[6];
+          v1 = q == 0 ? mslab[1] : q == 1 ? mslab[3] : q == 2 ? mslab[5] : mslab[7];
+        } else {
+          v0 = q == 0 ? mslab[0] : q == 1 ? mslab[1] : q == 2 ? mslab[2] : mslab[3];
+        }
 #pragma unroll
         for (int cb = 0; cb < kGCB; ++cb) {
           const int src = 4 * (16 * cb + col_l);
