@@ -7,6 +7,7 @@
 
 #include "qmm_deferred.h"
 #include "qmm_internal.h"
+#include "qmm_skinny.h"
 
 namespace {
 
@@ -41,9 +42,9 @@ bool gemv_fits(int64_t n, int64_t d, const qmm::Layout& l) {
   return n * (d / 2) < (int64_t(1) << 31) && l.meta_bytes < (int64_t(1) << 31);
 }
 
-qmm_status check_ws(int f, int64_t t, int64_t n, int64_t d, const void* ws, size_t ws_bytes) {
-  const size_t need = qmm_workspace_bytes(static_cast<qmm_format>(f), t, n, d);
-  if (need && (!ws || ws_bytes < need)) return fail(QMM_E_WORKSPACE, "workspace too small");
+// A workspace is optional; one that is passed must hold what the call uses.
+qmm_status check_ws(size_t need, const void* ws, size_t ws_bytes) {
+  if (ws && ws_bytes < need) return fail(QMM_E_WORKSPACE, "workspace smaller than qmm_workspace_bytes()");
   return QMM_OK;
 }
 
@@ -68,7 +69,11 @@ size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d) {
   return size_t(l.total_bytes);
 }
 
-size_t qmm_workspace_bytes(qmm_format, int64_t, int64_t, int64_t) { return 0; }
+size_t qmm_workspace_bytes(qmm_format f, int64_t t, int64_t n, int64_t d) {
+  qmm::Layout l;
+  if (!valid_format(f) || n < 1 || d < 1 || !qmm::layout_of(f, n, d, &l)) return 0;
+  return qmm::skinny_fits(t, n, d, l) ? qmm::skinny_workspace_bytes(t, n, d) : 0;
+}
 
 uint32_t qmm_layout_version(void) { return qmm::kLayoutVersion; }
 
@@ -180,7 +185,7 @@ qmm_status qmm_gemv(qmm_format f, const void* packed, int64_t n, int64_t d, cons
   if (!aligned(packed, 256)) return fail(QMM_E_ALIGN, "packed must be 256-byte aligned");
   if (!aligned(x, 16)) return fail(QMM_E_ALIGN, "x must be 16-byte aligned");
   if (!aligned(y, 2)) return fail(QMM_E_ALIGN, "y must be 2-byte aligned");
-  if ((st = check_ws(f, 1, n, d, ws, ws_bytes))) return st;
+  if ((st = check_ws(0, ws, ws_bytes))) return st;
   qmm::GemvArgs a{};
   a.f = f;
   a.packed = static_cast<const uint8_t*>(packed);
@@ -205,8 +210,10 @@ qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int6
   if (!aligned(packed, 256)) return fail(QMM_E_ALIGN, "packed must be 256-byte aligned");
   if (!aligned(x, 16)) return fail(QMM_E_ALIGN, "x must be 16-byte aligned");
   if (!aligned(y, 2)) return fail(QMM_E_ALIGN, "y must be 2-byte aligned");
-  if ((st = check_ws(f, t, n, d, ws, ws_bytes))) return st;
-  if (t == 1) return qmm_gemv(f, packed, n, d, x, y, ws, ws_bytes, stream);
+  const size_t need = qmm_workspace_bytes(f, t, n, d);
+  if ((st = check_ws(need, ws, ws_bytes))) return st;
+  if (t == 1) return qmm_gemv(f, packed, n, d, x, y, nullptr, 0, stream);
+  if (need && ws && !aligned(ws, 16)) return fail(QMM_E_ALIGN, "ws must be 16-byte aligned");
   qmm::GemmArgs a{};
   a.f = f;
   a.packed = static_cast<const uint8_t*>(packed);
@@ -215,7 +222,7 @@ qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int6
   a.d = int(d);
   a.x = x;
   a.y = y;
-  int err = qmm::launch_gemm(a, stream);
+  int err = need && ws ? qmm::launch_skinny(a, static_cast<float*>(ws), stream) : qmm::launch_gemm(a, stream);
   if (err) return hip_fail(err, "qmm_gemm");
   return QMM_OK;
 }
@@ -246,7 +253,7 @@ qmm_status grouped(const char* name, bool swiglu, qmm_format f, const void* pack
   if (!aligned(y, 2)) return fail(QMM_E_ALIGN, "y must be 2-byte aligned");
   if (!aligned(row_index, 4) || !aligned(seg_expert, 4) || !aligned(seg_offsets, 4))
     return fail(QMM_E_ALIGN, "routing tables must be 4-byte aligned");
-  if ((st = check_ws(f, m_total, n, d, ws, ws_bytes))) return st;
+  if ((st = check_ws(0, ws, ws_bytes))) return st;
   if (n_seg == 0 || m_total == 0) return QMM_OK;
   int err;
   // one row per segment takes the decode GEMV, unless the activation is

@@ -86,8 +86,14 @@ typedef uint16_t qmm_bf16; /* raw bf16 bits */
  * format is invalid.  Host only; touches no device. */
 size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
 
-/* Workspace the matmul calls need for these sizes (bytes, 0 = none).  The
- * kernels of this build need none; callers may pass ws = NULL, ws_bytes = 0. */
+/* Workspace that lets qmm_gemm(f, t, n, d) take its fastest path (bytes, 0 =
+ * none helps; 0 also for an invalid shape).  Nonzero for 2 <= t <= 64 rows: one
+ * fp32 [t][n] plane per 512-code slab of d, ceil(d/512)·t·n·4 bytes (2.2 MB for
+ * t = 4, n = 13824, d = 5120).  A workspace is always optional: every call
+ * accepts ws = NULL (qmm_gemm then runs its tile kernel, several times slower
+ * for such t); a non-NULL ws must be 16-byte aligned and hold at least this many
+ * bytes (QMM_E_ALIGN, QMM_E_WORKSPACE).  Its contents on entry do not matter,
+ * and calls sharing one workspace must be ordered on one stream.  Host only. */
 size_t qmm_workspace_bytes(qmm_format f, int64_t t, int64_t n, int64_t d);
 
 /* Pack canonical weights into the MI355X device layout.
@@ -140,7 +146,11 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
  *   x bf16[t][d] row-major; y bf16[t][n] row-major (written whole).
  * t = 1 runs the GEMV kernel; t > 1 dequantizes weight tiles to bf16 and
  * feeds bf16 MFMA with fp32 accumulation (the weight is rounded to bf16 once,
- * as the MFMA operand). */
+ * as the MFMA operand).  For 2 <= t <= 64 with a workspace of
+ * qmm_workspace_bytes(f, t, n, d) bytes the product is split along d: each
+ * 512-code slab's fp32 partial sums go to the workspace and a second kernel
+ * adds them in slab order, then rounds to bf16 (a batch of decode rows streams
+ * the weights once across the whole chip); without one, the tile kernel. */
 qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
                     const qmm_bf16* x, qmm_bf16* y, void* ws, size_t ws_bytes, void* stream);
 

@@ -59,6 +59,25 @@ def test_packed_bytes_rejects_bad_shapes():
     assert qmm.qmm_workspace_bytes(A, 2048, 13824, 5120) == 0
 
 
+def test_workspace_contract():
+    # split-K partials of qmm_gemm for 2 <= t <= 64: one fp32 [t][n] plane per
+    # 512-code slab of d; nothing for other t or invalid shapes
+    assert qmm.qmm_workspace_bytes(A, 2, 13824, 5120) == 10 * 2 * 13824 * 4
+    assert qmm.qmm_workspace_bytes(M, 64, 300, 1088) == 3 * 64 * 300 * 4
+    for t in (1, 65, 2048):
+        assert qmm.qmm_workspace_bytes(A, t, 13824, 5120) == 0
+    assert qmm.qmm_workspace_bytes(A, 4, 8, 96) == 0
+    # optional, but one that is passed must be large enough and 16-byte aligned
+    # (host validation: nothing is launched)
+    lib = qmm.load()
+    need = qmm.qmm_workspace_bytes(A, 4, 16, 64)
+    assert need == 256
+    assert lib.qmm_gemm(A, P, 4, 16, 64, P, P, P, need - 1, None) == E_WS
+    assert "workspace" in qmm.qmm_last_error()
+    assert lib.qmm_gemm(A, P, 4, 16, 64, P, P, P + 8, need, None) == E_ALIGN
+    assert lib.qmm_gemv(A, P, 16, 64, P + 1, P, P, 1, None) == E_ALIGN   # gemv ignores ws, checks x
+
+
 def test_status_strings_and_version():
     assert qmm.qmm_status_string(0) == "ok"
     for s in range(1, 9):

@@ -325,6 +325,68 @@ def test_gemm_integer_exact():
     assert np.array_equal(y, oracle.f64_to_bf16_bits(yr))
 
 
+def run_gemm_split(fmt, packed, n, d, x_bits):
+    """qmm_gemm with the workspace that enables the split-K path (2 <= t <= 64),
+    NaN-filled first: its contents on entry must not matter."""
+    t = x_bits.shape[0]
+    need = qmm.qmm_workspace_bytes(fmt, t, n, d)
+    assert need == -(-d // 512) * t * n * 4
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    y = nan_out(t, n)
+    qmm.qmm_gemm(fmt, packed, t, n, d, dev(x_bits), y, ws)
+    torch.cuda.synchronize()
+    return host_u16(y)
+
+
+@pytest.mark.parametrize("t,n,d", [(2, 5, 64), (2, 300, 512), (3, 257, 1088), (16, 1000, 1024),
+                                   (17, 256, 576), (33, 300, 2048), (64, 520, 640), (48, 77, 5120)])
+def test_gemm_split_k_affine(t, n, d):
+    say("gemm split-k affine", t, n, d)
+    w = synth.affine_weights(5100 + n, n, d)
+    x = synth.activations(6100 + t, synth.S_X, t, d)
+    y = run_gemm_split(A, pack_affine(w), n, d, x)
+    yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    assert_parity(y, yr, ar, f"gemm split-k affine {t}x{n}x{d}")
+
+
+@pytest.mark.parametrize("t,n,d,elo,ecount", [(2, 7, 32, 118, 9), (5, 300, 96, 118, 9),
+                                              (16, 257, 3584, 118, 9), (64, 130, 1056, 100, 50)])
+def test_gemm_split_k_mxfp4(t, n, d, elo, ecount):
+    say("gemm split-k mxfp4", t, n, d)
+    w = rand_mxfp4(7100 + n, n, d, elo, ecount)
+    x = synth.activations(8100 + t, synth.S_X, t, d)
+    y = run_gemm_split(M, pack_mxfp4(w), n, d, x)
+    yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    assert_parity(y, yr, ar, f"gemm split-k mxfp4 {t}x{n}x{d}")
+
+
+def test_gemm_split_k_integer_exact():
+    """Integer weights and activations: every slab's partial and their sum are
+    integers below 2^24, so the split-K path must match bit for bit."""
+    say("gemm split-k integer exact")
+    rng = np.random.default_rng(16)
+    t, n, d = 20, 300, 1088
+    w = integer_affine(23, n, d)
+    x = synth.bf16_bits(rng.integers(-3, 4, size=(t, d)).astype(float))
+    yr, _ = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    assert np.all(np.abs(yr) < 2 ** 24)
+    y = run_gemm_split(A, pack_affine(w), n, d, x)
+    assert np.array_equal(y, oracle.f64_to_bf16_bits(yr))
+
+
+def test_gemm_split_k_decode_batch_full():
+    """A batch of 8 decode rows against the whole 13824 x 5120 decode matrix,
+    every output checked."""
+    say("gemm split-k 8x13824x5120")
+    cfg = synth.CONFIGS[1]
+    n, d = cfg["n"], cfg["d"]
+    w = synth.affine_weights(synth.seed_of(1), n, d)
+    x = synth.activations(synth.seed_of(1), synth.S_X, 8, d, sub=3)
+    y = run_gemm_split(A, pack_affine(w), n, d, x)
+    yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    assert_parity(y, yr, ar, "gemm split-k 8x13824x5120")
+
+
 def test_gemm_prefill_workload_sampled():
     """2048 x 5120 x 13824 in the benchmark's launch configuration; the oracle
     evaluates 3000 sampled outputs one by one (all tile corners included)."""
