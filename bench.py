@@ -5,7 +5,8 @@
 One step runs every row of the hot path once, each on inputs already resident
 in HBM:
   decode    affine GEMV, T=1, D=5120, N=13824 (the headline), then its
-            deferred-dequantisation variant (int8 activations) on the same weights
+            deferred-dequantisation variant (int8 activations) and a batch of
+            8 rows (qmm_gemm split along K) on the same weights
   qkv       a Q/K/V triple (5120, 1024, 1024 rows of D=5120) sharing one x: one
             GEMV over the matrices packed as one, then the three separately
   prefill   affine GEMM, T=2048, D=5120, N=13824 (bf16 MFMA)
@@ -176,6 +177,14 @@ def main(argv=None) -> int:
                           # the deferred-dequantisation variant (int8 activations) on the same weights
                           (lambda s: qmm.qmm_gemv_int8(A, copies[(s + 12) % len(copies)], n1, d1, x1, y1i),
                            "gemv_int8", b1, 2.0 * n1 * d1)]
+        # a batch of 8 decode rows on the same weights: qmm_gemm split along K
+        # through a workspace (both of its kernels inside the stamped interval)
+        x8 = T(synth.activations(synth.seed_of(1), synth.S_X, 8, d1, sub=3))
+        y8 = torch.empty(8, n1, dtype=torch.int16, device=dev)
+        ws8 = torch.empty(qmm.qmm_workspace_bytes(A, 8, n1, d1) // 4, dtype=torch.float32, device=dev)
+        b8 = n1 * d1 * 36 // 64 + 2 * 8 * d1 + 2 * 8 * n1
+        work["decode"].append((lambda s: qmm.qmm_gemm(A, copies[(s + 6) % len(copies)], 8, n1, d1, x8, y8, ws8),
+                               "gemm_t8_split_k", b8, 2.0 * 8 * n1 * d1))
         log("decode ready", len(copies), "copies")
 
     # ---- fused projections: a Q/K/V triple sharing x as one GEMV, against three ----------
@@ -407,7 +416,7 @@ def main(argv=None) -> int:
         "dtype": "bf16", "data": "synthetic (seeded counter-based generator; no weights or datasets)",
         "config": {"workload": synth.CONFIGS[1]["name"], "t": 1, "d": d1, "n": n1,
                    "format": "affine4_g64", "rotation_copies": args.rotate,
-                   "step": "decode GEMV + fused Q/K/V GEMV (and the three separately) + prefill GEMM"
+                   "step": "decode GEMV (+ int8 variant, + 8-row batch) + fused Q/K/V GEMV (and the three separately) + prefill GEMM"
                            " + MoE decode grouped GEMV x2 + MoE prefill route + grouped GEMM"
                            " + expert FFN (gate_up with SwiGLU, down, combine)"
                    if rows == ["decode", "qkv", "prefill", "moe_dec", "moe_pre", "moe_ffn"] else ",".join(rows)},
