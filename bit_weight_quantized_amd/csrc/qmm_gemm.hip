@@ -689,9 +689,21 @@ int launch_gemm(const GemmArgs& a, void* stream) {
     launch_kernel(kernel, dim3(unsigned(tiles_m * tiles_n)), dim3(256), s, codes, meta, a.t, a.n, a.d,
                   a.x, a.y, tiles_m, tiles_n, cb, mb);
   };
-  // 256-row tiles for tall X, 128-row tiles otherwise
+  // Tile height by a cost model of whole rounds of tiles over the CUs: a round
+  // of 256-row tiles (one per CU) takes ~12 units, a round of 128-row tiles
+  // (per CU, whether one or two share it) ~7 (measured at n = 13824, d = 5120:
+  // ~125 and ~73 µs).  So t = 256 / 512 run on 128-row tiles (68 / 81 µs
+  // against 107 / 113), t = 768..1024 and 2048 on 256-row tiles, t = 1280..1536
+  // on 128-row tiles again (225 / 232 µs against 242 / 246, where 256-row tiles
+  // spill into a second round).  Each output sums its k in the same order on
+  // both, so results are identical.
+  DevInfo di{};
+  const int64_t cus = device_info(&di) == 0 && di.cus > 0 ? di.cus : 256;
+  const int64_t r128 = (int64_t((a.t + 127) / 128) * tiles_n + cus - 1) / cus;
+  const int64_t r256 = (int64_t((a.t + 255) / 256) * tiles_n + cus - 1) / cus;
+  const bool small = a.t <= 128 || 7 * r128 < 12 * r256;
   const bool aff = a.f == QMM_AFFINE4_G64;
-  if (a.t > 128) {
+  if (!small) {
     if (aff)
       fast ? go(gemm_kernel<QMM_AFFINE4_G64, 256, true>, 256) : go(gemm_kernel<QMM_AFFINE4_G64, 256, false>, 256);
     else

@@ -3,6 +3,8 @@
 // (format and layout in qmm_internal.h).
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -163,15 +165,16 @@ int device_info(DevInfo* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return int(e);
-  static int cached_dev = -1, cached_cus = 0;
-  if (cached_dev != dev) {
-    int cus = 0;
+  // per-device cache, safe under concurrent callers (a racing first query
+  // stores the same value twice)
+  static std::atomic<int> cached_cus[64];
+  int cus = dev >= 0 && dev < 64 ? cached_cus[dev].load(std::memory_order_relaxed) : 0;
+  if (cus <= 0) {
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return int(e);
-    cached_cus = cus;
-    cached_dev = dev;
+    if (dev >= 0 && dev < 64) cached_cus[dev].store(cus, std::memory_order_relaxed);
   }
-  out->cus = cached_cus;
+  out->cus = cus;
   return 0;
 }
 

@@ -313,6 +313,25 @@ def test_gemm_mxfp4(t, n, d, elo, ecount):
     assert_parity(y, yr, ar, f"gemm mxfp4 {t}x{n}x{d}")
 
 
+@pytest.mark.parametrize("fmt,d", [(A, 512), (A, 576), (M, 512), (M, 1056)])
+def test_gemm_256_row_tiles(fmt, d):
+    """2048 x 4352 outputs: 272 tiles of 128 rows, more than a 256-CU chip has
+    CUs, so the launcher takes the 256-row tile; d a multiple of 512 or not
+    (whole-region or per-slab weight addressing), MXFP4 with a half K step."""
+    t, n = 2048, 4352
+    say("gemm 256-row tiles", fmt, t, n, d)
+    x = synth.activations(6300 + d, synth.S_X, t, d)
+    if fmt == A:
+        w = synth.affine_weights(5300 + d, n, d)
+        y = run_gemm(A, pack_affine(w), n, d, x)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(7300 + d, n, d)
+        y = run_gemm(M, pack_mxfp4(w), n, d, x)
+        yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    assert_parity(y, yr, ar, f"gemm 256-row tiles {fmt} {t}x{n}x{d}")
+
+
 def test_gemm_integer_exact():
     say("gemm integer exact")
     rng = np.random.default_rng(6)
