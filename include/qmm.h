@@ -259,10 +259,11 @@ qmm_status qmm_route(const qmm_bf16* x, int64_t t, int64_t d, const qmm_bf16* r,
  * "LLM Decode / Prefill 优化案例（Metal）", Step 1).  Arms two caller-owned
  * hipEvent_t handles for the next qmm_gemv / qmm_gemm / qmm_grouped_gemm /
  * qmm_grouped_gemm_swiglu / qmm_moe_combine / qmm_route / qmm_stream_read call
- * on this thread: its kernel is launched with hipExtLaunchKernel so `start`
- * and `stop` are stamped by the dispatch itself, and their elapsed time is
- * the kernel's execution time.  Either may be NULL.  The arming is consumed
- * by that next launch; a call rejected by validation leaves it armed. */
+ * on this thread: its kernels are launched with hipExtLaunchKernel so `start`
+ * is stamped by the dispatch of its first kernel and `stop` by that of its last
+ * (calls of several kernels: qmm_route, qmm_gemm split along K), and their
+ * elapsed time is the call's execution time.  Either may be NULL.  The arming
+ * is consumed by that next call; a call rejected by validation leaves it armed. */
 qmm_status qmm_profile_next(void* start_event, void* stop_event);
 
 /* Measurement support: the achievable HBM read rate.  Reads every byte of the
