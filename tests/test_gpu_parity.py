@@ -332,6 +332,38 @@ def test_gemm_256_row_tiles(fmt, d):
     assert_parity(y, yr, ar, f"gemm 256-row tiles {fmt} {t}x{n}x{d}")
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_gemm_random_shapes(seed):
+    """Seeded random shapes across the GEMM's paths, two per (path, format):
+    the GEMV (t = 1), the split-K kernel (2 <= t <= 64 with a workspace), the
+    tile kernel for the same t without one, and t > 64; d a multiple of 512 or
+    ending in a narrow slab (MXFP4 also in a half K step), n and t ragged."""
+    rng = np.random.default_rng(900 + seed)
+    fmt = A if (seed // 4) % 2 == 0 else M
+    kind = seed % 4
+    g = 64 if fmt == A else 32
+    d = int(rng.integers(1, 41)) * g
+    n = int(rng.integers(1, 700))
+    t = [1, int(rng.integers(2, 65)), int(rng.integers(2, 65)), int(rng.integers(65, 400))][kind]
+    use_ws = kind == 1
+    say("gemm random", seed, "fmt", fmt, "t n d", t, n, d, "ws", use_ws)
+    x = synth.activations(9000 + seed, synth.S_X, t, d)
+    if fmt == A:
+        w = synth.affine_weights(9100 + seed, n, d)
+        packed = pack_affine(w)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(9100 + seed, n, d)
+        packed = pack_mxfp4(w)
+        yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    need = qmm.qmm_workspace_bytes(fmt, t, n, d)
+    ws = torch.full((max(need, 4) // 4,), float("nan"), dtype=torch.float32, device=DEV) if use_ws and need else None
+    y = nan_out(t, n)
+    qmm.qmm_gemm(fmt, packed, t, n, d, dev(x), y, ws)
+    torch.cuda.synchronize()
+    assert_parity(host_u16(y), yr, ar, f"gemm random {seed}: fmt {fmt} {t}x{n}x{d} ws {use_ws}")
+
+
 def test_gemm_integer_exact():
     say("gemm integer exact")
     rng = np.random.default_rng(6)
