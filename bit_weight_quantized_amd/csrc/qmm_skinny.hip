@@ -34,6 +34,11 @@ constexpr uint32_t kOOB = 0x80000000u;   // OR-ed into a buffer offset: past eve
 // chunk c stored at position c ^ (r & 15), so the 16 rows of one MFMA operand
 // read (same chunk) fall in 16 different bank groups
 __device__ __forceinline__ int xs_at(int r, int c) { return r * kSlabCodes + ((c ^ (r & 15)) << 3); }
+// After the activation slab (one 16-row block; affine weights): a block of
+// zeros that half the lanes read instead of activations, then the 16 rows'
+// activation sums per 64-code group (fp32).
+constexpr int kZeroElems = 512;
+constexpr int kSkExtraBytes = kZeroElems * 2 + 16 * 8 * 4;
 
 template <int FMT, int NRB>
 __global__ __launch_bounds__(256, 2) void skinny_kernel(const uint8_t* __restrict__ codes,
@@ -105,14 +110,99 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(const uint8_t* __restric
   }
   __syncthreads();
 
-  // 3. per step: the metadata each lane's chunk needs (from the lane that
-  //    loaded that column), then per word j the four column blocks'
-  //    dequantised words and the MFMAs of every row block
   f32x4_t acc[NRB][4];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if constexpr (FMT == QMM_AFFINE4_G64 && NRB == 1) {
+    // 3'. Affine, one row block: the codes enter the MFMAs as the exact bf16
+    //     values 128 + q (one v_and_or per pair instead of a dequantisation
+    //     per weight), one group per MFMA, and scale and bias are applied per
+    //     group afterwards:  Σ_k x·(s·q + b) = s·Σ_k x·(128 + q) + (b − 128·s)·Σ_k x.
+    //     A 128-code step holds two groups, lane group g's chunk lying in
+    //     group g / 2; the MFMAs of group h read activations on the lanes of
+    //     that half and zeros on the others, so each sums one group only.
+    uint16_t* zero = xs + 16 * kSlabCodes;
+    float* xsum = reinterpret_cast<float*>(zero + kZeroElems);
+    if (tid < kZeroElems / 8) *reinterpret_cast<u32x4_t*>(zero + 8 * tid) = u32x4_t{0u, 0u, 0u, 0u};
+    if (tid < 128) {   // row tid / 8, group tid % 8: its 64 activations summed in order
+      const int r = tid >> 3, gr = tid & 7;
+      float sum = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&xs[xs_at(r, 8 * gr + c)]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum = (sum + bf16_lo(v[q])) + bf16_hi(v[q]);
+      }
+      xsum[r * 8 + gr] = sum;
+    }
+    __syncthreads();
+    const int gh = g >> 1;
+    int aoff[4][2];   // element offset of word j's activations for group h (step 0)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int own = col_l * kSlabCodes + (((4 * g + j) ^ col_l) << 3);
+      aoff[j][0] = gh == 0 ? own : 16 * kSlabCodes;
+      aoff[j][1] = gh == 1 ? own : 16 * kSlabCodes;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (128 * s >= w) break;   // a narrow last slab ends early (uniform)
+      float gs[4][2], gc[4][2];   // scale and b − 128·s of groups 2s, 2s + 1 for the lane's column
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int src = 4 * (16 * cb + col_l);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t m = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mv[2 * s + h])));
+          gs[cb][h] = bf16_lo(m);
+          gc[cb][h] = __builtin_fmaf(-128.0f, bf16_lo(m), bf16_hi(m));
+        }
+      }
+      f32x4_t pg[4][2];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) pg[cb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4_t b[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const uint32_t v = wr[cb][s][j];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) b[cb][r] = and_or(v >> (4 * r), 0x000F000Fu, kMagic128x2);   // (128 + q) pairs
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xs[aoff[j][h] + 128 * s]);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            pg[cb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[cb]), pg[cb][h], 0, 0, 0);
+        }
+      }
+      // the lane's rows 4g + r: acc += s·P + (b − 128·s)·Σx, group 2s then 2s + 1
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float2 xg = *reinterpret_cast<const float2*>(&xsum[(4 * g + r) * 8 + 2 * s]);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          float v = acc[0][cb][r];
+          v = __builtin_fmaf(gs[cb][0], pg[cb][0][r], v);
+          v = __builtin_fmaf(gc[cb][0], xg.x, v);
+          v = __builtin_fmaf(gs[cb][1], pg[cb][1][r], v);
+          v = __builtin_fmaf(gc[cb][1], xg.y, v);
+          acc[0][cb][r] = v;
+        }
+      }
+    }
+  } else {
+  // 3. per step: the metadata each lane's chunk needs (from the lane that
+  //    loaded that column), then per word j the four column blocks'
+  //    dequantised words and the MFMAs of every row block
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     if (128 * s >= w) break;   // a narrow last slab ends early (uniform)
@@ -150,6 +240,8 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(const uint8_t* __restric
               __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bf[cb]), acc[rb][cb], 0, 0, 0);
       }
     }
+  }
+
   }
 
   // 4. this slab's partial sums: lane holds column col_l, rows 4g + r of each block
@@ -198,7 +290,7 @@ int launch_skinny(const GemmArgs& a, float* ws, void* stream) {
   const int slabs = (a.d + kSlabCodes - 1) / kSlabCodes;
   const dim3 grid(unsigned((a.n + 255) / 256), unsigned(slabs));
   const int rb = (a.t + 15) / 16;   // row blocks: 1, 2 or 4 (the launched kernel's NRB)
-  const size_t lds = size_t(rb == 3 ? 4 : rb) * 16 * kSlabCodes * 2;
+  const size_t lds = size_t(rb == 3 ? 4 : rb) * 16 * kSlabCodes * 2 + kSkExtraBytes;
   const uint32_t cb = uint32_t(int64_t(a.n) * (a.d / 2)), mb = uint32_t(l.meta_bytes);
   const int64_t tn = int64_t(a.t) * a.n;
   const unsigned rgrid = unsigned(std::min<int64_t>((tn + 255) / 256, 4096));

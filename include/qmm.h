@@ -150,7 +150,10 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
  * qmm_workspace_bytes(f, t, n, d) bytes the product is split along d: each
  * 512-code slab's fp32 partial sums go to the workspace and a second kernel
  * adds them in slab order, then rounds to bf16 (a batch of decode rows streams
- * the weights once across the whole chip); without one, the tile kernel. */
+ * the weights once across the whole chip); without one, the tile kernel.  On
+ * that path, affine weights with t <= 16 enter the MFMA as 128 + q (exact) and
+ * scale and bias are applied per group in fp32, so the weights are not rounded
+ * to bf16 there. */
 qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
                     const qmm_bf16* x, qmm_bf16* y, void* ws, size_t ws_bytes, void* stream);
 
