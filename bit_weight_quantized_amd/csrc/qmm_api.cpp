@@ -72,7 +72,8 @@ size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d) {
 size_t qmm_workspace_bytes(qmm_format f, int64_t t, int64_t n, int64_t d) {
   qmm::Layout l;
   if (!valid_format(f) || n < 1 || d < 1 || !qmm::layout_of(f, n, d, &l)) return 0;
-  return qmm::skinny_fits(t, n, d, l) ? qmm::skinny_workspace_bytes(t, n, d) : 0;
+  return qmm::skinny_fits(t, n, d, l) ? qmm::skinny_workspace_bytes(t, n, d)
+                                      : qmm::tile_split_workspace_bytes(t, n, d, l);
 }
 
 uint32_t qmm_layout_version(void) { return qmm::kLayoutVersion; }
@@ -222,7 +223,9 @@ qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int6
   a.d = int(d);
   a.x = x;
   a.y = y;
-  int err = need && ws ? qmm::launch_skinny(a, static_cast<float*>(ws), stream) : qmm::launch_gemm(a, stream);
+  int err = need && ws && t <= qmm::kSkinnyMaxT
+                ? qmm::launch_skinny(a, static_cast<float*>(ws), stream)
+                : qmm::launch_gemm_ws(a, need ? static_cast<float*>(ws) : nullptr, need ? ws_bytes : 0, stream);
   if (err) return hip_fail(err, "qmm_gemm");
   return QMM_OK;
 }

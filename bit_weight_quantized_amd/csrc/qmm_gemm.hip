@@ -26,11 +26,13 @@
 // block cost a quarter of the kernel's time in extra load instructions.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "qmm_device.h"
 #include "qmm_internal.h"
 #include "qmm_launch.h"
+#include "qmm_skinny.h"
 
 namespace qmm {
 namespace {
@@ -155,13 +157,19 @@ constexpr int gemm_lds_bytes() {
 // step is past d, which reads zeros); columns past n fall past the regions or
 // into other slabs' codes, which only feed output columns that are never
 // stored.  Otherwise each step builds descriptors bounded to its slab and tile.
+//
+// Split along K (FAST only; ws non-NULL): workgroup (tile, blockIdx.y) runs the
+// ks_per steps from blockIdx.y·ks_per and writes its fp32 sums to plane
+// blockIdx.y of ws ([splits][t][n]) instead of y; a second kernel adds the
+// planes in order.  ws NULL: ks_per = the whole of d, one plane, y written.
 template <int FMT, int WM, bool FAST>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ meta, int t, int n,
                                                    int d, const uint16_t* __restrict__ x,
                                                    uint16_t* __restrict__ y, int tiles_m,
                                                    int tiles_n, uint32_t codes_bytes,
-                                                   uint32_t meta_bytes) {
+                                                   uint32_t meta_bytes, int ks_per,
+                                                   float* __restrict__ ws) {
   constexpr int RB = WM / 32;
   constexpr int XSLOT = WM * 128;
   constexpr int WBASE = kXSlots * XSLOT;
@@ -184,7 +192,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   const int cols_n = min(256, n - n0);
 
   const Slabs L{n, d, FMT};
-  const int nk = (d + 63) / 64;
+  const int nk_all = (d + 63) / 64;
+  const int ks_base = FAST ? int(blockIdx.y) * ks_per : 0;   // this workgroup's first K step
+  const int nk = FAST ? min(ks_per, nk_all - ks_base) : nk_all;   // its steps
   const uint32_t lds_base = lds_addr(lds);
 
   // ---- activation copies: wave instruction i moves rows 8(w + 4i) .. +7 ----
@@ -194,7 +204,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   const uint32_t xlane = (uint32_t(8 * wave + xrow) * uint32_t(d) + 8u * xchunk) * 2u;
   const uint32_t xstep = 64u * uint32_t(d);  // bytes between instruction i and i + 1 (32 rows)
   auto copy_x = [&](int ks, int slot, int i) {
-    const int k0 = 64 * ks;
+    const int k0 = 64 * (ks + ks_base);
     uint32_t o;
     if constexpr (FAST)   // past d: 2^31 plus at most 7 row strides, still past the range
       o = xlane + ((ks < nk ? 2u * uint32_t(k0) : 0x80000000u) + uint32_t(i) * xstep);
@@ -222,7 +232,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   auto copy_w = [&](int ks, int slot) {
     const uint32_t dst = lds_base + WBASE + slot * kWSlotBytes;
     if constexpr (FAST) {
-      const int sl = ks >> 3, j = ks & 7;   // 8 steps per slab
+      const int kg = ks + ks_base;
+      const int sl = kg >> 3, j = kg & 7;   // 8 steps per slab
       const bool in = ks < nk;
       const uint32_t sc = in ? uint32_t(sl) * slab_bytes + 32u * j : 0x80000000u;
       const uint32_t mk = FMT == QMM_AFFINE4_G64 ? 4u * j : 4u * (j >> 1);
@@ -402,6 +413,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   }
 
   // epilogue: lane holds column col_l of each 32x32 block, rows 8(r/4) + 4g + r%4
+  float* plane = FAST && ws ? ws + int64_t(blockIdx.y) * t * n : nullptr;
 #pragma unroll
   for (int i = 0; i < RB; ++i)
 #pragma unroll
@@ -411,7 +423,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rl = 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (rl < rows_m) y[int64_t(m0 + rl) * n + n0 + cl] = f32_to_bf16(acc[i][cb][r]);
+        if (rl >= rows_m) continue;
+        const int64_t at = int64_t(m0 + rl) * n + n0 + cl;
+        if (plane)
+          plane[at] = acc[i][cb][r];
+        else
+          y[at] = f32_to_bf16(acc[i][cb][r]);
       }
     }
 }
@@ -671,7 +688,9 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
 
 }  // namespace
 
-int launch_gemm(const GemmArgs& a, void* stream) {
+int launch_gemm(const GemmArgs& a, void* stream) { return launch_gemm_ws(a, nullptr, 0, stream); }
+
+int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream) {
   Layout l;
   if (!layout_of(a.f, a.n, a.d, &l)) return int(hipErrorInvalidValue);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -684,10 +703,35 @@ int launch_gemm(const GemmArgs& a, void* stream) {
   const bool fast = a.d % kSlabCodes == 0 && code_bytes + (int64_t(1) << 16) < (int64_t(1) << 31) &&
                     l.meta_bytes + (int64_t(1) << 20) < (int64_t(1) << 31);
   const uint32_t cb = fast ? uint32_t(code_bytes) : 0u, mb = fast ? uint32_t(l.meta_bytes) : 0u;
+  DevInfo di{};
+  const int64_t cus = device_info(&di) == 0 && di.cus > 0 ? di.cus : 256;
+  const int nk = (a.d + 63) / 64;
   auto go = [&](auto kernel, int wm) {
     const int tiles_m = (a.t + wm - 1) / wm;
-    launch_kernel(kernel, dim3(unsigned(tiles_m * tiles_n)), dim3(256), s, codes, meta, a.t, a.n, a.d,
-                  a.x, a.y, tiles_m, tiles_n, cb, mb);
+    const int tiles = tiles_m * tiles_n;
+    // split along K while the tiles cannot fill the chip (few rows): as many
+    // splits as fit the CUs, at most kTileSplits, each at least 8 steps
+    int splits = 1;
+    if (fast && ws && a.t > kSkinnyMaxT) {
+      splits = int(std::min<int64_t>({int64_t(kTileSplits), cus / tiles, int64_t(nk / 8)}));
+      if (splits < 2 || size_t(splits) * size_t(a.t) * size_t(a.n) * 4 > ws_bytes) splits = 1;
+    }
+    if (splits == 1) {
+      launch_kernel(kernel, dim3(unsigned(tiles)), dim3(256), s, codes, meta, a.t, a.n, a.d,
+                    a.x, a.y, tiles_m, tiles_n, cb, mb, nk, static_cast<float*>(nullptr));
+      return;
+    }
+    const int ks_per = (nk + splits - 1) / splits;
+    splits = (nk + ks_per - 1) / ks_per;
+    const ProfileEvents pe = take_profile_events();   // start with the tiles, stop with the sum
+    if (pe.start)
+      hipExtLaunchKernelGGL(kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(256), 0, s,
+                            static_cast<hipEvent_t>(pe.start), nullptr, 0, codes, meta, a.t, a.n, a.d,
+                            a.x, a.y, tiles_m, tiles_n, cb, mb, ks_per, ws);
+    else
+      hipLaunchKernelGGL(kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(256), 0, s, codes, meta,
+                         a.t, a.n, a.d, a.x, a.y, tiles_m, tiles_n, cb, mb, ks_per, ws);
+    launch_partials_sum(ws, int64_t(a.t) * a.n, splits, a.y, pe.stop, s);
   };
   // Tile height by a cost model of whole rounds of tiles over the CUs: a round
   // of 256-row tiles (one per CU) takes ~12 units, a round of 128-row tiles
@@ -697,8 +741,6 @@ int launch_gemm(const GemmArgs& a, void* stream) {
   // on 128-row tiles again (225 / 232 µs against 242 / 246, where 256-row tiles
   // spill into a second round).  Each output sums its k in the same order on
   // both, so results are identical.
-  DevInfo di{};
-  const int64_t cus = device_info(&di) == 0 && di.cus > 0 ? di.cus : 256;
   const int64_t r128 = (int64_t((a.t + 127) / 128) * tiles_n + cus - 1) / cus;
   const int64_t r256 = (int64_t((a.t + 255) / 256) * tiles_n + cus - 1) / cus;
   const bool small = a.t <= 128 || 7 * r128 < 12 * r256;

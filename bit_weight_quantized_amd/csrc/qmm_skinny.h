@@ -28,4 +28,26 @@ inline bool skinny_fits(int64_t t, int64_t n, int64_t d, const Layout& l) {
 // Y = X·Ŵᵀ for 2 <= t <= kSkinnyMaxT rows through `ws` (skinny_workspace_bytes).
 int launch_skinny(const GemmArgs& a, float* ws, void* stream);
 
+// The tile GEMM split along K for t > kSkinnyMaxT while its 128-row tiles
+// would cover at most half of a 256-CU chip: up to kTileSplits fp32 [t][n]
+// planes (whole-region weight addressing only: d a multiple of 512).
+constexpr int kTileSplits = 4;
+inline size_t tile_split_workspace_bytes(int64_t t, int64_t n, int64_t d, const Layout& l) {
+  const bool whole = d % kSlabCodes == 0 && n * (d / 2) + (int64_t(1) << 16) < (int64_t(1) << 31) &&
+                     l.meta_bytes + (int64_t(1) << 20) < (int64_t(1) << 31);
+  const int64_t tiles128 = ((t + 127) / 128) * ((n + 255) / 256);
+  if (!whole || t <= kSkinnyMaxT || tiles128 > 128 || d / 64 < 16 ||
+      int64_t(kTileSplits) * t * n >= (int64_t(1) << 31))
+    return 0;
+  return size_t(kTileSplits) * size_t(t) * size_t(n) * 4;
+}
+
+// The tile GEMM, split along K through `ws` when it helps and ws_bytes allows
+// (ws NULL: launch_gemm).
+int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream);
+
+// y[i] = bf16(Σ_p ws[p·tn + i]) over `planes` planes in order; `stop`, when
+// not NULL, is a hipEvent_t stamped by the kernel's dispatch.
+void launch_partials_sum(const float* ws, int64_t tn, int planes, uint16_t* y, void* stop, void* stream);
+
 }  // namespace qmm

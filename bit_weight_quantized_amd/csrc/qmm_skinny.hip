@@ -293,7 +293,6 @@ int launch_skinny(const GemmArgs& a, float* ws, void* stream) {
   const size_t lds = size_t(rb == 3 ? 4 : rb) * 16 * kSlabCodes * 2 + kSkExtraBytes;
   const uint32_t cb = uint32_t(int64_t(a.n) * (a.d / 2)), mb = uint32_t(l.meta_bytes);
   const int64_t tn = int64_t(a.t) * a.n;
-  const unsigned rgrid = unsigned(std::min<int64_t>((tn + 255) / 256, 4096));
   // armed profiling events: start with the first kernel, stop with the second
   const ProfileEvents pe = take_profile_events();
   const int nrb = (a.t + 15) / 16;
@@ -308,13 +307,18 @@ int launch_skinny(const GemmArgs& a, float* ws, void* stream) {
                           codes, meta, cb, mb, a.t, a.n, a.d, a.x, ws);
   else
     hipLaunchKernelGGL(k1, grid, dim3(256), lds, s, codes, meta, cb, mb, a.t, a.n, a.d, a.x, ws);
-  if (pe.stop)
-    hipExtLaunchKernelGGL(skinny_reduce_kernel, dim3(rgrid), dim3(256), 0, s, nullptr,
-                          static_cast<hipEvent_t>(pe.stop), 0, static_cast<const float*>(ws), tn, slabs, a.y);
-  else
-    hipLaunchKernelGGL(skinny_reduce_kernel, dim3(rgrid), dim3(256), 0, s, static_cast<const float*>(ws), tn,
-                       slabs, a.y);
+  launch_partials_sum(ws, tn, slabs, a.y, pe.stop, s);
   return int(hipGetLastError());
+}
+
+void launch_partials_sum(const float* ws, int64_t tn, int planes, uint16_t* y, void* stop, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned grid = unsigned(std::min<int64_t>((tn + 255) / 256, 4096));
+  if (stop)
+    hipExtLaunchKernelGGL(skinny_reduce_kernel, dim3(grid), dim3(256), 0, s, nullptr, static_cast<hipEvent_t>(stop),
+                          0, ws, tn, planes, y);
+  else
+    hipLaunchKernelGGL(skinny_reduce_kernel, dim3(grid), dim3(256), 0, s, ws, tn, planes, y);
 }
 
 }  // namespace qmm

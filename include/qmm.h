@@ -87,9 +87,11 @@ typedef uint16_t qmm_bf16; /* raw bf16 bits */
 size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
 
 /* Workspace that lets qmm_gemm(f, t, n, d) take its fastest path (bytes, 0 =
- * none helps; 0 also for an invalid shape).  Nonzero for 2 <= t <= 64 rows: one
- * fp32 [t][n] plane per 512-code slab of d, ceil(d/512)·t·n·4 bytes (2.2 MB for
- * t = 4, n = 13824, d = 5120).  A workspace is always optional: every call
+ * none helps; 0 also for an invalid shape).  For 2 <= t <= 64 rows: one fp32
+ * [t][n] plane per 512-code slab of d, ceil(d/512)·t·n·4 bytes (2.2 MB for
+ * t = 4, n = 13824, d = 5120).  For larger t while the tile kernel has few
+ * tiles (128-row tiles over at most 128 workgroups) and d is a multiple of 512:
+ * 4·t·n·4 bytes, up to four K-split planes.  A workspace is always optional: every call
  * accepts ws = NULL (qmm_gemm then runs its tile kernel, several times slower
  * for such t); a non-NULL ws must be 16-byte aligned and hold at least this many
  * bytes (QMM_E_ALIGN, QMM_E_WORKSPACE).  Its contents on entry do not matter,
@@ -150,7 +152,9 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
  * qmm_workspace_bytes(f, t, n, d) bytes the product is split along d: each
  * 512-code slab's fp32 partial sums go to the workspace and a second kernel
  * adds them in slab order, then rounds to bf16 (a batch of decode rows streams
- * the weights once across the whole chip); without one, the tile kernel.  On
+ * the weights once across the whole chip); without one, the tile kernel.  For
+ * t > 64 with few tiles and a workspace, the tile kernel itself is split along
+ * d into up to four fp32 planes summed in order.  On
  * that path, affine weights with t <= 16 enter the MFMA as 128 + q (exact) and
  * scale and bias are applied per group in fp32, so the weights are not rounded
  * to bf16 there. */

@@ -64,8 +64,13 @@ def test_workspace_contract():
     # 512-code slab of d; nothing for other t or invalid shapes
     assert qmm.qmm_workspace_bytes(A, 2, 13824, 5120) == 10 * 2 * 13824 * 4
     assert qmm.qmm_workspace_bytes(M, 64, 300, 1088) == 3 * 64 * 300 * 4
-    for t in (1, 65, 2048):
+    for t in (1, 2048, 300):
         assert qmm.qmm_workspace_bytes(A, t, 13824, 5120) == 0
+    # the tile kernel split along K (up to 4 planes) while 128-row tiles would
+    # cover at most half of a 256-CU chip; d a multiple of 512 only
+    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5120) == 4 * 65 * 13824 * 4
+    assert qmm.qmm_workspace_bytes(M, 256, 13824, 5120) == 4 * 256 * 13824 * 4
+    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5056) == 0
     assert qmm.qmm_workspace_bytes(A, 4, 8, 96) == 0
     # optional, but one that is passed must be large enough and 16-byte aligned
     # (host validation: nothing is launched)

@@ -336,7 +336,8 @@ def test_gemm_256_row_tiles(fmt, d):
 def test_gemm_random_shapes(seed):
     """Seeded random shapes across the GEMM's paths, two per (path, format):
     the GEMV (t = 1), the split-K kernel (2 <= t <= 64 with a workspace), the
-    tile kernel for the same t without one, and t > 64; d a multiple of 512 or
+    tile kernel for the same t without one, and t > 64 with a workspace (the
+    tile kernel, split along K when its tiles are few); d a multiple of 512 or
     ending in a narrow slab (MXFP4 also in a half K step), n and t ragged."""
     rng = np.random.default_rng(900 + seed)
     fmt = A if (seed // 4) % 2 == 0 else M
@@ -345,7 +346,7 @@ def test_gemm_random_shapes(seed):
     d = int(rng.integers(1, 41)) * g
     n = int(rng.integers(1, 700))
     t = [1, int(rng.integers(2, 65)), int(rng.integers(2, 65)), int(rng.integers(65, 400))][kind]
-    use_ws = kind == 1
+    use_ws = kind in (1, 3)
     say("gemm random", seed, "fmt", fmt, "t n d", t, n, d, "ws", use_ws)
     x = synth.activations(9000 + seed, synth.S_X, t, d)
     if fmt == A:
@@ -409,6 +410,49 @@ def test_gemm_split_k_mxfp4(t, n, d, elo, ecount):
     y = run_gemm_split(M, pack_mxfp4(w), n, d, x)
     yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
     assert_parity(y, yr, ar, f"gemm split-k mxfp4 {t}x{n}x{d}")
+
+
+def run_gemm_ws(fmt, packed, n, d, x_bits):
+    """qmm_gemm given the workspace qmm_workspace_bytes asks for (NaN-filled)."""
+    t = x_bits.shape[0]
+    need = qmm.qmm_workspace_bytes(fmt, t, n, d)
+    assert need > 0
+    ws = torch.full((need // 4,), float("nan"), dtype=torch.float32, device=DEV)
+    y = nan_out(t, n)
+    qmm.qmm_gemm(fmt, packed, t, n, d, dev(x_bits), y, ws)
+    torch.cuda.synchronize()
+    return host_u16(y)
+
+
+@pytest.mark.parametrize("fmt,t,n,d", [(A, 65, 300, 1024), (A, 128, 1000, 2048), (M, 200, 700, 3072),
+                                       (A, 256, 4352, 1024), (M, 97, 257, 1536)])
+def test_gemm_tile_split_k(fmt, t, n, d):
+    """t > 64 with few tiles: the tile kernel split along K into 2, 3 or 4
+    fp32 planes (ragged t and n, both formats), summed in order."""
+    say("gemm tile split-k", fmt, t, n, d)
+    x = synth.activations(6400 + t, synth.S_X, t, d)
+    if fmt == A:
+        w = synth.affine_weights(5400 + n, n, d)
+        y = run_gemm_ws(A, pack_affine(w), n, d, x)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(7400 + n, n, d)
+        y = run_gemm_ws(M, pack_mxfp4(w), n, d, x)
+        yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    assert_parity(y, yr, ar, f"gemm tile split-k {fmt} {t}x{n}x{d}")
+
+
+def test_gemm_tile_split_k_integer_exact():
+    """Integer weights and activations through the split tile kernel: exact."""
+    say("gemm tile split-k integer exact")
+    rng = np.random.default_rng(17)
+    t, n, d = 130, 300, 2048
+    w = integer_affine(24, n, d)
+    x = synth.bf16_bits(rng.integers(-3, 4, size=(t, d)).astype(float))
+    yr, _ = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    assert np.all(np.abs(yr) < 2 ** 24)
+    y = run_gemm_ws(A, pack_affine(w), n, d, x)
+    assert np.array_equal(y, oracle.f64_to_bf16_bits(yr))
 
 
 def test_gemm_split_k_integer_exact():
