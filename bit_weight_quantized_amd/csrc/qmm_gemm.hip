@@ -17,7 +17,8 @@
 //
 // Dense kernel: workgroup tile WM×256, wave w owns columns [64w, 64w + 64)
 // and all WM rows, v_mfma_f32_32x32x16_bf16, K step 64 (one affine group).
-// Grouped kernel: one workgroup per (segment, 128-column tile), rows of the
+// Grouped kernel: one workgroup per (segment, 256-column tile; 128 output
+// columns of gate and up each with the fused SwiGLU), rows of the
 // segment gathered through row_index in blocks of 64, 16x16x32 MFMA so short
 // segments waste little, K step 128.  Each expert's weight tile is read once
 // per 64 routed rows.  Group metadata is loaded once per 512-code slab, one
