@@ -129,8 +129,8 @@ def main(argv=None) -> int:
                          "'copy' adds a plain 256 MiB device copy used to calibrate HBM byte counters")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the sharding plan is described in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(its kernels run on one GPU's share at the real shapes); run with --gpus 1", file=sys.stderr)
         return 2
 
     import torch
