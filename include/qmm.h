@@ -66,7 +66,7 @@ typedef enum {
   QMM_E_ARG = 1,          /* NULL pointer, bad enum, negative size, inconsistent argument */
   QMM_E_SHAPE = 2,        /* D not a multiple of the group, size out of supported range */
   QMM_E_ALIGN = 3,        /* pointer misaligned for the call */
-  QMM_E_UNSUPPORTED = 4,  /* valid request this build does not implement */
+  QMM_E_UNSUPPORTED = 4,  /* valid request the library does not implement */
   QMM_E_WORKSPACE = 5,    /* workspace NULL or smaller than qmm_workspace_bytes() */
   QMM_E_HIP = 6,          /* HIP runtime error; see qmm_last_error() */
   QMM_E_LAYOUT = 7,       /* packed blob header does not match (format, n, d, version) */
