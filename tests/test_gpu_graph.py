@@ -1,7 +1,8 @@
 """HIP graph capture of the hot path (needs an MI355X).
 
-A decode GEMV, a prefill GEMM and a whole routed MoE layer (route -> gate_up
-with SwiGLU -> down -> combine) are recorded once into a HIP graph through
+A decode GEMV, a prefill GEMM (also split along K through a workspace, 4 and 70
+rows) and a whole routed MoE layer (route -> gate_up with SwiGLU -> down ->
+combine) are recorded once into a HIP graph through
 torch.cuda.CUDAGraph and replayed: the matmul, routing and combine calls only
 enqueue kernels on the caller's stream (no allocation, copy, memset or
 synchronization), so a replay must reproduce an eager run on the same inputs
@@ -73,9 +74,16 @@ def test_graph_replay_matches_eager():
     xd = torch.empty(dd, dtype=torch.int16, device=DEV)
     xg = torch.empty(tg, dg, dtype=torch.int16, device=DEV)
     xm = torch.empty(t, dm, dtype=torch.int16, device=DEV)
+    # the GEMM split along K (two kernels each, fp32 partials in a workspace):
+    # 4 rows through the few-row kernel, 70 rows through the split tile kernel
+    ws4 = torch.empty(qmm.qmm_workspace_bytes(A, 4, ng, dg) // 4, dtype=torch.float32, device=DEV)
+    ws70 = torch.empty(qmm.qmm_workspace_bytes(A, tg, ng, dg) // 4, dtype=torch.float32, device=DEV)
+    assert ws4.numel() > 0 and ws70.numel() > 0
     outs = {
         "gemv": (torch.empty(nd, dtype=torch.int16, device=DEV), 0x7FC0),
         "gemm": (torch.empty(tg, ng, dtype=torch.int16, device=DEV), 0x7FC0),
+        "gemm_split4": (torch.empty(4, ng, dtype=torch.int16, device=DEV), 0x7FC0),
+        "gemm_split70": (torch.empty(tg, ng, dtype=torch.int16, device=DEV), 0x7FC0),
         "scores": (torch.empty(t, ne, dtype=torch.float32, device=DEV), float("nan")),
         "topk": (torch.empty(t, k, dtype=torch.int32, device=DEV), -7),
         "seg_expert": (torch.empty(ne, dtype=torch.int32, device=DEV), -7),
@@ -99,6 +107,8 @@ def test_graph_replay_matches_eager():
     def layer():
         qmm.qmm_gemv(A, pd, nd, dd, xd, O["gemv"])
         qmm.qmm_gemm(A, pg, tg, ng, dg, xg, O["gemm"])
+        qmm.qmm_gemm(A, pg, 4, ng, dg, xg, O["gemm_split4"], ws4)
+        qmm.qmm_gemm(A, pg, tg, ng, dg, xg, O["gemm_split70"], ws70)
         qmm.qmm_route(xm, t, dm, r_d, ne, bias_d, k, O["scores"], O["topk"], O["seg_expert"],
                       O["seg_offsets"], O["row_index"])
         qmm.qmm_grouped_gemm_swiglu(M, gu, gsz, ne, 2 * ni, dm, xm, t, O["row_index"], O["seg_expert"],
