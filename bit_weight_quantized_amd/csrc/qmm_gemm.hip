@@ -159,11 +159,11 @@ constexpr int gemm_lds_bytes() {
 // into other slabs' codes, which only feed output columns that are never
 // stored.  Otherwise each step builds descriptors bounded to its slab and tile.
 //
-// Split along K (FAST only; ws non-NULL): workgroup (tile, blockIdx.y) runs the
-// ks_per steps from blockIdx.y·ks_per and writes its fp32 sums to plane
-// blockIdx.y of ws ([splits][t][n]) instead of y; a second kernel adds the
-// planes in order.  ws NULL: ks_per = the whole of d, one plane, y written.
-template <int FMT, int WM, bool FAST>
+// SPLIT (with FAST): workgroup (tile, blockIdx.y) runs the ks_per steps from
+// blockIdx.y·ks_per and writes its fp32 sums to plane blockIdx.y of ws
+// ([splits][t][n]) instead of y; a second kernel adds the planes in order.  A
+// compile-time switch, so the unsplit kernel keeps its step loop as it was.
+template <int FMT, int WM, bool FAST, bool SPLIT = false>
 __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ meta, int t, int n,
                                                    int d, const uint16_t* __restrict__ x,
@@ -194,8 +194,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
 
   const Slabs L{n, d, FMT};
   const int nk_all = (d + 63) / 64;
-  const int ks_base = FAST ? int(blockIdx.y) * ks_per : 0;   // this workgroup's first K step
-  const int nk = FAST ? min(ks_per, nk_all - ks_base) : nk_all;   // its steps
+  const int ks_base = SPLIT ? int(blockIdx.y) * ks_per : 0;   // this workgroup's first K step
+  const int nk = SPLIT ? min(ks_per, nk_all - ks_base) : nk_all;   // its steps
   const uint32_t lds_base = lds_addr(lds);
 
   // ---- activation copies: wave instruction i moves rows 8(w + 4i) .. +7 ----
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   }
 
   // epilogue: lane holds column col_l of each 32x32 block, rows 8(r/4) + 4g + r%4
-  float* plane = FAST && ws ? ws + int64_t(blockIdx.y) * t * n : nullptr;
+  float* plane = SPLIT ? ws + int64_t(blockIdx.y) * t * n : nullptr;
 #pragma unroll
   for (int i = 0; i < RB; ++i)
 #pragma unroll
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
         const int rl = 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
         if (rl >= rows_m) continue;
         const int64_t at = int64_t(m0 + rl) * n + n0 + cl;
-        if (plane)
+        if constexpr (SPLIT)
           plane[at] = acc[i][cb][r];
         else
           y[at] = f32_to_bf16(acc[i][cb][r]);
@@ -707,7 +707,7 @@ int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream) 
   DevInfo di{};
   const int64_t cus = device_info(&di) == 0 && di.cus > 0 ? di.cus : 256;
   const int nk = (a.d + 63) / 64;
-  auto go = [&](auto kernel, int wm) {
+  auto go = [&](auto kernel, auto split_kernel, int wm) {
     const int tiles_m = (a.t + wm - 1) / wm;
     const int tiles = tiles_m * tiles_n;
     // split along K while the tiles cannot fill the chip (few rows): as many
@@ -726,11 +726,11 @@ int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream) 
     splits = (nk + ks_per - 1) / ks_per;
     const ProfileEvents pe = take_profile_events();   // start with the tiles, stop with the sum
     if (pe.start)
-      hipExtLaunchKernelGGL(kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(256), 0, s,
+      hipExtLaunchKernelGGL(split_kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(256), 0, s,
                             static_cast<hipEvent_t>(pe.start), nullptr, 0, codes, meta, a.t, a.n, a.d,
                             a.x, a.y, tiles_m, tiles_n, cb, mb, ks_per, ws);
     else
-      hipLaunchKernelGGL(kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(256), 0, s, codes, meta,
+      hipLaunchKernelGGL(split_kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(256), 0, s, codes, meta,
                          a.t, a.n, a.d, a.x, a.y, tiles_m, tiles_n, cb, mb, ks_per, ws);
     launch_partials_sum(ws, int64_t(a.t) * a.n, splits, a.y, pe.stop, s);
   };
@@ -746,16 +746,22 @@ int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream) 
   const int64_t r256 = (int64_t((a.t + 255) / 256) * tiles_n + cus - 1) / cus;
   const bool small = a.t <= 128 || 7 * r128 < 12 * r256;
   const bool aff = a.f == QMM_AFFINE4_G64;
+  // the split kernel exists for whole-region addressing only; otherwise the
+  // unsplit one is passed twice (go never splits without FAST)
   if (!small) {
     if (aff)
-      fast ? go(gemm_kernel<QMM_AFFINE4_G64, 256, true>, 256) : go(gemm_kernel<QMM_AFFINE4_G64, 256, false>, 256);
+      fast ? go(gemm_kernel<QMM_AFFINE4_G64, 256, true>, gemm_kernel<QMM_AFFINE4_G64, 256, true, true>, 256)
+           : go(gemm_kernel<QMM_AFFINE4_G64, 256, false>, gemm_kernel<QMM_AFFINE4_G64, 256, false>, 256);
     else
-      fast ? go(gemm_kernel<QMM_MXFP4_G32, 256, true>, 256) : go(gemm_kernel<QMM_MXFP4_G32, 256, false>, 256);
+      fast ? go(gemm_kernel<QMM_MXFP4_G32, 256, true>, gemm_kernel<QMM_MXFP4_G32, 256, true, true>, 256)
+           : go(gemm_kernel<QMM_MXFP4_G32, 256, false>, gemm_kernel<QMM_MXFP4_G32, 256, false>, 256);
   } else {
     if (aff)
-      fast ? go(gemm_kernel<QMM_AFFINE4_G64, 128, true>, 128) : go(gemm_kernel<QMM_AFFINE4_G64, 128, false>, 128);
+      fast ? go(gemm_kernel<QMM_AFFINE4_G64, 128, true>, gemm_kernel<QMM_AFFINE4_G64, 128, true, true>, 128)
+           : go(gemm_kernel<QMM_AFFINE4_G64, 128, false>, gemm_kernel<QMM_AFFINE4_G64, 128, false>, 128);
     else
-      fast ? go(gemm_kernel<QMM_MXFP4_G32, 128, true>, 128) : go(gemm_kernel<QMM_MXFP4_G32, 128, false>, 128);
+      fast ? go(gemm_kernel<QMM_MXFP4_G32, 128, true>, gemm_kernel<QMM_MXFP4_G32, 128, true, true>, 128)
+           : go(gemm_kernel<QMM_MXFP4_G32, 128, false>, gemm_kernel<QMM_MXFP4_G32, 128, false>, 128);
   }
   return int(hipGetLastError());
 }
