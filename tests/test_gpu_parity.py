@@ -647,6 +647,39 @@ def test_combine_small(t, ne, k, d):
     assert_parity(out, yr, ar, f"combine t={t} ne={ne} k={k} d={d}")
 
 
+@pytest.mark.parametrize("t,ne,k,d", [(1000, 5, 3, 64), (700, 20, 16, 40), (300, 40, 24, 16),
+                                      (300, 40, 40, 24)])
+def test_combine_long_segments(t, ne, k, d):
+    """Segments of tens to hundreds of rows, with 64, 16, 8 and 4 lanes
+    searching each slot's row (k = 3, 16, 24, 40): several narrowing rounds
+    before the last one.  Then one token is taken out of the longest segment
+    (the rows after it move up): that token's outputs are NaN, every other
+    token's unchanged."""
+    say("combine long segments", t, ne, k, d)
+    x, r, bias = synth.router_inputs(7500 + k, t=t, d=64, experts=ne)
+    sig = oracle.route_scores(x, r, None)[0].astype(np.float32)
+    tk = oracle.topk(oracle.route_scores(x, r, bias)[0], k)
+    offs, rows = oracle.group(tk, ne)
+    lens = np.diff(offs)
+    assert lens.max() > 64
+    o = synth.activations(7501 + k, synth.S_X, t * k, d)
+    out = run_combine(o, tk, sig, offs, rows, d)
+    yr, ar = oracle.combine(oracle.bf16_to_f64(o), tk, sig.astype(np.float64), offs, rows)
+    assert_parity(out, yr, ar, f"combine long t={t} ne={ne} k={k} d={d}")
+
+    e = int(np.argmax(lens))
+    pos = int(offs[e]) + int(lens[e]) // 2   # a token in the middle of the longest segment
+    gone = int(rows[pos])
+    rows2 = np.delete(rows, pos)
+    o2 = np.delete(o, pos, axis=0)
+    offs2 = offs.copy()
+    offs2[e + 1:] -= 1
+    out2 = oracle.bf16_to_f64(run_combine(o2, tk, sig, offs2, rows2, d))
+    assert np.all(np.isnan(out2[gone]))
+    keep = np.arange(t) != gone
+    assert np.array_equal(out2[keep], oracle.bf16_to_f64(out)[keep], equal_nan=True)
+
+
 def test_combine_missing_row_gives_nan():
     say("combine missing row")
     tk = np.array([[0, 1], [1, 0]])
