@@ -17,10 +17,12 @@
 //      expert id;
 //   3. grouping, one workgroup: per-expert counts with LDS atomics (order free),
 //      an exclusive scan into seg_offsets, then tokens in blocks of 512: each
-//      assignment sets its bit in an LDS bitmap [expert][512 tokens], and the
-//      thread of expert e writes the set bits in ascending token order behind
-//      its cursor -- so row_index lists each expert's tokens ascending, with no
-//      dependence on thread timing.
+//      assignment sets its bit in an LDS bitmap [expert][512 tokens], the
+//      thread of expert e turns its row of the bitmap into the row of each
+//      32-token word (its cursor plus the bits set before the word), and each
+//      assignment writes its token at that row plus the bits set below its own
+//      in the word -- so row_index lists each expert's tokens ascending, with
+//      no dependence on thread timing.
 // Segments are dense over all experts (segment e is expert e, possibly empty),
 // so the host needs no count back before launching the grouped matmul.
 #include <hip/hip_runtime.h>
@@ -255,6 +257,7 @@ __global__ __launch_bounds__(1024) void route_group_kernel(const int32_t* __rest
                                                            int32_t* __restrict__ row_index) {
   __shared__ int32_t cnt[kMaxExperts];
   __shared__ uint32_t bits[kMaxExperts][kGroupBlock / 32];
+  __shared__ int32_t wrow[kMaxExperts][kGroupBlock / 32];   // row of each word's first set bit
   __shared__ int32_t wsum[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -305,8 +308,13 @@ __global__ __launch_bounds__(1024) void route_group_kernel(const int32_t* __rest
     seg_offsets[tid] = cursor;
   }
   if (tid == ne - 1) seg_offsets[ne] = cursor + c;
-  // tokens in blocks: mark each assignment's bit, then each expert thread
-  // emits its tokens in ascending order
+  // tokens in blocks: mark each assignment's bit, give each 32-token word of
+  // an expert its first row, then every assignment writes its own row
+  auto place = [&](int e, int il, int b0) {   // assignment il of the block, expert e
+    const int tl = il / k, h = tl >> 5;
+    const uint32_t below = bits[e][h] & ((1u << (tl & 31)) - 1u);
+    row_index[wrow[e][h] + __builtin_popcount(below)] = b0 + tl;
+  };
   for (int b0 = 0; b0 < t; b0 += kGroupBlock) {
 #pragma unroll
     for (int h = 0; h < kGroupBlock / 32; ++h) bits[tid][h] = 0u;
@@ -341,11 +349,28 @@ __global__ __launch_bounds__(1024) void route_group_kernel(const int32_t* __rest
     if (tid < ne) {
 #pragma unroll
       for (int h = 0; h < kGroupBlock / 32; ++h) {
-        uint32_t m = bits[tid][h];
-        while (m) {
-          const int bpos = __builtin_ctz(m);
-          m &= m - 1u;
-          row_index[cursor++] = b0 + 32 * h + bpos;
+        wrow[tid][h] = cursor;
+        cursor += __builtin_popcount(bits[tid][h]);
+      }
+    }
+    __syncthreads();
+    // a token listed twice for one expert sets one bit: both entries write
+    // the same row, and the expert's cursor advances by one
+    if (cached) {
+#pragma unroll
+      for (int u = 0; u < kGroupCache; ++u) {
+        const int il = tid + 1024 * u - base;
+        if (il >= 0 && il < nab && uint32_t(ent[u]) < uint32_t(ne)) place(ent[u], il, b0);
+      }
+    } else {
+      for (int i0 = tid; i0 < nab; i0 += 4096) {
+        int32_t e[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) e[u] = topk[base + min(i0 + 1024 * u, nab - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int il = i0 + 1024 * u;
+          if (il < nab && uint32_t(e[u]) < uint32_t(ne)) place(e[u], il, b0);
         }
       }
     }
