@@ -87,7 +87,10 @@ typedef uint16_t qmm_bf16; /* raw bf16 bits */
 size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
 
 /* Workspace that lets qmm_gemm(f, t, n, d) take its fastest path (bytes, 0 =
- * none helps; 0 also for an invalid shape).  For 2 <= t <= 64 rows: one fp32
+ * none helps; 0 also for an invalid shape).  Every caller buffer has its size
+ * stated per format and shape by a call like this one, as the explicit
+ * per-format byte counts that fixed the NULL-scale crash of "Colibri Kimi K3
+ * Metal 后端实现全解析", Phase 10 (fmt_scale_bytes).  For 2 <= t <= 64 rows: one fp32
  * [t][n] plane per 512-code slab of d, ceil(d/512)·t·n·4 bytes (2.2 MB for
  * t = 4, n = 13824, d = 5120).  For larger t while the tile kernel has few
  * tiles (128-row tiles over at most 128 workgroups) and d is a multiple of 512:
@@ -98,7 +101,11 @@ size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
  * and calls sharing one workspace must be ordered on one stream.  Host only. */
 size_t qmm_workspace_bytes(qmm_format f, int64_t t, int64_t n, int64_t d);
 
-/* Pack canonical weights into the MI355X device layout.
+/* Pack canonical weights into the MI355X device layout.  The codes are the
+ * 4-bit values of "Kapitsa 源码拆解 02：权重、矩阵与 Metal", section "权重怎样存储"
+ * (eight codes per 32-bit word, one bf16 scale and one bf16 bias per group of
+ * 64), or the MXFP4 U8-packed codes with one E8M0 exponent per 32 of "Kimi K3
+ * 迁移到 Google TPU 的可行性评估（v2）", sections 2 and 3.1.
  *   codes   canonical codes (see above), device
  *   scales  affine: bf16 scales [n][d/64]; MXFP4: uint8 E8M0 [n][d/32], device
  *   biases  affine: bf16 biases [n][d/64]; MXFP4: must be NULL
@@ -114,7 +121,10 @@ qmm_status qmm_pack(qmm_format f, int64_t n, int64_t d, const void* codes, const
                     const void* biases, void* packed, void* stream);
 
 /* Inverse of qmm_pack (test support): rewrites the canonical arrays from a
- * blob.  SYNCHRONIZES `stream` to check the blob header first
+ * blob, so that the layout of "Kapitsa 源码拆解 02：权重、矩阵与 Metal", section
+ * "权重怎样存储", can be checked to survive packing bit for bit (every primitive
+ * checked against the CPU before it is used: "Colibri Kimi K3 Metal 后端实现全解析",
+ * Phase 5).  SYNCHRONIZES `stream` to check the blob header first
  * (QMM_E_LAYOUT on a mismatch or an invalid blob). */
 qmm_status qmm_unpack(qmm_format f, int64_t n, int64_t d, const void* packed, void* codes,
                       void* scales, void* biases, void* stream);
@@ -144,7 +154,9 @@ qmm_status qmm_gemv(qmm_format f, const void* packed, int64_t n, int64_t d, cons
 qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d, const qmm_bf16* x,
                          qmm_bf16* y, void* stream);
 
-/* Prefill GEMM: Y[t][n] = Σ_k X[t][k]·ŵ[n,k].
+/* Prefill GEMM: Y[t][n] = Σ_k X[t][k]·ŵ[n,k], the multi-row product of
+ * "Kapitsa 源码拆解 02：权重、矩阵与 Metal", section "矩阵乘法中数据和参数" (many
+ * activation rows share each weight read, unlike the one-row decode).
  *   x bf16[t][d] row-major; y bf16[t][n] row-major (written whole).
  * t = 1 runs the GEMV kernel; t > 1 dequantizes weight tiles to bf16 and
  * feeds bf16 MFMA with fp32 accumulation (the weight is rounded to bf16 once,
@@ -161,7 +173,9 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
 qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
                     const qmm_bf16* x, qmm_bf16* y, void* ws, size_t ws_bytes, void* stream);
 
-/* Routed-expert grouped matmul (all experts in one launch).
+/* Routed-expert grouped matmul (all experts in one launch): the per-expert
+ * GEMM of the MoE block of "Colibri Kimi K3 Metal 后端实现全解析", Phase 6, whose
+ * experts all run in one submission so the launch cost is paid once.
  *   packed_stack        n_experts blobs of qmm_packed_bytes(f, n, d) bytes,
  *                       blob e at packed_stack + e·expert_stride_bytes
  *                       (stride a multiple of 256, >= the blob size)
@@ -284,7 +298,10 @@ qmm_status qmm_profile_next(void* start_event, void* stop_event);
  * HBM-bound kernels against. */
 qmm_status qmm_stream_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
-/* Static description of a status code. */
+/* Static description of a status code.  Every entry point reports failure
+ * as a status the caller can act on (the stubs of "Colibri Kimi K3 Metal
+ * 后端实现全解析", Phase 4, return NOT IMPLEMENTED and the caller falls back;
+ * Phase 10's crash came from a size that was not checked). */
 const char* qmm_status_string(qmm_status s);
 
 /* Detail of the last failing call on this thread ("" if none). */

@@ -20,10 +20,14 @@ cases, one-hot columns, row sums and the tolerance checker's self-test; for the
 router, hand-worked scores and selections on tiny inputs (bias that changes the
 choice, ties to the lower id), a naive per-token full sort, the grouping's
 invariants and literal tables, and the top-k checker's self-test; for the expert
-FFN, hand-worked SiLU values and identities, a literal SwiGLU split and a
-hand-worked renormalised combine; for the deferred-dequantisation GEMV, a
-hand-worked quantisation (half-even ties, the absmax scale), an integer-exact
-case and a per-element brute force.  No function here is parity-unpinned.
+FFN, hand-worked SiLU values and identities, a literal SwiGLU split, the
+SwiGLU tolerance hand-worked and checked to bound every corner of its
+interval, and a hand-worked renormalised combine; for the
+deferred-dequantisation GEMV, a hand-worked quantisation (half-even ties, the
+absmax scale), an integer-exact case and a per-element brute force of both y
+and the size of its terms; for the router's fp32 score bound, hand-worked
+values and a simulation of fp32 summation in the GPU's order that it must
+contain.  No function here is parity-unpinned.
 """
 from __future__ import annotations
 
@@ -422,6 +426,24 @@ def combine(o, topk_ids, weights_src, seg_offsets, row_index):
             out[i] += term
             a[i] += np.abs(term)
     return out, a
+
+
+def route_score_bound(a, d):
+    """Acceptance bound on a routing weight sigmoid(logit) evaluated in fp32
+    rather than fp64, for logits accumulated as the GPU router accumulates
+    them: the products x·r of two bf16 values are exact in fp32; they are
+    summed in blocks of 32 (a tree of at most 5 roundings plus the add into
+    the running sum), the blocks of a token-expert pair accumulate in eight
+    interleaved chains of at most d/32 steps in all, and the eight chain sums
+    are added in sequence (7 roundings).  With u = 2^-24 the logit's error is
+    then at most n·u·A, n = d/32 + 12, A = Σ|x·r| (the second output of
+    route_scores), and the bound doubles it for margin.  The sigmoid's slope is
+    at most 1/4, and its own fp32 evaluation plus the fp32 add of the bias cost
+    a few ulps of 1, covered by 1e-6.  The pages fix no precision for the
+    router (its scores only choose experts and weigh their outputs), so this is
+    the reading used to accept an fp32 router; check_topk takes it as delta."""
+    gamma = 2.0 * (np.asarray(d, np.float64) / 32.0 + 12.0) * 2.0 ** -24
+    return 0.25 * gamma * np.asarray(a, np.float64) + 1e-6
 
 
 def check_topk(topk_ids, scores, delta) -> dict:

@@ -835,18 +835,6 @@ def run_route(x_bits, r_bits, bias, k):
             seg_o.cpu().numpy(), rows.cpu().numpy())
 
 
-def score_bound(a_ref, d):
-    """Error bound of an fp32 score: the logit's products are exact in fp32 and
-    are summed in 32-wide MFMA blocks (a tree of at most 5 roundings), the
-    blocks accumulate in eight interleaved chains of at most d/32 steps in all,
-    and the eight chain sums are added in sequence (7 roundings), so
-    |logit error| <= n·u·Σ|x·r| with n = d/32 + 12 and u = 2^-24, doubled for
-    margin; the sigmoid's slope is at most 1/4, and its fp32 evaluation plus
-    the bias add cost a few ulps of 1."""
-    gamma = 2.0 * (d / 32 + 12) * 2.0 ** -24
-    return 0.25 * gamma * a_ref + 1e-6
-
-
 def check_route(x, r, bias, k, what):
     """Scores are the bare sigmoid (the routing weights); the choice is made on
     sigmoid + bias, whose fp32 sum adds one rounding of at most 2^-24·|sum| to
@@ -854,7 +842,7 @@ def check_route(x, r, bias, k, what):
     s_gpu, tk, seg_e, seg_o, rows = run_route(x, r, bias, k)
     sig_ref, a_ref = oracle.route_scores(x, r, None)
     sel_ref, _ = oracle.route_scores(x, r, bias)
-    delta = score_bound(a_ref, x.shape[1])
+    delta = oracle.route_score_bound(a_ref, x.shape[1])
     err = np.abs(s_gpu - sig_ref)
     say(what, dict(max_err=float(err.max()), max_err_over_bound=float((err / delta).max())))
     assert np.all(err <= delta), what

@@ -269,6 +269,82 @@ def pin_silu():
     assert np.max(np.abs(np.diff(oracle.silu(grid)) / np.diff(grid))) <= oracle.SILU_SLOPE_MAX
 
 
+def pin_swiglu_tolerance():
+    """The SwiGLU acceptance bound, hand-worked on two elements: g = 0, u = 1
+    with both tolerances 1e-3 gives 1.1·1e-3·(1 + 1e-3) = 1.1011e-3 (silu(0) and
+    h are 0); g = 2, u = −3 with tol_g = 0.01, tol_u = 0.02 gives
+    1.1·0.01·3.02 + silu(2)·0.02 + 1e-6·|silu(2)·(−3)| = 0.06845716790158315
+    (silu(2) = 2/(1 + e^−2) = 1.7615941559557646).  And it is a bound: at
+    every corner g ± tol_g, u ± tol_u of a grid of values, the exact SwiGLU
+    moves by no more than it."""
+    y = np.array([[0.0, 2.0, 1.0, -3.0]])
+    tol = np.array([[1e-3, 1e-2, 1e-3, 2e-2]])
+    b = oracle.swiglu_tolerance(y, tol, 2)
+    assert abs(b[0, 0] - 1.1011e-3) <= 1e-15 and abs(b[0, 1] - 0.06845716790158315) <= 1e-15
+    g = np.linspace(-12.0, 12.0, 97)
+    u = np.linspace(-5.0, 5.0, 41)
+    gg, uu = [a.reshape(1, -1) for a in np.meshgrid(g, u)]
+    for rel in (1e-3, 0.05, 0.5):
+        tg, tu = rel * (np.abs(gg) + 0.1), rel * (np.abs(uu) + 0.2)
+        bound = oracle.swiglu_tolerance(np.concatenate([gg, uu], axis=1),
+                                        np.concatenate([tg, tu], axis=1), gg.shape[1])
+        h = gg / (1.0 + np.exp(-gg)) * uu
+        for sg in (-1.0, 1.0):
+            for su in (-1.0, 1.0):
+                g2, u2 = gg + sg * tg, uu + su * tu
+                assert np.all(np.abs(g2 / (1.0 + np.exp(-g2)) * u2 - h) <= bound)
+
+
+def sim_router_logit_f32(xv, rv):
+    """One logit summed in fp32 the way the GPU router sums it: products exact
+    (bf16 x bf16), 32-product blocks as a pairwise tree, block sums added into
+    eight chains (chain w takes 64-code pieces w, w + 8, ...), the chain sums
+    then added in order."""
+    p = (xv.astype(np.float32) * rv.astype(np.float32)).astype(np.float32)
+    d = p.shape[0]
+    chains = [np.float32(0.0)] * 8
+    for piece in range((d + 63) // 64):
+        for half in range(2):
+            blk = np.zeros(32, np.float32)
+            seg = p[64 * piece + 32 * half:64 * piece + 32 * half + 32]
+            blk[:seg.shape[0]] = seg
+            while blk.shape[0] > 1:
+                blk = (blk[0::2] + blk[1::2]).astype(np.float32)
+            chains[piece % 8] = np.float32(chains[piece % 8] + blk[0])
+    total = np.float32(0.0)
+    for c in chains:
+        total = np.float32(total + c)
+    return total
+
+
+def pin_route_score_bound():
+    """The router's score bound, hand-worked: A = 1, d = 64 gives
+    0.25·2·(2 + 12)·2^-24 + 1e-6 = 1.4172325134277343e-06; A = 10, d = 3584
+    gives 0.25·2·124·2^-24·10 + 1e-6 = 3.7954879760742185e-05.  And it bounds
+    an fp32 evaluation in the GPU's summation order: every simulated sigmoid
+    score, same-sign and mixed-sign inputs, lies within it of the fp64 one; a
+    score moved by twice the bound is rejected."""
+    assert abs(oracle.route_score_bound(1.0, 64) - 1.4172325134277343e-06) <= 1e-21
+    assert abs(oracle.route_score_bound(10.0, 3584) - 3.7954879760742185e-05) <= 1e-19
+    rng = np.random.default_rng(RNG_SEED + 31)
+    for d in (64, 96, 1024, 3584):
+        for trial in range(6):
+            if trial % 2:
+                xv = oracle.bf16_to_f64(synth.bf16_bits(rng.uniform(0.5, 2.0, d)))
+                rv = oracle.bf16_to_f64(synth.bf16_bits(rng.uniform(0.001, 0.02, d)))
+            else:
+                xv = oracle.bf16_to_f64(synth.bf16_bits(rng.standard_normal(d)))
+                rv = oracle.bf16_to_f64(synth.bf16_bits(rng.normal(0.0, 0.02, d)))
+            logit64 = float(np.dot(xv, rv))
+            a = float(np.dot(np.abs(xv), np.abs(rv)))
+            l32 = sim_router_logit_f32(xv, rv)
+            s32 = float(np.float32(1.0) / (np.float32(1.0) + np.exp(-l32, dtype=np.float32)))
+            s64 = 1.0 / (1.0 + np.exp(-logit64))
+            bound = float(oracle.route_score_bound(a, d))
+            assert abs(s32 - s64) <= bound, (d, trial, abs(s32 - s64), bound)
+            assert not abs((s64 + 2.0 * bound) - s64) <= bound
+
+
 def pin_swiglu_literal():
     """Gate first, up second: y = [1, −1 | 2, 3] -> [silu(1)·2, silu(−1)·3]."""
     h = oracle.swiglu(np.array([[1.0, -1.0, 2.0, 3.0]]), 2)
@@ -305,7 +381,8 @@ def pin_quantize_int8():
 
 def pin_deferred_brute():
     """The deferred GEMV written out element by element from its definition on
-    small shapes (Python ints and floats), and the integer-exact case: scale
+    small shapes (Python ints and floats), y and the size of its terms A =
+    s_x·Σ_g (|scale·isum| + |bias·xsum|), and the integer-exact case: scale
     1, bias 0 and integer x with absmax 127 make y = Σ x·q exactly."""
     rng = np.random.default_rng(RNG_SEED + 21)
     for n, d in ((3, 64), (5, 192)):
@@ -324,6 +401,12 @@ def pin_deferred_brute():
                 xsum = sum(xq[64 * gi:64 * gi + 64])
                 total += float(oracle.bf16_to_f64(w[1][r, gi])) * isum + float(oracle.bf16_to_f64(w[2][r, gi])) * xsum
             assert abs(float(sx) * total - y[r]) <= 1e-12 * max(a[r], 1e-30)
+            size = 0.0
+            for gi in range(d // 64):
+                isum = sum(xq[k] * int(codes[r, k]) for k in range(64 * gi, 64 * gi + 64))
+                xsum = sum(xq[64 * gi:64 * gi + 64])
+                size += abs(float(oracle.bf16_to_f64(w[1][r, gi])) * isum) + abs(float(oracle.bf16_to_f64(w[2][r, gi])) * xsum)
+            assert abs(float(sx) * size - a[r]) <= 1e-12 * float(sx) * size
     n, d = 4, 128
     codes = rng.integers(0, 2 ** 32, (n, d // 8), dtype=np.uint64).astype(np.uint32)
     ones = np.full((n, d // 64), 0x3F80, np.uint16)
@@ -384,6 +467,8 @@ def all_pins(golden):
     pin_check_topk()
     pin_silu()
     pin_swiglu_literal()
+    pin_swiglu_tolerance()
+    pin_route_score_bound()
     pin_combine_hand_worked()
     pin_quantize_int8()
     pin_deferred_brute()
@@ -478,6 +563,14 @@ def test_silu():
     pin_silu()
 
 
+def test_swiglu_tolerance():
+    pin_swiglu_tolerance()
+
+
+def test_route_score_bound():
+    pin_route_score_bound()
+
+
 def test_swiglu_literal():
     pin_swiglu_literal()
 
@@ -565,6 +658,15 @@ MUTATIONS = {
     "quantize_half_away": ("quantize_rows_int8", lambda orig: _quantize_half_away),
     "deferred_no_bias_correction": ("gemv_affine_deferred", lambda orig: (
         lambda x, c, s, b: orig(x, c, s, np.zeros_like(b)))),
+    "swiglu_tolerance_10x_loose": ("swiglu_tolerance", lambda orig: (lambda y, t, n: 10.0 * orig(y, t, n))),
+    "swiglu_tolerance_drops_up_term": ("swiglu_tolerance", lambda orig: (
+        lambda y, t, n: orig(y, t, n) - np.abs(oracle.silu(np.asarray(y, np.float64)[:, :n]))
+        * np.broadcast_to(np.asarray(t, np.float64), np.shape(y))[:, n:2 * n])),
+    "deferred_size_drops_bias_term": ("gemv_affine_deferred", lambda orig: (
+        lambda x, c, s, b: (orig(x, c, s, b)[0], orig(x, c, s, np.zeros_like(b))[1]))),
+    "route_bound_10x_loose": ("route_score_bound", lambda orig: (lambda a, d: 10.0 * orig(a, d))),
+    "route_bound_no_slope": ("route_score_bound", lambda orig: (lambda a, d: 4.0 * orig(a, d) - 3e-6)),
+    "route_bound_100x_tight": ("route_score_bound", lambda orig: (lambda a, d: 0.01 * orig(a, d))),
     "combine_not_renormalised": ("combine", lambda orig: (
         lambda o, tk, src, so, ri: (lambda res, sums: (res[0] * sums, res[1] * sums))(
             orig(o, tk, src, so, ri),
