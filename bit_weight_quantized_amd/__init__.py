@@ -17,7 +17,7 @@ __all__ = [
     "qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
     "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
     "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route",
-    "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "qmm_gemv_int8", "EXPORTS",
+    "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "qmm_gemv_int8", "qmm_gemm_noalloc", "EXPORTS",
 ]
 
 QMM_AFFINE4_G64 = 1
@@ -29,7 +29,7 @@ STATUS = {0: "QMM_OK", 1: "QMM_E_ARG", 2: "QMM_E_SHAPE", 3: "QMM_E_ALIGN", 4: "Q
 EXPORTS = ("qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
            "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
            "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route",
-           "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "qmm_gemv_int8")
+           "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "qmm_gemv_int8", "qmm_gemm_noalloc")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -82,6 +82,7 @@ def load():
                                                    vp, i32, i32, i32, vp, vp, sz, vp]),
         "qmm_moe_combine": (ctypes.c_int, [vp, i32, i64, i64, i32, vp, vp, i32, vp, vp, vp, vp]),
         "qmm_gemv_int8": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp, vp]),
+        "qmm_gemm_noalloc": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, i64, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -179,6 +180,11 @@ def qmm_gemv(fmt, packed, n, d, x, y, ws=None, stream=None):
 def qmm_gemm(fmt, packed, t, n, d, x, y, ws=None, stream=None):
     _check(load().qmm_gemm(fmt, _ptr(packed), t, n, d, _ptr(x), _ptr(y), _ptr(ws), _nbytes(ws),
                            _stream(stream)), "qmm_gemm")
+
+
+def qmm_gemm_noalloc(fmt, packed, t, n, d, x, y, stream=None):
+    _check(load().qmm_gemm_noalloc(fmt, _ptr(packed), t, n, d, _ptr(x), _ptr(y), _stream(stream)),
+           "qmm_gemm_noalloc")
 
 
 def qmm_grouped_gemm(fmt, packed_stack, expert_stride_bytes, n_experts, n, d, x, t_x, row_index,

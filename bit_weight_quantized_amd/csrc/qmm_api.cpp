@@ -199,8 +199,15 @@ qmm_status qmm_gemv(qmm_format f, const void* packed, int64_t n, int64_t d, cons
   return QMM_OK;
 }
 
-qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
-                    const qmm_bf16* x, qmm_bf16* y, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// qmm_gemm and its allocation-free variant: the same validation and kernels,
+// the split-K partials in the caller's workspace or in the static scratch.
+qmm_status gemm_impl(const char* name, bool noalloc, qmm_format f, const void* packed, int64_t t,
+                     int64_t n, int64_t d, const qmm_bf16* x, qmm_bf16* y, void* ws, size_t ws_bytes,
+                     void* stream) {
   g_last_error[0] = 0;
   qmm::Layout l;
   qmm_status st = check_shape(f, n, d, &l);
@@ -212,6 +219,17 @@ qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int6
   if (!aligned(x, 16)) return fail(QMM_E_ALIGN, "x must be 16-byte aligned");
   if (!aligned(y, 2)) return fail(QMM_E_ALIGN, "y must be 2-byte aligned");
   const size_t need = qmm_workspace_bytes(f, t, n, d);
+  if (noalloc) {
+    if (need > qmm::kNoAllocScratchBytes)
+      return fail(QMM_E_WORKSPACE, "the split-K partials of this shape exceed the 64 MiB static scratch of qmm_gemm_noalloc");
+    ws = nullptr;
+    ws_bytes = 0;
+    if (need && t > 1) {
+      const int err = qmm::noalloc_scratch(stream, &ws);
+      if (err) return hip_fail(err, name);
+      ws_bytes = qmm::kNoAllocScratchBytes;
+    }
+  }
   if ((st = check_ws(need, ws, ws_bytes))) return st;
   if (t == 1) return qmm_gemv(f, packed, n, d, x, y, nullptr, 0, stream);
   if (need && ws && !aligned(ws, 16)) return fail(QMM_E_ALIGN, "ws must be 16-byte aligned");
@@ -226,8 +244,22 @@ qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int6
   int err = need && ws && t <= qmm::kSkinnyMaxT
                 ? qmm::launch_skinny(a, static_cast<float*>(ws), stream)
                 : qmm::launch_gemm_ws(a, need ? static_cast<float*>(ws) : nullptr, need ? ws_bytes : 0, stream);
-  if (err) return hip_fail(err, "qmm_gemm");
+  if (err) return hip_fail(err, name);
   return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
+                    const qmm_bf16* x, qmm_bf16* y, void* ws, size_t ws_bytes, void* stream) {
+  return gemm_impl("qmm_gemm", false, f, packed, t, n, d, x, y, ws, ws_bytes, stream);
+}
+
+qmm_status qmm_gemm_noalloc(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
+                            const qmm_bf16* x, qmm_bf16* y, void* stream) {
+  return gemm_impl("qmm_gemm_noalloc", true, f, packed, t, n, d, x, y, nullptr, 0, stream);
 }
 
 namespace {

@@ -46,6 +46,12 @@ inline size_t tile_split_workspace_bytes(int64_t t, int64_t n, int64_t d, const 
 // (ws NULL: launch_gemm).
 int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream);
 
+// The static scratch of qmm_gemm_noalloc (qmm_noalloc.hip): its size, and
+// its device address on the device of `stream` (the current device for a
+// NULL stream), looked up once per device.  0 on success, else a hipError_t.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+int noalloc_scratch(void* stream, void** out);
+
 // y[i] = bf16(Σ_p ws[p·tn + i]) over `planes` planes in order; `stop`, when
 // not NULL, is a hipEvent_t stamped by the kernel's dispatch.
 void launch_partials_sum(const float* ws, int64_t tn, int planes, uint16_t* y, void* stop, void* stream);

@@ -173,6 +173,22 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
 qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
                     const qmm_bf16* x, qmm_bf16* y, void* ws, size_t ws_bytes, void* stream);
 
+/* qmm_gemm without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, kernels and results as qmm_gemm
+ * given a workspace of qmm_workspace_bytes(f, t, n, d) bytes: bitwise the same
+ * outputs.  The split-K partial sums go to a static 64 MiB device array inside
+ * the library instead (one per GPU, allocated with the library's code object
+ * and held until the process ends; its address is looked up on the first call
+ * on each device).  Limit: qmm_workspace_bytes(f, t, n, d) <= 64 MiB
+ * (67108864 bytes), else QMM_E_WORKSPACE and nothing launched.  The call
+ * allocates and frees nothing.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, unordered threads) race on
+ * it and must be serialised by the caller.  Nothing in the array needs to
+ * start at zero (each partial sum read is written first in the same call). */
+qmm_status qmm_gemm_noalloc(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
+                            const qmm_bf16* x, qmm_bf16* y, void* stream);
+
 /* Routed-expert grouped matmul (all experts in one launch): the per-expert
  * GEMM of the MoE block of "Colibri Kimi K3 Metal 后端实现全解析", Phase 6, whose
  * experts all run in one submission so the launch cost is paid once.

@@ -83,6 +83,17 @@ def test_workspace_contract():
     assert lib.qmm_gemv(A, P, 16, 64, P + 1, P, P, 1, None) == E_ALIGN   # gemv ignores ws, checks x
 
 
+def test_noalloc_limit_is_checked_on_the_host():
+    # the allocation-free GEMM refuses shapes whose split-K partials exceed its
+    # 64 MiB static scratch before looking up the scratch or launching anything
+    lib = qmm.load()
+    assert qmm.qmm_workspace_bytes(A, 64, 65536, 5120) > 64 << 20
+    assert lib.qmm_gemm_noalloc(A, P, 64, 65536, 5120, P, P, None) == E_WS
+    assert "64 MiB" in qmm.qmm_last_error()
+    assert lib.qmm_gemm_noalloc(A, P + 8, 8, 16, 64, P, P, None) == E_ALIGN
+    assert lib.qmm_gemm_noalloc(A, P, 0, 16, 64, P, P, None) == E_ARG
+
+
 def test_status_strings_and_version():
     assert qmm.qmm_status_string(0) == "ok"
     for s in range(1, 9):
