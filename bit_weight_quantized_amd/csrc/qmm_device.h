@@ -160,8 +160,11 @@ __device__ __forceinline__ float e8m0_scale(uint32_t e) {
   return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
 }
 
-// MXFP4: E2M1(c)·scale converted straight to bf16 (exact while the product
-// is a normal bf16, i.e. E8M0 in [2, 253]).
+// MXFP4: E2M1(c)·scale converted straight to bf16, exact while the product
+// is a normal bf16: for every code when E8M0 is in [2, 252].  At 253 the codes
+// of magnitude 4 and 6, at 254 those of magnitude 2 and up, reach 2^128 and
+// become ±inf (the GEMV paths scale the fp32 chunk sum instead and may stay
+// finite there).
 __device__ __forceinline__ u32x4_t mxfp4_word_to_bf16x8(uint32_t v, float scale) {
   u32x4_t r;
   r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, scale, 0));

@@ -82,6 +82,14 @@ def hashes(seed: int, stream: int, sub: int, start: int, count: int) -> np.ndarr
         return _mix64(k + i * np.uint64(GAMMA))
 
 
+def hashes_at(seed: int, stream: int, sub: int, idx) -> np.ndarray:
+    """h(seed, stream, sub, i) for every i in the integer array `idx`."""
+    k = np.uint64(key(seed, stream, sub))
+    i = np.asarray(idx, np.uint64) + np.uint64(1)
+    with np.errstate(over="ignore"):
+        return _mix64(k + i * np.uint64(GAMMA))
+
+
 def code_bytes(seed: int, stream: int, sub: int, nbytes: int, start_byte: int = 0) -> np.ndarray:
     """Bytes [start_byte, start_byte + nbytes) of the little-endian hash stream."""
     if nbytes == 0:
@@ -183,6 +191,28 @@ def mxfp4_weights(seed: int, n: int, d: int, codes_stream: int, e8m0_stream: int
     codes = code_bytes(seed, codes_stream, sub, n * d // 2).reshape(n, d // 2)
     e = small_int(seed, e8m0_stream, sub, n * (d // 32), e_lo, e_count).astype(np.uint8)
     return MXFP4(codes, e.reshape(n, d // 32))
+
+
+def mxfp4_rows(seed: int, n: int, d: int, codes_stream: int, e8m0_stream: int, sub: int, rows,
+               e_lo: int = 118, e_count: int = 9) -> MXFP4:
+    """Rows `rows` of mxfp4_weights(seed, n, d, ...), each regenerated on its
+    own from its place in the counter streams (row j's codes are bytes
+    [j·d/2, (j+1)·d/2) of the code stream, its exponents elements
+    [j·d/32, (j+1)·d/32) of the E8M0 stream)."""
+    rows = np.asarray(rows, np.int64).reshape(-1)
+    if d % 32 or rows.size and (rows.min() < 0 or rows.max() >= n):
+        raise ValueError("d must be a multiple of 32 and rows inside [0, n)")
+    b = rows[:, None] * (d // 2) + np.arange(d // 2)[None, :]          # byte offsets in the code stream
+    h = hashes_at(seed, codes_stream, sub, b // 8)
+    codes = ((h >> (np.uint64(8) * (b % 8).astype(np.uint64))) & np.uint64(0xFF)).astype(np.uint8)
+    ie = rows[:, None] * (d // 32) + np.arange(d // 32)[None, :]
+    he = hashes_at(seed, e8m0_stream, sub, ie)
+    e = e_lo + (((he >> np.uint64(32)) * np.uint64(e_count)) >> np.uint64(32)).astype(np.int64)
+    return MXFP4(codes, e.astype(np.uint8))
+
+
+def expert_gate_up_rows(seed: int, e: int, rows, n: int = 6144, d: int = 3584) -> MXFP4:
+    return mxfp4_rows(seed, n, d, S_GU_CODES, S_GU_E8M0, e, rows)
 
 
 def expert_gate_up(seed: int, e: int, n: int = 6144, d: int = 3584) -> MXFP4:

@@ -47,3 +47,15 @@ def test_draw_experts():
     e = synth.draw_experts(1003, 16, 896, 0)
     assert len(set(e.tolist())) == 16 and e.min() >= 0 and e.max() < 896
     assert not np.array_equal(e, synth.draw_experts(1003, 16, 896, 1))
+
+
+def test_rows_regenerate_alone():
+    # any rows of an expert matrix regenerate bit for bit without the rest
+    full = synth.expert_gate_up(1003, 17, n=96, d=256)
+    rows = [0, 5, 31, 32, 95]
+    part = synth.expert_gate_up_rows(1003, 17, rows, n=96, d=256)
+    assert np.array_equal(part.codes, full.codes[rows]) and np.array_equal(part.e8m0, full.e8m0[rows])
+    whole = synth.expert_gate_up(1003, 4)
+    part = synth.expert_gate_up_rows(1003, 4, [0, 255, 256, 6143])
+    assert np.array_equal(part.codes, whole.codes[[0, 255, 256, 6143]])
+    assert np.array_equal(part.e8m0, whole.e8m0[[0, 255, 256, 6143]])
