@@ -223,8 +223,11 @@ def main(argv=None) -> int:
         p2s = [p2, p2.clone()]
         x2 = T(synth.activations(synth.seed_of(2), synth.S_X, t2, d2))
         y2 = torch.empty(t2, n2, dtype=torch.int16, device=dev)
+        # affine weights: the activations go to fp16 in the workspace first (the
+        # pre-pass kernel is inside the stamped interval)
+        ws2 = torch.empty(qmm.qmm_workspace_bytes(A, t2, n2, d2) // 4, dtype=torch.float32, device=dev)
         b2 = n2 * d2 * 36 // 64 + 2 * t2 * d2 + 2 * t2 * n2
-        work["prefill"] = [(lambda s: qmm.qmm_gemm(A, p2s[s % 2], t2, n2, d2, x2, y2),
+        work["prefill"] = [(lambda s: qmm.qmm_gemm(A, p2s[s % 2], t2, n2, d2, x2, y2, ws2),
                             "gemm", b2, 2.0 * t2 * n2 * d2)]
         log("prefill ready")
 

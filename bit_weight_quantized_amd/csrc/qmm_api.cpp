@@ -72,8 +72,9 @@ size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d) {
 size_t qmm_workspace_bytes(qmm_format f, int64_t t, int64_t n, int64_t d) {
   qmm::Layout l;
   if (!valid_format(f) || n < 1 || d < 1 || !qmm::layout_of(f, n, d, &l)) return 0;
+  if (t < 2 || t > qmm::kMaxT) return 0;
   return qmm::skinny_fits(t, n, d, l) ? qmm::skinny_workspace_bytes(t, n, d)
-                                      : qmm::tile_split_workspace_bytes(t, n, d, l);
+                                      : size_t(qmm::tile_ws_layout(f, t, n, d, l).total);
 }
 
 uint32_t qmm_layout_version(void) { return qmm::kLayoutVersion; }
@@ -232,6 +233,8 @@ qmm_status gemm_impl(const char* name, bool noalloc, qmm_format f, const void* p
   }
   if ((st = check_ws(need, ws, ws_bytes))) return st;
   if (t == 1) return qmm_gemv(f, packed, n, d, x, y, nullptr, 0, stream);
+  if (f == QMM_AFFINE4_G64 && !ws)
+    return fail(QMM_E_WORKSPACE, "affine weights with t >= 2 need a workspace of qmm_workspace_bytes() bytes");
   if (need && ws && !aligned(ws, 16)) return fail(QMM_E_ALIGN, "ws must be 16-byte aligned");
   qmm::GemmArgs a{};
   a.f = f;
@@ -241,7 +244,7 @@ qmm_status gemm_impl(const char* name, bool noalloc, qmm_format f, const void* p
   a.d = int(d);
   a.x = x;
   a.y = y;
-  int err = need && ws && t <= qmm::kSkinnyMaxT
+  int err = ws && qmm::skinny_fits(t, n, d, l)
                 ? qmm::launch_skinny(a, static_cast<float*>(ws), stream)
                 : qmm::launch_gemm_ws(a, need ? static_cast<float*>(ws) : nullptr, need ? ws_bytes : 0, stream);
   if (err) return hip_fail(err, name);

@@ -1,12 +1,18 @@
 // Prefill GEMM and routed-expert grouped GEMM on gfx950 MFMA.
 //
-// Y = X·Ŵᵀ is the one dense contraction of the path, so it runs on bf16 MFMA
-// with fp32 accumulation.  Weights stay 4-bit in HBM: each wave streams the
-// packed codes of its own output columns straight from global memory into
-// registers, dequantises them there into bf16 MFMA B operands, and never
-// writes dequantised weights back to memory (materialising them would move
-// four times the bytes).  Activation tiles are shared by the four waves of a
-// workgroup through LDS.
+// Y = X·Ŵᵀ is the one dense contraction of the path, so it runs on MFMA with
+// fp32 accumulation.  Weights stay 4-bit in HBM and are dequantised in
+// registers into MFMA B operands, never written back to memory (materialising
+// them would move four times the bytes).  The operands are exact or rounded
+// once within the tolerance: MXFP4 weights are bf16 values exactly; an affine
+// weight s·q + b has up to 12 significant bits plus the bias, which bf16 (8
+// bits) rounds by up to 2^-8 of its value -- more than the 2e-3 of Σ|x·w| the
+// result may be off -- so the dense kernel runs affine weights as fp16 (11
+// bits, 2^-11) against activations converted to fp16 exactly by a pre-pass,
+// with a power of two per row and per column that keeps both in fp16's
+// normal range, and the grouped kernel feeds the exact codes 128 + q and
+// applies each group's scale and bias in fp32.  Activation tiles are shared by
+// the four waves of a workgroup through LDS.
 //
 // k order inside a K step.  An MFMA sums over its k positions in any order,
 // so the k index a lane supplies only has to agree between its A and B
@@ -123,6 +129,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return uint32_t(uintptr_t((lds_ptr_t)p));
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// Two affine weights as fp16, each rounded once: lanes of `p` hold two codes as
+// fp16 subnormals (q·2^-24 or q·2^-20, see affine_word_to_bf16x8_mix), and
+// v_fma_mix{lo,hi}_f16 form fp16(sv·(fp16) + b) with the fma in fp32, so
+// sv = s·2^(24 + f) (or 2^(20 + f)) and b = bias·2^f give fp16(2^f·(s·q + bias)).
+__device__ __forceinline__ uint32_t mix_f16x2(float sv, uint32_t p, float b) {
+  uint32_t r;
+  asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(sv), "v"(p), "v"(b));
+  asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(sv), "v"(p), "v"(b));
+  return r;
+}
+
 // bf16 pair r (codes 2r, 2r + 1) of an MXFP4 word; r folds to a constant
 // once the caller's loops are unrolled.
 __device__ __forceinline__ uint32_t mxfp4_pair(uint32_t v, float sc, int r) {
@@ -151,6 +170,95 @@ constexpr int gemm_lds_bytes() {
   return kXSlots * WM * 128 + kWSlots * kWSlotBytes;
 }
 
+// Operand exponents of the affine fp16 MFMA path, one launch before the tile
+// kernel.  Workgroups [0, t): row t of x scaled by 2^e_t, the power of two
+// that puts its largest magnitude in [2^13, 2^14), converted to fp16 (xh) and
+// e_t stored (row_e).  A bf16 value has 8 significant bits, so it converts
+// exactly while its scaled magnitude is at least 2^-17 (fp16 subnormals step
+// by 2^-24): every element within 2^-30 of its row's largest; smaller ones
+// round to the fp16 grid.  The row is read twice, the second time from cache.
+// Workgroups [t, t + ceil(n/256)): 256 weight columns each, f_c such that the
+// column's largest |s·q + b| (at q = 0 or 15 in every group) lies in
+// [2^13, 2^14), stored to col_f.  The tile kernel forms fp16(2^f_c·w) and
+// multiplies each output by 2^-(e_t + f_c), exactly.
+__global__ __launch_bounds__(256) void xh_kernel(const uint16_t* __restrict__ x, int t, int d,
+                                                 uint16_t* __restrict__ xh, int* __restrict__ row_e,
+                                                 const uint8_t* __restrict__ meta, int n,
+                                                 int* __restrict__ col_f) {
+  if (int(blockIdx.x) >= t) {
+    const int c = (int(blockIdx.x) - t) * 256 + threadIdx.x;
+    if (c >= n) return;
+    const Slabs L{n, d, QMM_AFFINE4_G64};
+    float mw = 0.f;
+    // four slabs' metadata in flight at a time (index clamped into the slab's
+    // groups so every load is unconditional; groups a narrow or missing slab
+    // does not have count as zeros)
+    const uint8_t* mq = meta + int64_t(c >> 2) * L.meta_quad();
+    const int ns = L.count();
+    for (int s0 = 0; s0 < ns; s0 += 4) {
+      uint32_t v[4][kSlabCodes / 64];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sl = min(s0 + u, ns - 1);
+        const int ng = s0 + u < ns ? L.meta_row(sl) / 4 : 0;
+        const uint32_t* mp = reinterpret_cast<const uint32_t*>(mq + 4 * int64_t(sl) * L.meta_full() + (c & 3) * L.meta_row(sl));
+#pragma unroll
+        for (int gi = 0; gi < kSlabCodes / 64; ++gi) v[u][gi] = mp[min(gi, L.meta_row(sl) / 4 - 1)];
+#pragma unroll
+        for (int gi = 0; gi < kSlabCodes / 64; ++gi) v[u][gi] = gi < ng ? v[u][gi] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int gi = 0; gi < kSlabCodes / 64; ++gi) {
+          const float sv = bf16_lo(v[u][gi]), bv = bf16_hi(v[u][gi]);
+          mw = fmaxf(mw, fmaxf(fabsf(bv), fabsf(__builtin_fmaf(15.f, sv, bv))));
+        }
+    }
+    int f = 0;
+    if (mw > 0.f) {
+      int k;
+      frexpf(mw, &k);   // max in [2^(k-1), 2^k)
+      f = 14 - k;
+    }
+    col_f[c] = f;
+    return;
+  }
+  const int64_t row = blockIdx.x;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + row * d);
+  u32x4_t* dst = reinterpret_cast<u32x4_t*>(xh + row * d);
+  const int nc = d / 8;   // 16-byte pieces (d is a multiple of 64)
+  uint32_t m = 0;         // largest |x| as bf16 bits (order-preserving for |x|)
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    const u32x4_t v = src[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, uint32_t(__shfl_xor(int(m), o)));
+  __shared__ uint32_t wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  int e = 0;   // all-zero rows, and rows holding inf or NaN (whose outputs are not finite), stay unscaled
+  if (m != 0 && m < 0x7F80u) {
+    int k;
+    frexpf(__uint_as_float(m << 16), &k);   // max in [2^(k-1), 2^k)
+    e = 14 - k;
+  }
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    const u32x4_t v = src[c];
+    u32x4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 lo = _Float16(ldexpf(bf16_lo(v[i]), e)), hi = _Float16(ldexpf(bf16_hi(v[i]), e));
+      o[i] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+    }
+    dst[c] = o;
+  }
+  if (threadIdx.x == 0) row_e[row] = e;
+}
+
 // FAST (d a multiple of 512, so every slab is full, and the codes and the
 // metadata each below 2^31 bytes): the two weight descriptors span the whole
 // codes and metadata regions for the whole kernel, each lane keeps the
@@ -170,11 +278,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
                                                    uint16_t* __restrict__ y, int tiles_m,
                                                    int tiles_n, uint32_t codes_bytes,
                                                    uint32_t meta_bytes, int ks_per,
-                                                   float* __restrict__ ws) {
+                                                   float* __restrict__ ws,
+                                                   const int* __restrict__ row_e,
+                                                   const int* __restrict__ col_f) {
+  constexpr bool AFF = FMT == QMM_AFFINE4_G64;
   constexpr int RB = WM / 32;
   constexpr int XSLOT = WM * 128;
   constexpr int WBASE = kXSlots * XSLOT;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[gemm_lds_bytes<WM>()];
+  __shared__ int s_colf[AFF ? 256 : 1];   // affine: per-column exponent f
+  __shared__ __attribute__((aligned(16))) int s_rowe[AFF ? WM : 4];   // affine: per-row exponent e (row_e)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -197,6 +310,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   const int ks_base = SPLIT ? int(blockIdx.y) * ks_per : 0;   // this workgroup's first K step
   const int nk = SPLIT ? min(ks_per, nk_all - ks_base) : nk_all;   // its steps
   const uint32_t lds_base = lds_addr(lds);
+
+  // ---- affine: the fp16 operands' exponents, from the pre-pass (xh_kernel):
+  // column c's weights enter as fp16(2^f_c·w), row t's activations as
+  // 2^e_t·x; the epilogue multiplies by 2^-(e_t + f_c), exactly.  Read before
+  // the first LDS copy: these loads are waited for by the compiler, and none
+  // may be in flight once the copies' explicit counting starts.
+  if constexpr (AFF) {
+    s_colf[tid] = n0 + tid < n ? col_f[n0 + tid] : 0;
+    if (tid < WM) s_rowe[tid] = m0 + tid < t ? row_e[m0 + tid] : 0;
+  }
 
   // ---- activation copies: wave instruction i moves rows 8(w + 4i) .. +7 ----
   const auto xrs = make_rsrc(x + int64_t(m0) * d, uint32_t(rows_m) * uint32_t(d) * 2u);
@@ -294,26 +417,31 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][cb][r] = 0.f;
 
+  // affine: the exponent f of the lane's two columns (set after the prologue's barrier)
+  int cf[2] = {0, 0};
+
   // The 32 B-operand registers of a step, enumerated e = 8 j + 4 cb + r
-  // (word j of the chunk, column cb, bf16 pair r of the word).
+  // (word j of the chunk, column cb, fp16 (affine) or bf16 (MXFP4) pair r of
+  // the word).
   auto dequant_reg = [&](const WChunk& c, const AffineMix* am, const float* sc, int e) {
     const int j = e >> 3, cb = (e >> 2) & 1, r = e & 3;
     const uint32_t v = c.w[cb][j];
     if (FMT == QMM_AFFINE4_G64) {
       const uint32_t pr = (r >= 2 ? v >> 8 : v) & ((r & 1) ? 0x00F000F0u : 0x000F000Fu);
       const float sv = (r & 1) ? am[cb].s20 : am[cb].s24;
-      return pack_bf16x2(__builtin_fmaf(sv, f16_lo(pr), am[cb].b),
-                         __builtin_fmaf(sv, f16_hi(pr), am[cb].b));
+      return mix_f16x2(sv, pr, am[cb].b);
     }
     return mxfp4_pair(v, sc[cb], r);
   };
   auto consts = [&](const WChunk& c, AffineMix* am, float* sc) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      if (FMT == QMM_AFFINE4_G64)
-        am[cb] = affine_mix_consts(c.m[cb]);
-      else
+      if (FMT == QMM_AFFINE4_G64) {
+        const float sv = bf16_lo(c.m[cb]), bv = bf16_hi(c.m[cb]);
+        am[cb] = {ldexpf(sv, 24 + cf[cb]), ldexpf(sv, 20 + cf[cb]), ldexpf(bv, cf[cb])};
+      } else {
         sc[cb] = e8m0_scale(c.m[cb]);
+      }
     }
   };
 
@@ -344,10 +472,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
     for (int p = 0; p < NP; ++p) {
       const int i = p % RB, j = p / RB;
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
-        acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8_t, a[p]), __builtin_bit_cast(bf16x8_t, bcur[cb][j]),
-            acc[i][cb], 0, 0, 0);
+      for (int cb = 0; cb < 2; ++cb) {
+        if constexpr (AFF)
+          acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(f16x8_t, a[p]), __builtin_bit_cast(f16x8_t, bcur[cb][j]),
+              acc[i][cb], 0, 0, 0);
+        else
+          acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, a[p]), __builtin_bit_cast(bf16x8_t, bcur[cb][j]),
+              acc[i][cb], 0, 0, 0);
+      }
       if (p + kAhead < NP) {
         const int q = p + kAhead;
         a[q] = *reinterpret_cast<const u32x4_t*>(ab + aoff[q / RB] + 4096 * (q % RB));
@@ -385,7 +519,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   u32x4_t pa[kAhead], pb[kAhead];
   {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Q));
-    __syncthreads();   // X(0) copied by every wave
+    __syncthreads();   // X(0) copied by every wave (and the affine exponents stored)
+    if constexpr (AFF) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) cf[cb] = s_colf[64 * wave + 32 * cb + col_l];
+    }
 #pragma unroll
     for (int p = 0; p < kAhead; ++p)
       pa[p] = *reinterpret_cast<const u32x4_t*>(lds + aoff[p / RB] + 4096 * (p % RB));
@@ -416,7 +554,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
   // epilogue: lane holds column col_l of each 32x32 block, rows 8(r/4) + 4g + r%4
   float* plane = SPLIT ? ws + int64_t(blockIdx.y) * t * n : nullptr;
 #pragma unroll
-  for (int i = 0; i < RB; ++i)
+  for (int i = 0; i < RB; ++i) {
+    // affine: the exponents of the lane's 16 rows of this block, four
+    // consecutive rows per 16-byte read, all read before the first store
+    int4 re[4];
+    if constexpr (AFF) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) re[h] = *reinterpret_cast<const int4*>(&s_rowe[32 * i + 8 * h + 4 * g]);
+    }
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int cl = 64 * wave + 32 * cb + col_l;
@@ -426,12 +571,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
         const int rl = 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
         if (rl >= rows_m) continue;
         const int64_t at = int64_t(m0 + rl) * n + n0 + cl;
+        float v = acc[i][cb][r];
+        if constexpr (AFF) {
+          // undo the operands' power-of-two scaling (exact)
+          const int4 e4 = re[r >> 2];
+          const int e = (r & 3) == 0 ? e4.x : (r & 3) == 1 ? e4.y : (r & 3) == 2 ? e4.z : e4.w;
+          v = ldexpf(v, -(e + cf[cb]));
+        }
         if constexpr (SPLIT)
-          plane[at] = acc[i][cb][r];
+          plane[at] = v;
         else
-          y[at] = f32_to_bf16(acc[i][cb][r]);
+          y[at] = f32_to_bf16(v);
       }
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -449,14 +602,21 @@ constexpr int kGXs = 136;   // LDS row stride in bf16 for a 128-wide K step
 // accumulators to the gate waves through LDS (the activation buffers), which
 // apply the activation before the one bf16 rounding.  row_index NULL: row r
 // of the grouped order reads row r of x.
+// Affine weights keep per-group partial sums beside the accumulators: one
+// workgroup per CU, which leaves them the whole register file.
 template <int FMT, bool GLU>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
+__global__ __launch_bounds__(256, FMT == QMM_AFFINE4_G64 ? 1 : 2) void grouped_gemm_kernel(
     const uint8_t* __restrict__ base, int64_t expert_stride, int n_experts, int64_t codes_off,
     int64_t meta_off, int n, int d, const uint16_t* __restrict__ x, int64_t t_x,
     const int32_t* __restrict__ row_index, const int32_t* __restrict__ seg_expert,
     const int32_t* __restrict__ seg_offsets, int m_total, uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][kGBM * kGXs];
   __shared__ int32_t src_row[kGBM];
+  // affine: each staged row's activation sum per 64-code group of the K step,
+  // and a zero operand for the lanes outside the group an MFMA sums
+  __shared__ float xsum[2][kGBM][2];
+  __shared__ __attribute__((aligned(16))) uint32_t zero16[4];
+  if (FMT == QMM_AFFINE4_G64 && threadIdx.x < 4) zero16[threadIdx.x] = 0u;
   static_assert(sizeof(xs) >= 2 * 16 * 64 * sizeof(f32x4_t), "the up accumulators fit the activation buffers");
 
   const int tid = threadIdx.x;
@@ -526,8 +686,21 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
     };
     auto store_x = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4_t*>(&xs[buf][(16 * i + 4 * wave + (lane >> 4)) * kGXs + 8 * xc]) = xreg[i];
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * i + 4 * wave + (lane >> 4);
+        *reinterpret_cast<u32x4_t*>(&xs[buf][row * kGXs + 8 * xc]) = xreg[i];
+        if constexpr (FMT == QMM_AFFINE4_G64) {
+          // the row's sum over each group: 8 codes per lane in order, then the
+          // 8 lanes of the group (chunks 8h .. 8h + 7) in a fixed tree
+          float sum = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sum = (sum + bf16_lo(xreg[i][q])) + bf16_hi(xreg[i][q]);
+          sum += __shfl_xor(sum, 1);
+          sum += __shfl_xor(sum, 2);
+          sum += __shfl_xor(sum, 4);
+          if ((xc & 7) == 0) xsum[buf][row][xc >> 3] = sum;
+        }
+      }
     };
     auto load_w = [&](u32x4_t (&wr)[kGCB], int k0) {
       const int k = k0 + 32 * g;
@@ -575,9 +748,10 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
       const int buf = ks & 1;
       const int k0 = ks * 128;
       // this step's group metadata for each column block: dword q of the slab
-      // metadata (MXFP4, byte g) or dword 2q + g/2 (affine), from the lane that loaded it
+      // metadata (MXFP4, byte g) or dwords 2q and 2q + 1 (affine: both groups
+      // of the step), from the lane that loaded it
       const int q = ks & 3;
-      uint32_t mreg[kGCB];
+      uint32_t mreg[kGCB], mreg1[kGCB];
       {
         uint32_t v0, v1 = 0u;
         if constexpr (FMT == QMM_AFFINE4_G64) {
@@ -590,9 +764,8 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
         for (int cb = 0; cb < kGCB; ++cb) {
           const int src = 4 * (16 * cb + col_l);
           if (FMT == QMM_AFFINE4_G64) {
-            const uint32_t a = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(v0)));
-            const uint32_t b = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(v1)));
-            mreg[cb] = (g >> 1) ? b : a;
+            mreg[cb] = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(v0)));
+            mreg1[cb] = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(v1)));
           } else {
             mreg[cb] = (uint32_t(__builtin_amdgcn_ds_bpermute(src, int(v0))) >> (8 * g)) & 0xFFu;
           }
@@ -608,6 +781,61 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(
       // No masking: past d the activations are zero and the weights finite
       // (affine scale and bias and E8M0 < 255 are checked at pack time), so
       // those products are exact zeros; columns past n are never stored.
+      if constexpr (FMT == QMM_AFFINE4_G64) {
+        // Affine: the codes enter the MFMAs as the exact bf16 values 128 + q
+        // and scale and bias follow per group in fp32,
+        //   Σ_k x·(s·q + b) = s·Σ_k x·(128 + q) + (b − 128·s)·Σ_k x,
+        // so no weight is rounded.  Lane group g's chunk lies in group g / 2
+        // of the step; the MFMAs of group h take the zero operand on the
+        // other lanes, so each sums one group only.
+        u32x4_t bq[4][kGCB];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int cb = 0; cb < kGCB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bq[j][cb][r] = and_or(wreg[p][cb][j] >> (4 * r), 0x000F000Fu, kMagic128x2);
+        float gsc[kGCB][2], gcb[kGCB][2];   // scale and b − 128·s of the step's two groups
+#pragma unroll
+        for (int cb = 0; cb < kGCB; ++cb) {
+          gsc[cb][0] = bf16_lo(mreg[cb]);
+          gcb[cb][0] = __builtin_fmaf(-128.0f, bf16_lo(mreg[cb]), bf16_hi(mreg[cb]));
+          gsc[cb][1] = bf16_lo(mreg1[cb]);
+          gcb[cb][1] = __builtin_fmaf(-128.0f, bf16_lo(mreg1[cb]), bf16_hi(mreg1[cb]));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i < nrb) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              f32x4_t pg[kGCB];
+#pragma unroll
+              for (int cb = 0; cb < kGCB; ++cb) pg[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const u32x4_t* ap = (g >> 1) == h
+                                        ? reinterpret_cast<const u32x4_t*>(&xs[buf][(16 * i + col_l) * kGXs + 32 * g + 8 * j])
+                                        : reinterpret_cast<const u32x4_t*>(zero16);
+                const u32x4_t a = *ap;
+#pragma unroll
+                for (int cb = 0; cb < kGCB; ++cb)
+                  pg[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, bq[j][cb]), pg[cb], 0, 0, 0);
+              }
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float xg = xsum[buf][16 * i + 4 * g + r][h];
+#pragma unroll
+                for (int cb = 0; cb < kGCB; ++cb)
+                  acc[i][cb][r] = __builtin_fmaf(gcb[cb][h], xg, __builtin_fmaf(gsc[cb][h], pg[cb][r], acc[i][cb][r]));
+              }
+            }
+          }
+        }
+        if (ks + 1 < nk) store_x(buf ^ 1);
+        return;
+      }
       u32x4_t bfrag[kGCB][4];
 #pragma unroll
       for (int cb = 0; cb < kGCB; ++cb) dequant_chunk<FMT>(wreg[p][cb], mreg[cb], bfrag[cb]);
@@ -695,6 +923,7 @@ int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream) 
   Layout l;
   if (!layout_of(a.f, a.n, a.d, &l)) return int(hipErrorInvalidValue);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool aff = a.f == QMM_AFFINE4_G64;
   const uint8_t* codes = a.packed + l.codes_offset;
   const uint8_t* meta = a.packed + l.meta_offset;
   const int tiles_n = (a.n + 255) / 256;
@@ -707,32 +936,62 @@ int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream) 
   DevInfo di{};
   const int64_t cus = device_info(&di) == 0 && di.cus > 0 ? di.cus : 256;
   const int nk = (a.d + 63) / 64;
+  // affine: the fp16 activations and row exponents live in the workspace,
+  // the K-split planes (if any) after them
+  const TileWs tw = tile_ws_layout(a.f, a.t, a.n, a.d, l);
+  if (aff && (!ws || int64_t(ws_bytes) < tw.planes)) return int(hipErrorInvalidValue);
+  uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+  const uint16_t* xk = aff ? reinterpret_cast<const uint16_t*>(wsb + tw.xh) : a.x;
+  int* row_e = aff ? reinterpret_cast<int*>(wsb + tw.rowe) : nullptr;
+  int* col_f = aff ? reinterpret_cast<int*>(wsb + tw.colf) : nullptr;
+  float* planes = ws ? reinterpret_cast<float*>(wsb + tw.planes) : nullptr;
+  const size_t planes_bytes = ws ? ws_bytes - size_t(tw.planes) : 0;
+  ProfileEvents pe = take_profile_events();   // start with the first kernel, stop with the last
+  if (aff) {
+    const dim3 pgrid(unsigned(a.t + (a.n + 255) / 256));
+    uint16_t* xh = reinterpret_cast<uint16_t*>(wsb + tw.xh);
+    if (pe.start)
+      hipExtLaunchKernelGGL(xh_kernel, pgrid, dim3(256), 0, s, static_cast<hipEvent_t>(pe.start), nullptr, 0,
+                            a.x, a.t, a.d, xh, row_e, meta, a.n, col_f);
+    else
+      hipLaunchKernelGGL(xh_kernel, pgrid, dim3(256), 0, s, a.x, a.t, a.d, xh, row_e, meta, a.n, col_f);
+    pe.start = nullptr;
+  }
   auto go = [&](auto kernel, auto split_kernel, int wm) {
     const int tiles_m = (a.t + wm - 1) / wm;
     const int tiles = tiles_m * tiles_n;
     // split along K while the tiles cannot fill the chip (few rows): as many
     // splits as fit the CUs, at most kTileSplits, each at least 8 steps
     int splits = 1;
-    if (fast && ws && a.t > kSkinnyMaxT) {
+    if (fast && planes && a.t > kSkinnyMaxT) {
       splits = int(std::min<int64_t>({int64_t(kTileSplits), cus / tiles, int64_t(nk / 8)}));
-      if (splits < 2 || size_t(splits) * size_t(a.t) * size_t(a.n) * 4 > ws_bytes) splits = 1;
+      if (splits < 2 || size_t(splits) * size_t(a.t) * size_t(a.n) * 4 > planes_bytes) splits = 1;
     }
     if (splits == 1) {
-      launch_kernel(kernel, dim3(unsigned(tiles)), dim3(256), s, codes, meta, a.t, a.n, a.d,
-                    a.x, a.y, tiles_m, tiles_n, cb, mb, nk, static_cast<float*>(nullptr));
+      if (pe.start || pe.stop)
+        hipExtLaunchKernelGGL(kernel, dim3(unsigned(tiles)), dim3(256), 0, s,
+                              static_cast<hipEvent_t>(pe.start), static_cast<hipEvent_t>(pe.stop), 0,
+                              codes, meta, a.t, a.n, a.d, xk, a.y, tiles_m, tiles_n, cb, mb, nk,
+                              static_cast<float*>(nullptr), static_cast<const int*>(row_e),
+                              static_cast<const int*>(col_f));
+      else
+        hipLaunchKernelGGL(kernel, dim3(unsigned(tiles)), dim3(256), 0, s, codes, meta, a.t, a.n, a.d,
+                           xk, a.y, tiles_m, tiles_n, cb, mb, nk, static_cast<float*>(nullptr),
+                           static_cast<const int*>(row_e), static_cast<const int*>(col_f));
       return;
     }
     const int ks_per = (nk + splits - 1) / splits;
     splits = (nk + ks_per - 1) / ks_per;
-    const ProfileEvents pe = take_profile_events();   // start with the tiles, stop with the sum
     if (pe.start)
       hipExtLaunchKernelGGL(split_kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(256), 0, s,
                             static_cast<hipEvent_t>(pe.start), nullptr, 0, codes, meta, a.t, a.n, a.d,
-                            a.x, a.y, tiles_m, tiles_n, cb, mb, ks_per, ws);
+                            xk, a.y, tiles_m, tiles_n, cb, mb, ks_per, planes,
+                            static_cast<const int*>(row_e), static_cast<const int*>(col_f));
     else
       hipLaunchKernelGGL(split_kernel, dim3(unsigned(tiles), unsigned(splits)), dim3(256), 0, s, codes, meta,
-                         a.t, a.n, a.d, a.x, a.y, tiles_m, tiles_n, cb, mb, ks_per, ws);
-    launch_partials_sum(ws, int64_t(a.t) * a.n, splits, a.y, pe.stop, s);
+                         a.t, a.n, a.d, xk, a.y, tiles_m, tiles_n, cb, mb, ks_per, planes,
+                         static_cast<const int*>(row_e), static_cast<const int*>(col_f));
+    launch_partials_sum(planes, int64_t(a.t) * a.n, splits, a.y, pe.stop, s);
   };
   // Tile height by a cost model of whole rounds of tiles over the CUs: a round
   // of 256-row tiles (one per CU) takes ~12 units, a round of 128-row tiles
@@ -745,7 +1004,6 @@ int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream) 
   const int64_t r128 = (int64_t((a.t + 127) / 128) * tiles_n + cus - 1) / cus;
   const int64_t r256 = (int64_t((a.t + 255) / 256) * tiles_n + cus - 1) / cus;
   const bool small = a.t <= 128 || 7 * r128 < 12 * r256;
-  const bool aff = a.f == QMM_AFFINE4_G64;
   // the split kernel exists for whole-region addressing only; otherwise the
   // unsplit one is passed twice (go never splits without FAST)
   if (!small) {

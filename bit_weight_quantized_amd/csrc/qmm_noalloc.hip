@@ -1,6 +1,8 @@
-// A fixed scratch area for qmm_gemm_noalloc: the fp32 partial sums of the
-// GEMM split along K live in a file-scope device array instead of a caller
-// workspace, for callers that cannot allocate device memory.
+// A fixed scratch area for qmm_gemm_noalloc: what qmm_gemm keeps in its
+// workspace (the fp32 partial sums of the GEMM split along K; for affine
+// weights through the tile kernel the fp16 activations and the operand
+// exponents) lives in a file-scope device array instead, for callers that
+// cannot allocate device memory.
 //
 // The array is part of this library's code object, so every GPU the library
 // runs on holds its own copy, at its own address, until the process ends.  In
@@ -9,9 +11,10 @@
 // current) and only that address is ever handed to kernels.
 //
 // Every call on a GPU shares that GPU's array and finds the previous call's
-// contents in it.  The split-K kernels write every partial sum they later
-// read (each workgroup stores its whole [t][256-column] block of its plane),
-// so nothing has to start at zero.  Calls that overlap on one GPU (different
+// contents in it.  Every kernel writes what it later reads (each split-K
+// workgroup stores its whole [t][256-column] block of its plane, the
+// activation pre-pass every converted row and exponent), so nothing has to
+// start at zero.  Calls that overlap on one GPU (different
 // streams, or threads that do not order their calls) race on the array.
 #include <hip/hip_runtime.h>
 

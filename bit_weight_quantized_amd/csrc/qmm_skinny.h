@@ -32,7 +32,7 @@ int launch_skinny(const GemmArgs& a, float* ws, void* stream);
 // would cover at most half of a 256-CU chip: up to kTileSplits fp32 [t][n]
 // planes (whole-region weight addressing only: d a multiple of 512).
 constexpr int kTileSplits = 4;
-inline size_t tile_split_workspace_bytes(int64_t t, int64_t n, int64_t d, const Layout& l) {
+inline size_t tile_split_planes_bytes(int64_t t, int64_t n, int64_t d, const Layout& l) {
   const bool whole = d % kSlabCodes == 0 && n * (d / 2) + (int64_t(1) << 16) < (int64_t(1) << 31) &&
                      l.meta_bytes + (int64_t(1) << 20) < (int64_t(1) << 31);
   const int64_t tiles128 = ((t + 127) / 128) * ((n + 255) / 256);
@@ -42,8 +42,29 @@ inline size_t tile_split_workspace_bytes(int64_t t, int64_t n, int64_t d, const 
   return size_t(kTileSplits) * size_t(t) * size_t(n) * 4;
 }
 
-// The tile GEMM, split along K through `ws` when it helps and ws_bytes allows
-// (ws NULL: launch_gemm).
+// Workspace of the tile kernel.  Affine weights: the activations converted
+// to fp16 (row t scaled by 2^e_t, t·d·2 bytes at `xh`), the int32 exponents
+// e_t (at `rowe`) and f_c of the weight columns (at `colf`), then the K-split
+// planes if the split applies (at `planes`).  MXFP4: the planes only.
+// Offsets 256-byte aligned.
+struct TileWs {
+  int64_t xh, rowe, colf, planes, total;
+};
+inline TileWs tile_ws_layout(int f, int64_t t, int64_t n, int64_t d, const Layout& l) {
+  const int64_t planes = int64_t(tile_split_planes_bytes(t, n, d, l));
+  TileWs w{0, 0, 0, 0, planes};
+  if (f == QMM_AFFINE4_G64) {
+    w.rowe = round_up(t * d * 2, 256);
+    w.colf = w.rowe + round_up(t * 4, 256);
+    w.planes = w.colf + round_up(n * 4, 256);
+    w.total = w.planes + planes;
+  }
+  return w;
+}
+
+// The tile GEMM, split along K through the workspace when it helps and
+// ws_bytes allows; affine weights need the workspace (tile_ws_layout), MXFP4
+// weights take ws NULL (launch_gemm).
 int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream);
 
 // The static scratch of qmm_gemm_noalloc (qmm_noalloc.hip): its size, and

@@ -34,14 +34,17 @@ constexpr uint32_t kOOB = 0x80000000u;   // OR-ed into a buffer offset: past eve
 // chunk c stored at position c ^ (r & 15), so the 16 rows of one MFMA operand
 // read (same chunk) fall in 16 different bank groups
 __device__ __forceinline__ int xs_at(int r, int c) { return r * kSlabCodes + ((c ^ (r & 15)) << 3); }
-// After the activation slab (one 16-row block; affine weights): a block of
-// zeros that half the lanes read instead of activations, then the 16 rows'
-// activation sums per 64-code group (fp32).
+// After the activation slab (affine weights): a block of zeros that half the
+// lanes read instead of activations, then the rows' activation sums per
+// 64-code group (fp32, up to 64 rows × 8 groups).
 constexpr int kZeroElems = 512;
-constexpr int kSkExtraBytes = kZeroElems * 2 + 16 * 8 * 4;
+constexpr int kSkExtraBytes = kZeroElems * 2 + 64 * 8 * 4;
 
+// Affine weights with four row blocks hold the most registers (the exact path
+// keeps per-group partial sums beside the accumulators): one workgroup per CU,
+// which leaves them the whole register file.
 template <int FMT, int NRB>
-__global__ __launch_bounds__(256, 2) void skinny_kernel(const uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(256, FMT == QMM_AFFINE4_G64 && NRB == 4 ? 1 : 2) void skinny_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ meta,
                                                         uint32_t codes_bytes, uint32_t meta_bytes,
                                                         int t, int n, int d,
@@ -116,37 +119,39 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(const uint8_t* __restric
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (FMT == QMM_AFFINE4_G64 && NRB == 1) {
-    // 3'. Affine, one row block: the codes enter the MFMAs as the exact bf16
-    //     values 128 + q (one v_and_or per pair instead of a dequantisation
-    //     per weight), one group per MFMA, and scale and bias are applied per
-    //     group afterwards:  Σ_k x·(s·q + b) = s·Σ_k x·(128 + q) + (b − 128·s)·Σ_k x.
-    //     A 128-code step holds two groups, lane group g's chunk lying in
-    //     group g / 2; the MFMAs of group h read activations on the lanes of
-    //     that half and zeros on the others, so each sums one group only.
-    uint16_t* zero = xs + 16 * kSlabCodes;
+  if constexpr (FMT == QMM_AFFINE4_G64) {
+    // 3'. Affine: the codes enter the MFMAs as the exact bf16 values 128 + q
+    //     (one v_and_or per pair instead of a dequantisation per weight), one
+    //     group per MFMA, and scale and bias are applied per group afterwards
+    //     in fp32:  Σ_k x·(s·q + b) = s·Σ_k x·(128 + q) + (b − 128·s)·Σ_k x.
+    //     No weight is rounded.  A 128-code step holds two groups, lane group
+    //     g's chunk lying in group g / 2; the MFMAs of group h read activations
+    //     on the lanes of that half and zeros on the others, so each sums one
+    //     group only.
+    uint16_t* zero = xs + NRB * 16 * kSlabCodes;
     float* xsum = reinterpret_cast<float*>(zero + kZeroElems);
     if (tid < kZeroElems / 8) *reinterpret_cast<u32x4_t*>(zero + 8 * tid) = u32x4_t{0u, 0u, 0u, 0u};
-    if (tid < 128) {   // row tid / 8, group tid % 8: its 64 activations summed in order
-      const int r = tid >> 3, gr = tid & 7;
-      float sum = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&xs[xs_at(r, 8 * gr + c)]);
+    for (int p0 = 0; p0 < NRB * 128; p0 += 256) {   // (row, group) p: its 64 activations summed in order
+      const int p = p0 + tid;
+      if (p < NRB * 128) {
+        const int r = p >> 3, gr = p & 7;
+        float sum = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sum = (sum + bf16_lo(v[q])) + bf16_hi(v[q]);
+        for (int c = 0; c < 8; ++c) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&xs[xs_at(r, 8 * gr + c)]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sum = (sum + bf16_lo(v[q])) + bf16_hi(v[q]);
+        }
+        xsum[r * 8 + gr] = sum;
       }
-      xsum[r * 8 + gr] = sum;
     }
     __syncthreads();
     const int gh = g >> 1;
-    int aoff[4][2];   // element offset of word j's activations for group h (step 0)
+    const int zoff = NRB * 16 * kSlabCodes;   // the zero block, as an element offset
+    int own[4];   // element offset of word j's activations in row block 0 (step 0)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int own = col_l * kSlabCodes + (((4 * g + j) ^ col_l) << 3);
-      aoff[j][0] = gh == 0 ? own : 16 * kSlabCodes;
-      aoff[j][1] = gh == 1 ? own : 16 * kSlabCodes;
-    }
+    for (int j = 0; j < 4; ++j) own[j] = col_l * kSlabCodes + (((4 * g + j) ^ col_l) << 3);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (128 * s >= w) break;   // a narrow last slab ends early (uniform)
@@ -161,76 +166,104 @@ __global__ __launch_bounds__(256, 2) void skinny_kernel(const uint8_t* __restric
           gc[cb][h] = __builtin_fmaf(-128.0f, bf16_lo(m), bf16_hi(m));
         }
       }
-      f32x4_t pg[4][2];
+      if constexpr (NRB == 1) {
+        // one row block: word j's (128 + q) pairs feed both groups' MFMAs
+        f32x4_t pg[4][2];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) pg[cb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          for (int h = 0; h < 2; ++h) pg[cb][h] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4_t b[4];
+        for (int j = 0; j < 4; ++j) {
+          u32x4_t b[4];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const uint32_t v = wr[cb][s][j];
+          for (int cb = 0; cb < 4; ++cb) {
+            const uint32_t v = wr[cb][s][j];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) b[cb][r] = and_or(v >> (4 * r), 0x000F000Fu, kMagic128x2);   // (128 + q) pairs
+            for (int r = 0; r < 4; ++r) b[cb][r] = and_or(v >> (4 * r), 0x000F000Fu, kMagic128x2);
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xs[(gh == h ? own[j] : zoff) + 128 * s]);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+              pg[cb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[cb]), pg[cb][h], 0, 0, 0);
+          }
         }
+        // the lane's rows 4g + r: acc += s·P + (b − 128·s)·Σx, group 2s then 2s + 1
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xs[aoff[j][h] + 128 * s]);
+        for (int r = 0; r < 4; ++r) {
+          const float2 xg = *reinterpret_cast<const float2*>(&xsum[(4 * g + r) * 8 + 2 * s]);
 #pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-            pg[cb][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[cb]), pg[cb][h], 0, 0, 0);
+          for (int cb = 0; cb < 4; ++cb) {
+            float v = acc[0][cb][r];
+            v = __builtin_fmaf(gs[cb][0], pg[cb][0][r], v);
+            v = __builtin_fmaf(gc[cb][0], xg.x, v);
+            v = __builtin_fmaf(gs[cb][1], pg[cb][1][r], v);
+            v = __builtin_fmaf(gc[cb][1], xg.y, v);
+            acc[0][cb][r] = v;
+          }
         }
-      }
-      // the lane's rows 4g + r: acc += s·P + (b − 128·s)·Σx, group 2s then 2s + 1
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float2 xg = *reinterpret_cast<const float2*>(&xsum[(4 * g + r) * 8 + 2 * s]);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          float v = acc[0][cb][r];
-          v = __builtin_fmaf(gs[cb][0], pg[cb][0][r], v);
-          v = __builtin_fmaf(gc[cb][0], xg.x, v);
-          v = __builtin_fmaf(gs[cb][1], pg[cb][1][r], v);
-          v = __builtin_fmaf(gc[cb][1], xg.y, v);
-          acc[0][cb][r] = v;
+      } else {
+        // several row blocks: every word's (128 + q) pairs once per step, then
+        // one group of one row block at a time
+        u32x4_t b[4][4];   // (128 + q) pairs of word j, column block cb
+  #pragma unroll
+        for (int j = 0; j < 4; ++j)
+  #pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const uint32_t v = wr[cb][s][j];
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) b[j][cb][r] = and_or(v >> (4 * r), 0x000F000Fu, kMagic128x2);
+          }
+  #pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+  #pragma unroll
+          for (int h = 0; h < 2; ++h) {   // group 2s + h
+            f32x4_t pg[4];
+  #pragma unroll
+            for (int cb = 0; cb < 4; ++cb) pg[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int off = (gh == h ? own[j] + rb * 16 * kSlabCodes : zoff) + 128 * s;
+              const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xs[off]);
+  #pragma unroll
+              for (int cb = 0; cb < 4; ++cb)
+                pg[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b[j][cb]), pg[cb], 0, 0, 0);
+            }
+            // the lane's rows 16rb + 4g + r: acc += s·P + (b − 128·s)·Σx
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float xg = xsum[(16 * rb + 4 * g + r) * 8 + 2 * s + h];
+  #pragma unroll
+              for (int cb = 0; cb < 4; ++cb)
+                acc[rb][cb][r] = __builtin_fmaf(gc[cb][h], xg, __builtin_fmaf(gs[cb][h], pg[cb][r], acc[rb][cb][r]));
+            }
+          }
         }
       }
     }
   } else {
-  // 3. per step: the metadata each lane's chunk needs (from the lane that
-  //    loaded that column), then per word j the four column blocks'
-  //    dequantised words and the MFMAs of every row block
+  // 3. MXFP4 (exact in bf16): per step the exponent each lane's chunk needs
+  //    (from the lane that loaded that column), then per word j the four
+  //    column blocks' weights and the MFMAs of every row block
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     if (128 * s >= w) break;   // a narrow last slab ends early (uniform)
-    AffineMix am[4];
     float sc[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
+      // group (128s + 32g) / 32 = 4s + g: byte g of dword s
       const int src = 4 * (16 * cb + col_l);
-      if constexpr (FMT == QMM_AFFINE4_G64) {
-        // group (128s + 32g) / 64 = 2s + g/2 of the column
-        const uint32_t m0 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mv[2 * s])));
-        const uint32_t m1 = uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mv[2 * s + 1])));
-        am[cb] = affine_mix_consts((g >> 1) ? m1 : m0);
-      } else {
-        // group (128s + 32g) / 32 = 4s + g: byte g of dword s
-        sc[cb] = e8m0_scale((uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mv[s]))) >> (8 * g)) & 0xFFu);
-      }
+      sc[cb] = e8m0_scale((uint32_t(__builtin_amdgcn_ds_bpermute(src, int(mv[s]))) >> (8 * g)) & 0xFFu);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       u32x4_t bf[4];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        if constexpr (FMT == QMM_AFFINE4_G64)
-          bf[cb] = affine_word_to_bf16x8_mix(wr[cb][s][j], am[cb]);
-        else
-          bf[cb] = mxfp4_word_to_bf16x8(wr[cb][s][j], sc[cb]);
-      }
+      for (int cb = 0; cb < 4; ++cb) bf[cb] = mxfp4_word_to_bf16x8(wr[cb][s][j], sc[cb]);
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xs[xs_at(16 * rb + col_l, 16 * s + 4 * g + j)]);

@@ -86,19 +86,25 @@ typedef uint16_t qmm_bf16; /* raw bf16 bits */
  * format is invalid.  Host only; touches no device. */
 size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
 
-/* Workspace that lets qmm_gemm(f, t, n, d) take its fastest path (bytes, 0 =
- * none helps; 0 also for an invalid shape).  Every caller buffer has its size
- * stated per format and shape by a call like this one, as the explicit
- * per-format byte counts that fixed the NULL-scale crash of "Colibri Kimi K3
- * Metal 后端实现全解析", Phase 10 (fmt_scale_bytes).  For 2 <= t <= 64 rows: one fp32
- * [t][n] plane per 512-code slab of d, ceil(d/512)·t·n·4 bytes (2.2 MB for
- * t = 4, n = 13824, d = 5120).  For larger t while the tile kernel has few
- * tiles (128-row tiles over at most 128 workgroups) and d is a multiple of 512:
- * 4·t·n·4 bytes, up to four K-split planes.  A workspace is always optional: every call
- * accepts ws = NULL (qmm_gemm then runs its tile kernel, several times slower
- * for such t); a non-NULL ws must be 16-byte aligned and hold at least this many
- * bytes (QMM_E_ALIGN, QMM_E_WORKSPACE).  Its contents on entry do not matter,
- * and calls sharing one workspace must be ordered on one stream.  Host only. */
+/* Workspace of qmm_gemm(f, t, n, d) in bytes (0 = none used; 0 also for
+ * t = 1 and for an invalid shape).  Every caller buffer has its size stated
+ * per format and shape by a call like this one, as the explicit per-format
+ * byte counts that fixed the NULL-scale crash of "Colibri Kimi K3 Metal
+ * 后端实现全解析", Phase 10 (fmt_scale_bytes).
+ *   2 <= t <= 64 rows: one fp32 [t][n] plane per 512-code slab of d,
+ *     ceil(d/512)·t·n·4 bytes (2.2 MB for t = 4, n = 13824, d = 5120).
+ *   t > 64, affine weights: the activations converted to fp16 (t·d·2 bytes),
+ *     one int32 exponent per row and per weight column, each rounded up to
+ *     256 bytes (21.0 MB for t = 2048, n = 13824, d = 5120), plus, while the
+ *     tile kernel has few tiles (128-row tiles over at most 128 workgroups)
+ *     and d is a multiple of 512, up to four K-split planes of t·n·4 bytes.
+ *   t > 64, MXFP4 weights: those K-split planes, else 0.
+ * Affine weights with t >= 2 REQUIRE this workspace (QMM_E_WORKSPACE without
+ * one).  For MXFP4 it is optional: ws = NULL runs the tile kernel, several
+ * times slower for 2 <= t <= 64.  A non-NULL ws must be 16-byte aligned and
+ * hold at least this many bytes (QMM_E_ALIGN, QMM_E_WORKSPACE).  Its contents
+ * on entry do not matter, and calls sharing one workspace must be ordered on
+ * one stream.  Host only. */
 size_t qmm_workspace_bytes(qmm_format f, int64_t t, int64_t n, int64_t d);
 
 /* Pack canonical weights into the MI355X device layout.  The codes are the
@@ -157,19 +163,27 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
 /* Prefill GEMM: Y[t][n] = Σ_k X[t][k]·ŵ[n,k], the multi-row product of
  * "Kapitsa 源码拆解 02：权重、矩阵与 Metal", section "矩阵乘法中数据和参数" (many
  * activation rows share each weight read, unlike the one-row decode).
- *   x bf16[t][d] row-major; y bf16[t][n] row-major (written whole).
- * t = 1 runs the GEMV kernel; t > 1 dequantizes weight tiles to bf16 and
- * feeds bf16 MFMA with fp32 accumulation (the weight is rounded to bf16 once,
- * as the MFMA operand).  For 2 <= t <= 64 with a workspace of
- * qmm_workspace_bytes(f, t, n, d) bytes the product is split along d: each
- * 512-code slab's fp32 partial sums go to the workspace and a second kernel
- * adds them in slab order, then rounds to bf16 (a batch of decode rows streams
- * the weights once across the whole chip); without one, the tile kernel.  For
- * t > 64 with few tiles and a workspace, the tile kernel itself is split along
- * d into up to four fp32 planes summed in order.  On
- * that path, affine weights with t <= 16 enter the MFMA as 128 + q (exact) and
- * scale and bias are applied per group in fp32, so the weights are not rounded
- * to bf16 there. */
+ *   x bf16[t][d] row-major; y bf16[t][n] row-major (written whole);
+ *   ws, ws_bytes: the workspace of qmm_workspace_bytes(f, t, n, d), required
+ *   for affine weights with t >= 2 (see there), optional for MXFP4.
+ * t = 1 runs the GEMV kernel.  Otherwise MFMA with fp32 accumulation, every
+ * output rounded once to bf16:
+ *   2 <= t <= 64 (with the workspace): split along d, each 512-code slab's
+ *     fp32 partial sums in the workspace, added in slab order by a second
+ *     kernel.  Affine codes enter bf16 MFMAs as the exact values 128 + q and
+ *     each group's scale and bias follow in fp32, so no weight is rounded.
+ *   t > 64, affine: a first kernel converts x to fp16 in the workspace, each
+ *     row scaled by a power of two (exact for every element within 2^-30 of
+ *     its row's largest), and finds a power of two per weight column; the
+ *     tile kernel forms each weight fp16(2^f·(s·q + b)), rounded once
+ *     (relative error <= 2^-11 wherever the scaled weight is a normal fp16:
+ *     every weight within 2^-27 of its column's largest), runs fp16 MFMAs
+ *     and removes both powers of two exactly.  With few tiles the tile kernel
+ *     is split along d into up to four fp32 planes summed in order.
+ *   MXFP4: the weights are bf16 MFMA operands, exact for E8M0 in [2, 252]
+ *     (at 253 and 254 the largest codes reach 2^128: not representable).
+ * Profiling events armed by qmm_profile_next bracket every kernel of the
+ * call. */
 qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
                     const qmm_bf16* x, qmm_bf16* y, void* ws, size_t ws_bytes, void* stream);
 
@@ -177,15 +191,16 @@ qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int6
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Same arguments, kernels and results as qmm_gemm
  * given a workspace of qmm_workspace_bytes(f, t, n, d) bytes: bitwise the same
- * outputs.  The split-K partial sums go to a static 64 MiB device array inside
- * the library instead (one per GPU, allocated with the library's code object
- * and held until the process ends; its address is looked up on the first call
- * on each device).  Limit: qmm_workspace_bytes(f, t, n, d) <= 64 MiB
+ * outputs.  What that workspace holds (split-K partial sums; for affine
+ * weights with t > 64 the fp16 activations and the exponents) goes to a
+ * static 64 MiB device array inside the library instead (one per GPU,
+ * allocated with the library's code object and held until the process ends;
+ * its address is looked up on the first call on each device).  Limit: qmm_workspace_bytes(f, t, n, d) <= 64 MiB
  * (67108864 bytes), else QMM_E_WORKSPACE and nothing launched.  The call
  * allocates and frees nothing.  Every call on one GPU shares that GPU's array:
  * calls that overlap on one GPU (other streams, unordered threads) race on
  * it and must be serialised by the caller.  Nothing in the array needs to
- * start at zero (each partial sum read is written first in the same call). */
+ * start at zero (everything read from it is written first in the same call). */
 qmm_status qmm_gemm_noalloc(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
                             const qmm_bf16* x, qmm_bf16* y, void* stream);
 

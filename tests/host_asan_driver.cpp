@@ -113,6 +113,14 @@ int main() {
   EXPECT(qmm_gemm(A, P(), (int64_t(1) << 24) + 1, 16, 64, B(), B(), nullptr, 0, nullptr) == QMM_E_SHAPE);
   EXPECT(qmm_gemm(M, P(), 2048, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_OK && g_called == "gemm_ws");
   EXPECT(g_ws == nullptr && g_ws_bytes == 0);
+  // affine weights through the tile kernel need the workspace (fp16 activations)
+  const size_t need2k = qmm_workspace_bytes(A, 2048, 13824, 5120);
+  EXPECT(need2k == size_t(2048) * 5120 * 2 + 2048 * 4 + 13824 * 4);
+  EXPECT(qmm_gemm(A, P(), 2048, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_E_WORKSPACE);
+  EXPECT(qmm_gemm(A, P(), 2048, 13824, 5120, B(), B(), P(), need2k, nullptr) == QMM_OK && g_called == "gemm_ws");
+  EXPECT(g_ws == P() && g_ws_bytes == need2k);
+  EXPECT(qmm_gemm(A, P(), 3, 16, 64, B(), B(), P(), qmm_workspace_bytes(A, 3, 16, 64), nullptr) == QMM_OK &&
+         g_called == "skinny");
 
   // the allocation-free GEMM: the static scratch replaces the workspace; too
   // large a shape is refused before the scratch is looked up

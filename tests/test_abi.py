@@ -56,7 +56,7 @@ def test_packed_bytes_rejects_bad_shapes():
     for f, n, d in [(A, 8, 96), (M, 8, 48), (A, 0, 64), (A, 8, 0), (3, 8, 64), (A, -1, 64),
                     (A, 8, 65536 + 64), (A, (1 << 28) + 1, 64)]:
         assert qmm.qmm_packed_bytes(f, n, d) == 0
-    assert qmm.qmm_workspace_bytes(A, 2048, 13824, 5120) == 0
+    assert qmm.qmm_workspace_bytes(A, 1, 13824, 5120) == 0
 
 
 def test_workspace_contract():
@@ -65,12 +65,19 @@ def test_workspace_contract():
     assert qmm.qmm_workspace_bytes(A, 2, 13824, 5120) == 10 * 2 * 13824 * 4
     assert qmm.qmm_workspace_bytes(M, 64, 300, 1088) == 3 * 64 * 300 * 4
     for t in (1, 2048, 300):
-        assert qmm.qmm_workspace_bytes(A, t, 13824, 5120) == 0
+        assert qmm.qmm_workspace_bytes(M, t, 13824, 5120) == 0
+    # affine weights through the tile kernel (t > 64): the activations as fp16,
+    # one int32 exponent per row and per weight column, each region rounded up
+    # to 256 bytes
+    up = lambda v: -(-v // 256) * 256
+    assert qmm.qmm_workspace_bytes(A, 2048, 13824, 5120) == 2048 * 5120 * 2 + 2048 * 4 + 13824 * 4
+    assert qmm.qmm_workspace_bytes(A, 300, 13824, 5120) == 300 * 5120 * 2 + up(300 * 4) + 13824 * 4
     # the tile kernel split along K (up to 4 planes) while 128-row tiles would
     # cover at most half of a 256-CU chip; d a multiple of 512 only
-    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5120) == 4 * 65 * 13824 * 4
+    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5120) == up(65 * 5120 * 2) + up(65 * 4) + 13824 * 4 + 4 * 65 * 13824 * 4
     assert qmm.qmm_workspace_bytes(M, 256, 13824, 5120) == 4 * 256 * 13824 * 4
-    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5056) == 0
+    assert qmm.qmm_workspace_bytes(M, 65, 13824, 5056) == 0
+    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5056) == up(65 * 5056 * 2) + up(65 * 4) + 13824 * 4
     assert qmm.qmm_workspace_bytes(A, 4, 8, 96) == 0
     # optional, but one that is passed must be large enough and 16-byte aligned
     # (host validation: nothing is launched)
@@ -81,6 +88,9 @@ def test_workspace_contract():
     assert "workspace" in qmm.qmm_last_error()
     assert lib.qmm_gemm(A, P, 4, 16, 64, P, P, P + 8, need, None) == E_ALIGN
     assert lib.qmm_gemv(A, P, 16, 64, P + 1, P, P, 1, None) == E_ALIGN   # gemv ignores ws, checks x
+    # affine weights with t >= 2 cannot do without it
+    assert lib.qmm_gemm(A, P, 2048, 16, 64, P, P, None, 0, None) == E_WS
+    assert "affine" in qmm.qmm_last_error()
 
 
 def test_noalloc_limit_is_checked_on_the_host():

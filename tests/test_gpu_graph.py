@@ -59,6 +59,11 @@ def test_graph_replay_matches_eager():
     qmm.qmm_pack(A, nd, dd, dev(wd.codes), dev(wd.scale), dev(wd.bias), pd)
     pg = torch.empty(qmm.qmm_packed_bytes(A, ng, dg), dtype=torch.uint8, device=DEV)
     qmm.qmm_pack(A, ng, dg, dev(wg.codes), dev(wg.scale), dev(wg.bias), pg)
+    # the unsplit tile kernel (d not a multiple of 512) after its activation pre-pass
+    du = 576
+    wu = synth.affine_weights(905, ng, du)
+    pu = torch.empty(qmm.qmm_packed_bytes(A, ng, du), dtype=torch.uint8, device=DEV)
+    qmm.qmm_pack(A, ng, du, dev(wu.codes), dev(wu.scale), dev(wu.bias), pu)
     gsz, dsz = qmm.qmm_packed_bytes(M, 2 * ni, dm), qmm.qmm_packed_bytes(M, dm, ni)
     gu = torch.empty(gsz * ne, dtype=torch.uint8, device=DEV)
     dn = torch.empty(dsz * ne, dtype=torch.uint8, device=DEV)
@@ -73,6 +78,8 @@ def test_graph_replay_matches_eager():
     # the captured buffers: inputs, then outputs (with the sentinel each is reset to)
     xd = torch.empty(dd, dtype=torch.int16, device=DEV)
     xg = torch.empty(tg, dg, dtype=torch.int16, device=DEV)
+    xu = torch.empty(tg, du, dtype=torch.int16, device=DEV)
+    wsu = torch.empty(qmm.qmm_workspace_bytes(A, tg, ng, du) // 4, dtype=torch.float32, device=DEV)
     xm = torch.empty(t, dm, dtype=torch.int16, device=DEV)
     # the GEMM split along K (two kernels each, fp32 partials in a workspace):
     # 4 rows through the few-row kernel, 70 rows through the split tile kernel
@@ -98,6 +105,7 @@ def test_graph_replay_matches_eager():
     def inputs(seed):
         xd.copy_(dev(synth.activations(seed, synth.S_X, 1, dd)[0]))
         xg.copy_(dev(synth.activations(seed, synth.S_X, tg, dg, sub=1)))
+        xu.copy_(dev(synth.activations(seed, synth.S_X, tg, du, sub=3)))
         xm.copy_(dev(synth.activations(seed, synth.S_X, t, dm, sub=2)))
 
     def reset():
@@ -106,7 +114,7 @@ def test_graph_replay_matches_eager():
 
     def layer():
         qmm.qmm_gemv(A, pd, nd, dd, xd, O["gemv"])
-        qmm.qmm_gemm(A, pg, tg, ng, dg, xg, O["gemm"])
+        qmm.qmm_gemm(A, pu, tg, ng, du, xu, O["gemm"], wsu)
         qmm.qmm_gemm(A, pg, 4, ng, dg, xg, O["gemm_split4"], ws4)
         qmm.qmm_gemm(A, pg, tg, ng, dg, xg, O["gemm_split70"], ws70)
         qmm.qmm_route(xm, t, dm, r_d, ne, bias_d, k, O["scores"], O["topk"], O["seg_expert"],

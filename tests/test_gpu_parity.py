@@ -317,9 +317,14 @@ def test_gemv_integer_exact():
 # ---------------------------------------------------------------------------
 
 def run_gemm(fmt, packed, n, d, x_bits):
+    """qmm_gemm as a caller without a workspace of its own would call it:
+    MXFP4 weights with none; affine weights (t >= 2) with the workspace they
+    need (NaN-filled: its contents on entry must not matter)."""
     t = x_bits.shape[0]
+    need = qmm.qmm_workspace_bytes(fmt, t, n, d) if fmt == A else 0
+    ws = guarded((need // 4,), float("nan"), torch.float32) if need else None
     y = nan_out(t, n)
-    qmm.qmm_gemm(fmt, packed, t, n, d, dev(x_bits), y)
+    qmm.qmm_gemm(fmt, packed, t, n, d, dev(x_bits), y, ws)
     torch.cuda.synchronize()
     return host_u16(y)
 
@@ -373,10 +378,11 @@ def test_gemm_256_row_tiles(fmt, d):
 @pytest.mark.parametrize("seed", range(16))
 def test_gemm_random_shapes(seed):
     """Seeded random shapes across the GEMM's paths, two per (path, format):
-    the GEMV (t = 1), the split-K kernel (2 <= t <= 64 with a workspace), the
-    tile kernel for the same t without one, and t > 64 with a workspace (the
-    tile kernel, split along K when its tiles are few); d a multiple of 512 or
-    ending in a narrow slab (MXFP4 also in a half K step), n and t ragged."""
+    the GEMV (t = 1), the split-K kernel (2 <= t <= 64 with a workspace), for
+    the same t without one the MXFP4 tile kernel (affine weights always take
+    their workspace), and t > 64 with a workspace (the tile kernel, split along
+    K when its tiles are few); d a multiple of 512 or ending in a narrow slab
+    (MXFP4 also in a half K step), n and t ragged."""
     rng = np.random.default_rng(900 + seed)
     fmt = A if (seed // 4) % 2 == 0 else M
     kind = seed % 4
@@ -384,7 +390,7 @@ def test_gemm_random_shapes(seed):
     d = int(rng.integers(1, 41)) * g
     n = int(rng.integers(1, 700))
     t = [1, int(rng.integers(2, 65)), int(rng.integers(2, 65)), int(rng.integers(65, 400))][kind]
-    use_ws = kind in (1, 3)
+    use_ws = kind in (1, 3) or fmt == A
     say("gemm random", seed, "fmt", fmt, "t n d", t, n, d, "ws", use_ws)
     x = synth.activations(9000 + seed, synth.S_X, t, d)
     if fmt == A:
@@ -437,6 +443,70 @@ def test_mxfp4_e8m0_range_limits():
     say("gemm E8M0 253 row 0 (weights beyond bf16, not checked):", oracle.bf16_to_f64(yg[:, 0]).tolist(),
         "exact:", yr[:, 0].tolist())
     assert_parity(yg[:, 1:], yr[:, 1:], ar[:, 1:], "gemm E8M0 253, other rows")
+
+
+def halfway_affine(n, d):
+    """Affine weights that bf16 cannot hold: every group has scale 2^-8 and
+    bias 1, so w = 1 + q·2^-8 lies exactly halfway between two bf16 numbers
+    for odd q; round-to-nearest-even takes q ≡ 1 (mod 4) down and q ≡ 3
+    (mod 4) up by 2^-8.  Row r holds q_dn = 1 + 4·(r % 4) on the first 32
+    codes of each group and q_up = 3 + 4·(r // 4 % 4) on the last 32."""
+    g = d // 64
+    scale = np.full((n, g), 0x3B80, np.uint16)   # 2^-8
+    bias = np.full((n, g), 0x3F80, np.uint16)    # 1.0
+    q = np.empty((n, d), np.uint32)
+    r = np.arange(n)
+    q_dn, q_up = 1 + 4 * (r % 4), 3 + 4 * (r // 4 % 4)
+    first = (np.arange(d) % 64) < 32
+    q[:, first] = q_dn[:, None]
+    q[:, ~first] = q_up[:, None]
+    codes = np.zeros((n, d // 8), np.uint32)
+    for j in range(8):
+        codes |= q[:, j::8] << np.uint32(4 * j)
+    return synth.Affine(codes, scale, bias), q_dn, q_up
+
+
+def halfway_x(t, d):
+    """x = +1 on each group's first 32 codes and -1 on its last 32, row t
+    scaled by 2^(t % 5 - 2): every bf16 rounding of those weights would move
+    the sum the same way."""
+    sign = np.where((np.arange(d) % 64) < 32, 1.0, -1.0)
+    return synth.bf16_bits(sign[None, :] * (2.0 ** (np.arange(t) % 5 - 2))[:, None])
+
+
+@pytest.mark.parametrize("t,n,d", [(1, 300, 1024), (8, 300, 1024), (20, 300, 1024), (40, 300, 1024),
+                                   (100, 600, 1024), (130, 300, 576), (300, 520, 5120), (2048, 4352, 512)])
+def test_affine_weights_not_rounded(t, n, d):
+    """Weights exactly halfway between two bf16 numbers, activations signed so
+    that rounding them would add up: bf16 operands land at 1.94x the
+    tolerance.  Every affine matmul path (GEMV, few-row kernel with one, two
+    and four row blocks, tile kernel split and unsplit) must stay within it."""
+    say("affine halfway weights", t, n, d)
+    w, q_dn, q_up = halfway_affine(n, d)
+    x = halfway_x(t, d)
+    yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    # the oracle, hand-worked: 32 codes of q_dn minus 32 of q_up per group
+    want = (2.0 ** (np.arange(t) % 5 - 2))[:, None] * (d // 64) * 32 * (q_dn - q_up)[None, :] * 2.0 ** -8
+    assert np.array_equal(yr, want)
+    p = pack_affine(w)
+    y = run_gemv(A, p, w, x[0])[None, :] if t == 1 else run_gemm(A, p, n, d, x)
+    assert_parity(y, yr, ar, f"affine halfway {t}x{n}x{d}")
+
+
+def test_grouped_affine_weights_not_rounded():
+    """The same halfway weights through the routed-expert grouped kernels
+    (matmul path, and the SwiGLU variant's gate and up halves)."""
+    n, d = 256, 1024
+    w, _, _ = halfway_affine(n, d)
+    stk, size = stack(A, [w, w])
+    x = halfway_x(45, d)
+    seg_expert, seg_offsets = [1, 0], [0, 5, 45]
+    rows = np.arange(45)
+    yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    y = run_grouped(A, stk, size, 2, n, d, x, seg_expert, seg_offsets, rows, 40)
+    assert_parity(y, yr, ar, "grouped affine halfway")
+    h = run_grouped_swiglu(A, stk, size, 2, n, d, x, seg_expert, seg_offsets, rows, 40)
+    assert_swiglu(h, yr, ar, n // 2, "grouped swiglu affine halfway")
 
 
 def test_gemm_integer_exact():

@@ -72,10 +72,11 @@ def both(fmt, p, t, n, d, x):
     return y0.cpu().numpy().view(np.uint16), y1.cpu().numpy().view(np.uint16)
 
 
-# (format, n, d, first t, second t): few-row split-K (2 <= t <= 64) and the
-# tile kernel split along K (t > 64 with few tiles, d a multiple of 512)
+# (format, n, d, first t, second t): few-row split-K (2 <= t <= 64), the tile
+# kernel split along K (t > 64 with few tiles, d a multiple of 512), and the
+# affine tile kernel unsplit (its fp16 activations in the scratch)
 CASES = [(A, 13824, 5120, 40, 8), (M, 1000, 3584, 64, 3), (A, 1000, 2048, 200, 70),
-         (M, 700, 3072, 97, 66)]
+         (M, 700, 3072, 97, 66), (A, 4352, 1024, 2048, 300)]
 
 
 @pytest.mark.parametrize("fmt,n,d,t1,t2", CASES)
