@@ -25,6 +25,13 @@ ceiling at that size (`stream_ceiling`), and when the prefill row runs, a
 dense bf16 GEMM of its shape through the vendor library (torch.matmul, no
 dequantisation) is timed beside it (`prefill_gemm.bf16_library_gemm`).
 
+After the GPU measurements an oracle phase checks the outputs of the last
+timed step of every workload against the CPU oracle (max |err|/tol, on a
+stated sample for the large ones: `accuracy`) and times the oracle on the
+same samples on this host, extrapolated to one whole workload
+(`cpu_baseline`, with the CPU model, its logical CPUs and the BLAS threads
+the oracle used; the decode GEMV also on one thread).
+
 Each kernel launch gets HIP start/stop events stamped by its own dispatch
 (qmm_profile_next -> hipExtLaunchKernel, on the stream it runs on); their
 average interval, the kernel's execution time, gives achieved GB/s (bytes the algorithm must move: packed
@@ -158,6 +165,7 @@ def main(argv=None) -> int:
         print("[bench]", *a, file=sys.stderr, flush=True)
 
     work = {}     # row -> list of (launch fn(step), name, bytes, flops)
+    ctx = {}      # workload -> host inputs and GPU outputs for the oracle phase
     t_setup = time.time()
 
     # ---- decode: affine GEMV 13824 x 5120 -------------------------------------------------
@@ -185,6 +193,20 @@ def main(argv=None) -> int:
         b8 = n1 * d1 * 36 // 64 + 2 * 8 * d1 + 2 * 8 * n1
         work["decode"].append((lambda s: qmm.qmm_gemm(A, copies[(s + 6) % len(copies)], 8, n1, d1, x8, y8, ws8),
                                "gemm_t8_split_k", b8, 2.0 * 8 * n1 * d1))
+        # the small GEMV workload (T=1, D=256, N=512): 73.7 KB of weights, held
+        # in cache after the first launch -- latency, not bandwidth, is its measure
+        c0 = synth.CONFIGS[0]
+        n0, d0 = c0["n"], c0["d"]
+        w0 = synth.affine_weights(synth.seed_of(0), n0, d0)
+        p0 = torch.empty(qmm.qmm_packed_bytes(A, n0, d0), dtype=torch.uint8, device=dev)
+        qmm.qmm_pack(A, n0, d0, T(w0.codes), T(w0.scale), T(w0.bias), p0)
+        x0h = synth.activations(synth.seed_of(0), synth.S_X, 1, d0)
+        x0, y0 = T(x0h), torch.empty(n0, dtype=torch.int16, device=dev)
+        b0 = n0 * d0 * 36 // 64 + 2 * d0 + 2 * n0
+        work["decode"].append((lambda s: qmm.qmm_gemv(A, p0, n0, d0, x0, y0), "gemv_cfg0_512x256", b0, 2.0 * n0 * d0))
+        ctx["cfg0"] = dict(name=c0["name"], w=w0, x=x0h, y=y0, bytes=b0, budget=1.0)
+        ctx["cfg1"] = dict(name=c1["name"], w=w1, x=synth.activations(synth.seed_of(1), synth.S_X, 1, d1), y=y1,
+                           bytes=b1, budget=3.0)
         log("decode ready", len(copies), "copies")
 
     # ---- fused projections: a Q/K/V triple sharing x as one GEMV, against three ----------
@@ -229,6 +251,8 @@ def main(argv=None) -> int:
         b2 = n2 * d2 * 36 // 64 + 2 * t2 * d2 + 2 * t2 * n2
         work["prefill"] = [(lambda s: qmm.qmm_gemm(A, p2s[s % 2], t2, n2, d2, x2, y2, ws2),
                             "gemm", b2, 2.0 * t2 * n2 * d2)]
+        ctx["cfg2"] = dict(name=c2["name"], w=w2, x=synth.activations(synth.seed_of(2), synth.S_X, t2, d2), y=y2,
+                           t=t2, flops=2.0 * t2 * n2 * d2)
         log("prefill ready")
 
     # ---- MoE: 896-expert MXFP4 stacks built on the device ----------------------------------
@@ -261,6 +285,10 @@ def main(argv=None) -> int:
         o3 = torch.empty(16, dn_n, dtype=torch.int16, device=dev)
         bg = 16 * (gsz - 256) + 2 * gu_d + 2 * 16 * gu_n
         bd = 16 * (dsz - 256) + 2 * 16 * dn_d + 2 * 16 * dn_n
+        ctx["cfg3"] = dict(name=synth.CONFIGS[3]["name"], experts=synth.draw_experts(seed3, 16, 896, args.steps - 1),
+                           x=synth.activations(seed3, synth.S_X, 1, gu_d), z=synth.activations(seed3, synth.S_Z, 16, dn_d),
+                           h=h3, o=o3, bytes=None,
+                           gate_up=lambda e: synth.expert_gate_up(seed3, e), down=lambda e: synth.expert_down(seed3, e))
         work["moe_dec"] = [
             (lambda s: qmm.qmm_grouped_gemm(M, gu, gsz, 896, gu_n, gu_d, x3, 1, zero_idx, draws[s],
                                             offs, 16, 16, 1, h3), "grouped_gemv_gate_up", bg,
@@ -269,6 +297,7 @@ def main(argv=None) -> int:
                                             offs, 16, 16, 1, o3), "grouped_gemv_down", bd,
              2.0 * 16 * dn_n * dn_d),
         ]
+        ctx["cfg3"]["bytes"] = bg + bd
     if "moe_pre" in rows:
         # routed on the GPU every step (qmm_route), its tables driving the grouped
         # matmul directly: segments dense over all 896 experts, empty ones included
@@ -293,6 +322,9 @@ def main(argv=None) -> int:
             (route, "route", br, 2.0 * t4 * ne * gu_d),
             (lambda s: qmm.qmm_grouped_gemm(M, gu, gsz, 896, gu_n, gu_d, x4, t4, ri, se, so, ne, t4 * k4,
                                             t4, y4), "grouped_gemm", b4, 2.0 * t4 * k4 * gu_n * gu_d)]
+        ctx["cfg4"] = dict(name=synth.CONFIGS[4]["name"], x=xb, y=y4, flops=2.0 * t4 * k4 * gu_n * gu_d,
+                           gate_up=lambda e: synth.expert_gate_up(synth.seed_of(3), e),
+                           seg_offsets=None, row_index=None, tables=(so, ri))
         log("moe_pre ready", moe_pre_info)
     if "moe_ffn" in rows:
         # the rest of the expert FFN on the same routed rows: gate_up with the
@@ -373,15 +405,15 @@ def main(argv=None) -> int:
         sink = torch.empty(2048, dtype=torch.int32, device=dev)
         for i in range(10):
             qmm.qmm_stream_read(sbufs[i % len(sbufs)], sbytes, sink)
-        sev = [(hev.new(), hev.new()) for _ in range(args.steps)]
+        sev = [(hev.new(), hev.new()) for _ in range(max(args.steps, 100))]
         torch.cuda.synchronize()
         for i, (a, b) in enumerate(sev):
             qmm.qmm_profile_next(a, b)
             qmm.qmm_stream_read(sbufs[i % len(sbufs)], sbytes, sink)
         torch.cuda.synchronize()
         sus = np.array([hev.ms(a, b) * 1e3 for a, b in sev])
-        stream_ceiling = {"kernel": "stream_read_kernel", "bytes": int(sbytes),
-                          "us_mean": round(float(sus.mean()), 3),
+        stream_ceiling = {"kernel": "stream_read_kernel", "bytes": int(sbytes), "launches": len(sev),
+                          "us_mean": round(float(sus.mean()), 3), "us_median": round(float(np.median(sus)), 3),
                           "GBps": round(sbytes / float(sus.mean()) / 1e3, 1),
                           "frac": round(sbytes / float(sus.mean()) / 1e3 / HBM_PEAK_GBPS, 4)}
         del sbufs
@@ -452,32 +484,174 @@ def main(argv=None) -> int:
     out["setup_s"] = round(t_setup, 1)
     out["wall_s_timed"] = round(wall, 3)
 
-    if not args.no_cpu_baseline and "decode" in rows:
-        out["cpu_baseline"] = cpu_baseline(w1, synth.activations(synth.seed_of(1), synth.S_X, 1, d1), b1)
+    out["gpu"].update(hip_runtime())
+    if not args.no_cpu_baseline and ctx:
+        # GPU outputs of the last timed step to the host, then the oracle
+        for c in ctx.values():
+            for k in ("y", "h", "o"):
+                if k in c and hasattr(c[k], "cpu"):
+                    c[k] = c[k].cpu().numpy().view(np.uint16)
+            if "tables" in c:
+                c["seg_offsets"], c["row_index"] = (t_.cpu().numpy() for t_ in c.pop("tables"))
+        log("oracle phase")
+        t_or = time.time()
+        acc, base, info = oracle_phase(ctx)
+        out["accuracy"] = acc
+        if "cfg1" in base:
+            b = base["cfg1"]
+            out["cpu_baseline"] = {"value": b["GBps"], "unit": "GB/s", "cores": info["blas_threads"], "kind": "oracle",
+                                   "sample": f"{b['sample']} of the decode workload {b['workload']} (fp64 dequantisation "
+                                             f"in numpy, one thread; fp64 matvec in the numpy BLAS, "
+                                             f"{info['blas_threads']} threads)",
+                                   "value_single_thread": b["GBps_single_thread"], **info, "configs": base}
+        else:
+            out["cpu_baseline"] = {"kind": "oracle", **info, "configs": base}
+        log("oracle phase", round(time.time() - t_or, 1), "s")
     print(json.dumps(out), flush=True)
     return 0
 
 
-def cpu_baseline(w, x_bits, nbytes, budget_s: float = 12.0):
-    """The oracle as it stands, on this host, on whole decode GEMVs of the
-    headline workload (repeated until `budget_s` of CPU work is spent)."""
-    import oracle
+def hip_runtime():
+    """The HIP runtime the kernels ran on: the libamdhip64 this process mapped
+    (libqmm binds to the copy torch loaded first) and the ROCm release of the
+    machine."""
+    lib = None
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    lib = line.split()[-1]
+                    break
+    except OSError:
+        pass
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    return {"hip_runtime_library": lib, "rocm_release": rocm}
+
+
+def host_info():
+    """The host the oracle runs on: CPU model, logical CPUs, and the BLAS
+    threads numpy's matmul uses (the oracle's only multithreaded step)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        blas_threads = 1
-    reps, t = 0, 0.0
-    while t < budget_s and reps < 50:
-        t0 = time.perf_counter()
-        oracle.gemm_affine(x_bits, w.codes, w.scale, w.bias)
-        t += time.perf_counter() - t0
-        reps += 1
-    per = t / reps
-    return {"value": round(nbytes / per / 1e9, 3), "unit": "GB/s", "cores": int(blas_threads),
-            "kind": "oracle", "seconds_per_gemv": round(per, 3),
-            "sample": f"{reps} full 13824x5120 affine GEMVs (fp64 dequant in numpy, single thread; "
-                      f"fp64 matvec in the numpy BLAS with {blas_threads} threads)"}
+        blas = 1
+    return {"cpu_model": model, "host_cpus": os.cpu_count(), "blas_threads": int(blas)}
+
+
+def timed(fn, *a):
+    t0 = time.perf_counter()
+    r = fn(*a)
+    return r, time.perf_counter() - t0
+
+
+def oracle_phase(ctx, single_thread=True):
+    """After the timed steps: the GPU outputs of every workload against the
+    oracle (max |err|/tol per workload, on the stated sample), and the oracle's
+    own time on the same sample, extrapolated to one whole workload -- the CPU
+    baseline.  Runs on the host, after every GPU measurement."""
+    import oracle
+    acc, base = {}, {}
+    info = host_info()
+
+    def rec(name, r, n, sample):
+        acc[name] = {"max_err_over_tol": round(r["max_ratio"], 4), "ok": bool(r["ok"]), "outputs_checked": int(n),
+                     "sample": sample}
+
+    def single(fn, *a):
+        if not single_thread:
+            return None
+        try:
+            from threadpoolctl import threadpool_limits
+        except Exception:
+            return None
+        with threadpool_limits(1):
+            return timed(fn, *a)[1]
+
+    # configs 0 and 1: whole GEMVs, all threads and one thread
+    for key in ("cfg0", "cfg1"):
+        if key not in ctx:
+            continue
+        c = ctx[key]
+        (yr, ar), dt = timed(oracle.gemm_affine, c["x"], c["w"].codes, c["w"].scale, c["w"].bias)
+        reps, tot = 1, dt
+        while tot < c.get("budget", 0.0) and reps < 50:
+            tot += timed(oracle.gemm_affine, c["x"], c["w"].codes, c["w"].scale, c["w"].bias)[1]
+            reps += 1
+        st = single(oracle.gemm_affine, c["x"], c["w"].codes, c["w"].scale, c["w"].bias)
+        rec(key, oracle.check(c["y"], yr[0], ar[0]), yr.size, "every output")
+        base[key] = {"workload": c["name"], "seconds": round(tot / reps, 4), "GBps": round(c["bytes"] / (tot / reps) / 1e9, 4),
+                     "seconds_single_thread": None if st is None else round(st, 4),
+                     "GBps_single_thread": None if st is None else round(c["bytes"] / st / 1e9, 4),
+                     "sample": f"{reps} whole GEMVs"}
+    # config 2: the weights dequantised once, then 64 of the 2048 rows
+    if "cfg2" in ctx:
+        c = ctx["cfg2"]
+        w_hat, t_deq = timed(oracle.dequant_affine, c["w"].codes, c["w"].scale, c["w"].bias)
+        rows = np.linspace(0, c["t"] - 1, 64).astype(int)
+        (yr, ar), t_mm = timed(oracle.matmul, c["x"][rows], w_hat)
+        rec("cfg2", oracle.check(c["y"][rows], yr, ar), yr.size, "64 of the 2048 rows (evenly spaced), every column")
+        full = t_deq + t_mm * c["t"] / len(rows)
+        base["cfg2"] = {"workload": c["name"], "seconds": round(full, 3), "GFLOPs": round(c["flops"] / full / 1e9, 3),
+                        "sample": "dequantisation of all weights + 64 of 2048 rows, extrapolated to 2048 rows"}
+    # config 3: two of the 16 routed experts, gate_up and down
+    if "cfg3" in ctx:
+        c = ctx["cfg3"]
+        worst, n_out, t_or = 0.0, 0, 0.0
+        ok = True
+        for i in (0, len(c["experts"]) - 1):
+            e = int(c["experts"][i])
+            t0 = time.perf_counter()
+            g = c["gate_up"](e)
+            yr, ar = oracle.gemm_mxfp4(c["x"], g.codes, g.e8m0)
+            dw = c["down"](e)
+            yr2, ar2 = oracle.gemm_mxfp4(c["z"][i:i + 1], dw.codes, dw.e8m0)
+            t_or += time.perf_counter() - t0
+            for r in (oracle.check(c["h"][i], yr[0], ar[0]), oracle.check(c["o"][i], yr2[0], ar2[0])):
+                worst, ok = max(worst, r["max_ratio"]), ok and r["ok"]
+            n_out += yr.size + yr2.size
+        acc["cfg3"] = {"max_err_over_tol": round(worst, 4), "ok": ok, "outputs_checked": n_out,
+                       "sample": "2 of the 16 routed experts (the last step's draw), gate_up and down, every output"}
+        full = t_or * len(c["experts"]) / 2
+        base["cfg3"] = {"workload": c["name"], "seconds": round(full, 3), "GBps": round(c["bytes"] / full / 1e9, 4),
+                        "sample": "2 of 16 experts (weights generated, dequantised, multiplied), extrapolated to 16"}
+    # config 4: six routed segments on the GPU router's own tables
+    if "cfg4" in ctx:
+        c = ctx["cfg4"]
+        sizes = np.diff(c["seg_offsets"])
+        active = np.nonzero(sizes)[0]
+        rng = np.random.default_rng(4)
+        pick = sorted({int(active[np.argmax(sizes[active])]), *rng.choice(active, 5, replace=False).tolist()})
+        worst, n_out, t_or, ok = 0.0, 0, 0.0, True
+        for e in pick:
+            r0, r1 = int(c["seg_offsets"][e]), int(c["seg_offsets"][e + 1])
+            t0 = time.perf_counter()
+            g = c["gate_up"](e)
+            yr, ar = oracle.gemm_mxfp4(c["x"][c["row_index"][r0:r1]], g.codes, g.e8m0)
+            t_or += time.perf_counter() - t0
+            r = oracle.check(c["y"][r0:r1], yr, ar)
+            worst, ok, n_out = max(worst, r["max_ratio"]), ok and r["ok"], n_out + yr.size
+        acc["cfg4"] = {"max_err_over_tol": round(worst, 4), "ok": ok, "outputs_checked": n_out,
+                       "sample": f"{len(pick)} of {len(active)} routed segments (the largest and 5 at random), "
+                                 "every row and column, on the GPU router's tables"}
+        full = t_or * len(active) / len(pick)
+        base["cfg4"] = {"workload": c["name"], "seconds": round(full, 3), "GFLOPs": round(c["flops"] / full / 1e9, 3),
+                        "sample": f"{len(pick)} of {len(active)} active experts, extrapolated by expert count"}
+    return acc, base, info
 
 
 if __name__ == "__main__":

@@ -319,8 +319,9 @@ qmm_status qmm_route(const qmm_bf16* x, int64_t t, int64_t d, const qmm_bf16* r,
 qmm_status qmm_profile_next(void* start_event, void* stop_event);
 
 /* Measurement support: the achievable HBM read rate.  Reads every byte of the
- * device buffer `src` once (16-byte non-temporal loads, 2048 workgroups of 256
- * threads, grid-stride) and stores one word per workgroup to `sink` (device,
+ * device buffer `src` once (16-byte non-temporal loads, four in flight per
+ * thread, 2048 workgroups of 256 threads, grid-stride) and stores one word per
+ * workgroup to `sink` (device,
  * >= 2048 uint32): the XOR of the words it read, so the XOR of all 2048
  * stored words equals the XOR of the buffer.  `src` 16-byte aligned, `bytes`
  * a multiple of 16, 0 < bytes < 2^31 (QMM_E_ALIGN / QMM_E_SHAPE otherwise).
