@@ -171,92 +171,124 @@ constexpr int gemm_lds_bytes() {
 }
 
 // Operand exponents of the affine fp16 MFMA path, one launch before the tile
-// kernel.  Workgroups [0, t): row t of x scaled by 2^e_t, the power of two
-// that puts its largest magnitude in [2^13, 2^14), converted to fp16 (xh) and
-// e_t stored (row_e).  A bf16 value has 8 significant bits, so it converts
-// exactly while its scaled magnitude is at least 2^-17 (fp16 subnormals step
-// by 2^-24): every element within 2^-30 of its row's largest; smaller ones
-// round to the fp16 grid.  The row is read twice, the second time from cache.
-// Workgroups [t, t + ceil(n/256)): 256 weight columns each, f_c such that the
-// column's largest |s·q + b| (at q = 0 or 15 in every group) lies in
-// [2^13, 2^14), stored to col_f.  The tile kernel forms fp16(2^f_c·w) and
-// multiplies each output by 2^-(e_t + f_c), exactly.
+// kernel.  Workgroups [0, ceil(n/64)): 64 weight columns each, f_c such that
+// the column's largest |s·q + b| (at q = 0 or 15 in every group) lies in
+// [2^13, 2^14), stored to col_f; lane l takes column 64·blockIdx + l and wave w
+// the slabs w, w + 4, ..., three slabs' metadata in flight, and the four
+// waves' maxima meet in LDS.  The following workgroups: one row of x per wave,
+// scaled by 2^e_t, the power of two that puts the row's largest magnitude in
+// [2^13, 2^14), converted to fp16 (xh) and e_t stored (row_e).  A bf16 value
+// has 8 significant bits, so it converts exactly while its scaled magnitude
+// is at least 2^-17 (fp16 subnormals step by 2^-24): every element within
+// 2^-30 of its row's largest; smaller ones round to the fp16 grid.  Rows of
+// up to kXhRegPieces·512 elements are loaded once, all at once, and kept in
+// registers; longer rows read their remainder a second time.  The tile kernel
+// forms fp16(2^f_c·w) and multiplies each output by 2^-(e_t + f_c), exactly.
+constexpr int kXhRegPieces = 16;   // 16-byte pieces per lane held in registers
+
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2_scaled(uint32_t v, int e) {
+  const _Float16 lo = _Float16(ldexpf(bf16_lo(v), e)), hi = _Float16(ldexpf(bf16_hi(v), e));
+  return uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+}
+
 __global__ __launch_bounds__(256) void xh_kernel(const uint16_t* __restrict__ x, int t, int d,
                                                  uint16_t* __restrict__ xh, int* __restrict__ row_e,
                                                  const uint8_t* __restrict__ meta, int n,
                                                  int* __restrict__ col_f) {
-  if (int(blockIdx.x) >= t) {
-    const int c = (int(blockIdx.x) - t) * 256 + threadIdx.x;
-    if (c >= n) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ncb = (n + 63) / 64;
+  if (int(blockIdx.x) < ncb) {
+    const int c = int(blockIdx.x) * 64 + lane;
+    const int cc = min(c, n - 1);   // lanes past n read a real column, store nothing
     const Slabs L{n, d, QMM_AFFINE4_G64};
     float mw = 0.f;
-    // four slabs' metadata in flight at a time (index clamped into the slab's
-    // groups so every load is unconditional; groups a narrow or missing slab
-    // does not have count as zeros)
-    const uint8_t* mq = meta + int64_t(c >> 2) * L.meta_quad();
+    // slab index clamped so every load is unconditional; slabs past the
+    // wave's share, and groups a narrow slab does not have, count as zeros
+    const uint8_t* mq = meta + int64_t(cc >> 2) * L.meta_quad();
     const int ns = L.count();
-    for (int s0 = 0; s0 < ns; s0 += 4) {
-      uint32_t v[4][kSlabCodes / 64];
+    for (int s0 = wave; s0 < ns; s0 += 12) {
+      uint32_t v[3][kSlabCodes / 64];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int sl = min(s0 + u, ns - 1);
-        const int ng = s0 + u < ns ? L.meta_row(sl) / 4 : 0;
-        const uint32_t* mp = reinterpret_cast<const uint32_t*>(mq + 4 * int64_t(sl) * L.meta_full() + (c & 3) * L.meta_row(sl));
+      for (int u = 0; u < 3; ++u) {
+        const int su = s0 + 4 * u;
+        const int sl = min(su, ns - 1);
+        const int ng = su < ns ? L.meta_row(sl) / 4 : 0;
+        const uint32_t* mp = reinterpret_cast<const uint32_t*>(mq + 4 * int64_t(sl) * L.meta_full() + (cc & 3) * L.meta_row(sl));
 #pragma unroll
         for (int gi = 0; gi < kSlabCodes / 64; ++gi) v[u][gi] = mp[min(gi, L.meta_row(sl) / 4 - 1)];
 #pragma unroll
         for (int gi = 0; gi < kSlabCodes / 64; ++gi) v[u][gi] = gi < ng ? v[u][gi] : 0u;
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 3; ++u)
 #pragma unroll
         for (int gi = 0; gi < kSlabCodes / 64; ++gi) {
           const float sv = bf16_lo(v[u][gi]), bv = bf16_hi(v[u][gi]);
           mw = fmaxf(mw, fmaxf(fabsf(bv), fabsf(__builtin_fmaf(15.f, sv, bv))));
         }
     }
-    int f = 0;
-    if (mw > 0.f) {
-      int k;
-      frexpf(mw, &k);   // max in [2^(k-1), 2^k)
-      f = 14 - k;
+    __shared__ float s_mw[4][64];
+    s_mw[wave][lane] = mw;
+    __syncthreads();
+    if (wave == 0 && c < n) {
+      mw = fmaxf(fmaxf(s_mw[0][lane], s_mw[1][lane]), fmaxf(s_mw[2][lane], s_mw[3][lane]));
+      int f = 0;
+      if (mw > 0.f) {
+        int k;
+        frexpf(mw, &k);   // max in [2^(k-1), 2^k)
+        f = 14 - k;
+      }
+      col_f[c] = f;
     }
-    col_f[c] = f;
     return;
   }
-  const int64_t row = blockIdx.x;
+  const int64_t row = int64_t(int(blockIdx.x) - ncb) * 4 + wave;
+  if (row >= t) return;   // whole waves; no barrier follows
   const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + row * d);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(xh + row * d);
   const int nc = d / 8;   // 16-byte pieces (d is a multiple of 64)
-  uint32_t m = 0;         // largest |x| as bf16 bits (order-preserving for |x|)
-  for (int c = threadIdx.x; c < nc; c += 256) {
-    const u32x4_t v = src[c];
+  u32x4_t v[kXhRegPieces];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) m = max(m, max(v[i] & 0x7FFFu, (v[i] >> 16) & 0x7FFFu));
+  for (int i = 0; i < kXhRegPieces; ++i) {
+    const int c = 64 * i + lane;
+    v[i] = c < nc ? src[c] : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  uint32_t m = 0;   // largest |x| as bf16 bits (order-preserving for |x|)
+#pragma unroll
+  for (int i = 0; i < kXhRegPieces; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(v[i][j] & 0x7FFFu, (v[i][j] >> 16) & 0x7FFFu));
+  for (int c = 64 * kXhRegPieces + lane; c < nc; c += 64) {
+    const u32x4_t w = src[c];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = max(m, uint32_t(__shfl_xor(int(m), o)));
-  __shared__ uint32_t wmax[4];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
   int e = 0;   // all-zero rows, and rows holding inf or NaN (whose outputs are not finite), stay unscaled
   if (m != 0 && m < 0x7F80u) {
     int k;
     frexpf(__uint_as_float(m << 16), &k);   // max in [2^(k-1), 2^k)
     e = 14 - k;
   }
-  for (int c = threadIdx.x; c < nc; c += 256) {
-    const u32x4_t v = src[c];
+#pragma unroll
+  for (int i = 0; i < kXhRegPieces; ++i) {
+    const int c = 64 * i + lane;
+    if (c < nc) {
+      u32x4_t o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = bf16x2_to_f16x2_scaled(v[i][j], e);
+      dst[c] = o;
+    }
+  }
+  for (int c = 64 * kXhRegPieces + lane; c < nc; c += 64) {
+    const u32x4_t w = src[c];
     u32x4_t o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const _Float16 lo = _Float16(ldexpf(bf16_lo(v[i]), e)), hi = _Float16(ldexpf(bf16_hi(v[i]), e));
-      o[i] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
-    }
+    for (int j = 0; j < 4; ++j) o[j] = bf16x2_to_f16x2_scaled(w[j], e);
     dst[c] = o;
   }
-  if (threadIdx.x == 0) row_e[row] = e;
+  if (lane == 0) row_e[row] = e;
 }
 
 // FAST (d a multiple of 512, so every slab is full, and the codes and the
@@ -948,7 +980,7 @@ int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream) 
   const size_t planes_bytes = ws ? ws_bytes - size_t(tw.planes) : 0;
   ProfileEvents pe = take_profile_events();   // start with the first kernel, stop with the last
   if (aff) {
-    const dim3 pgrid(unsigned(a.t + (a.n + 255) / 256));
+    const dim3 pgrid(unsigned((a.n + 63) / 64 + (a.t + 3) / 4));
     uint16_t* xh = reinterpret_cast<uint16_t*>(wsb + tw.xh);
     if (pe.start)
       hipExtLaunchKernelGGL(xh_kernel, pgrid, dim3(256), 0, s, static_cast<hipEvent_t>(pe.start), nullptr, 0,
