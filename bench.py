@@ -481,6 +481,10 @@ def main(argv=None) -> int:
         out["rows"]["grouped_gemm"].update(moe_pre_info)
     out["gpu"] = {"name": props.name, "cus": props.multi_processor_count,
                   "hip": torch.version.hip, "torch": torch.__version__}
+    # a kernel forced through QMM_FORCE_KERNEL (A/B runs) is named in the line
+    ks = qmm.qmm_get_kernel()
+    out["kernel_setting"] = {0: "auto", 1: "tile", 2: "tile_unsplit", 3: "few_row",
+                             4: "grouped_matmul"}.get(ks, f"invalid ({ks})")
     out["setup_s"] = round(t_setup, 1)
     out["wall_s_timed"] = round(wall, 3)
 

@@ -17,11 +17,19 @@ __all__ = [
     "qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
     "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
     "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route",
-    "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "qmm_gemv_int8", "qmm_gemm_noalloc", "EXPORTS",
+    "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "qmm_gemv_int8", "qmm_gemm_noalloc", "qmm_set_kernel", "qmm_get_kernel",
+    "QMM_KERNEL_AUTO", "QMM_KERNEL_TILE", "QMM_KERNEL_TILE_UNSPLIT", "QMM_KERNEL_FEW_ROW",
+    "QMM_KERNEL_GROUPED_MATMUL", "EXPORTS",
 ]
 
 QMM_AFFINE4_G64 = 1
 QMM_MXFP4_G32 = 2
+
+QMM_KERNEL_AUTO = 0
+QMM_KERNEL_TILE = 1
+QMM_KERNEL_TILE_UNSPLIT = 2
+QMM_KERNEL_FEW_ROW = 3
+QMM_KERNEL_GROUPED_MATMUL = 4
 
 STATUS = {0: "QMM_OK", 1: "QMM_E_ARG", 2: "QMM_E_SHAPE", 3: "QMM_E_ALIGN", 4: "QMM_E_UNSUPPORTED",
           5: "QMM_E_WORKSPACE", 6: "QMM_E_HIP", 7: "QMM_E_LAYOUT", 8: "QMM_E_VALUE"}
@@ -29,7 +37,8 @@ STATUS = {0: "QMM_OK", 1: "QMM_E_ARG", 2: "QMM_E_SHAPE", 3: "QMM_E_ALIGN", 4: "Q
 EXPORTS = ("qmm_packed_bytes", "qmm_workspace_bytes", "qmm_pack", "qmm_unpack", "qmm_gemv",
            "qmm_gemm", "qmm_grouped_gemm", "qmm_status_string", "qmm_last_error",
            "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route",
-           "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "qmm_gemv_int8", "qmm_gemm_noalloc")
+           "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "qmm_gemv_int8", "qmm_gemm_noalloc",
+           "qmm_set_kernel", "qmm_get_kernel")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -83,6 +92,8 @@ def load():
         "qmm_moe_combine": (ctypes.c_int, [vp, i32, i64, i64, i32, vp, vp, i32, vp, vp, vp, vp]),
         "qmm_gemv_int8": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, vp, vp, vp]),
         "qmm_gemm_noalloc": (ctypes.c_int, [ctypes.c_int, vp, i64, i64, i64, vp, vp, vp]),
+        "qmm_set_kernel": (ctypes.c_int, [ctypes.c_int]),
+        "qmm_get_kernel": (ctypes.c_int, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -185,6 +196,16 @@ def qmm_gemm(fmt, packed, t, n, d, x, y, ws=None, stream=None):
 def qmm_gemm_noalloc(fmt, packed, t, n, d, x, y, stream=None):
     _check(load().qmm_gemm_noalloc(fmt, _ptr(packed), t, n, d, _ptr(x), _ptr(y), _stream(stream)),
            "qmm_gemm_noalloc")
+
+
+def qmm_set_kernel(kernel):
+    """Force one matmul kernel process-wide (QMM_KERNEL_*), or AUTO."""
+    _check(load().qmm_set_kernel(kernel), "qmm_set_kernel")
+
+
+def qmm_get_kernel():
+    """The current kernel setting; -1 if QMM_FORCE_KERNEL holds an unknown value."""
+    return load().qmm_get_kernel()
 
 
 def qmm_grouped_gemm(fmt, packed_stack, expert_stride_bytes, n_experts, n, d, x, t_x, row_index,

@@ -3,7 +3,11 @@
 #include <hip/hip_runtime.h>
 
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "qmm_deferred.h"
 #include "qmm_internal.h"
@@ -48,6 +52,52 @@ qmm_status check_ws(size_t need, const void* ws, size_t ws_bytes) {
   return QMM_OK;
 }
 
+// Kernel override (qmm_set_kernel / QMM_FORCE_KERNEL): process-wide.
+constexpr int kKernelUnset = -2, kKernelInvalid = -1;
+std::atomic<int> g_kernel{kKernelUnset};
+
+int parse_kernel(const char* v) {
+  if (!v || !*v || !strcmp(v, "auto") || !strcmp(v, "0")) return QMM_KERNEL_AUTO;
+  if (!strcmp(v, "tile") || !strcmp(v, "1")) return QMM_KERNEL_TILE;
+  if (!strcmp(v, "tile_unsplit") || !strcmp(v, "2")) return QMM_KERNEL_TILE_UNSPLIT;
+  if (!strcmp(v, "few_row") || !strcmp(v, "3")) return QMM_KERNEL_FEW_ROW;
+  if (!strcmp(v, "grouped_matmul") || !strcmp(v, "4")) return QMM_KERNEL_GROUPED_MATMUL;
+  return kKernelInvalid;
+}
+
+// The environment is read once, at the first use; qmm_set_kernel wins over it.
+int forced_kernel() {
+  static std::once_flag once;
+  std::call_once(once, [] {
+    int unset = kKernelUnset;
+    g_kernel.compare_exchange_strong(unset, parse_kernel(getenv("QMM_FORCE_KERNEL")));
+  });
+  return g_kernel.load(std::memory_order_relaxed);
+}
+
+qmm_status check_kernel(int* k) {
+  *k = forced_kernel();
+  if (*k == kKernelInvalid)
+    return fail(QMM_E_ARG, "QMM_FORCE_KERNEL is not one of auto, tile, tile_unsplit, few_row, grouped_matmul (or 0..4)");
+  return QMM_OK;
+}
+
+bool forces_tile(int k) { return k == QMM_KERNEL_TILE || k == QMM_KERNEL_TILE_UNSPLIT; }
+
+// Workspace of qmm_gemm under kernel setting k (0 where the call runs no
+// kernel that takes one, or where it fails).
+size_t gemm_ws_bytes(int k, int f, int64_t t, int64_t n, int64_t d, const qmm::Layout& l) {
+  if (t < 1 || t > qmm::kMaxT) return 0;
+  if (forces_tile(k)) {
+    const qmm::TileWs tw = qmm::tile_ws_layout(f, t, n, d, l);
+    return size_t(k == QMM_KERNEL_TILE_UNSPLIT ? tw.planes : tw.total);
+  }
+  if (t < 2) return 0;
+  if (k == QMM_KERNEL_FEW_ROW) return qmm::skinny_fits(t, n, d, l) ? qmm::skinny_workspace_bytes(t, n, d) : 0;
+  return qmm::skinny_fits(t, n, d, l) ? qmm::skinny_workspace_bytes(t, n, d)
+                                      : size_t(qmm::tile_ws_layout(f, t, n, d, l).total);
+}
+
 }  // namespace
 
 qmm::ProfileEvents qmm::take_profile_events() {
@@ -72,10 +122,19 @@ size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d) {
 size_t qmm_workspace_bytes(qmm_format f, int64_t t, int64_t n, int64_t d) {
   qmm::Layout l;
   if (!valid_format(f) || n < 1 || d < 1 || !qmm::layout_of(f, n, d, &l)) return 0;
-  if (t < 2 || t > qmm::kMaxT) return 0;
-  return qmm::skinny_fits(t, n, d, l) ? qmm::skinny_workspace_bytes(t, n, d)
-                                      : size_t(qmm::tile_ws_layout(f, t, n, d, l).total);
+  const int k = forced_kernel();
+  return k == kKernelInvalid ? 0 : gemm_ws_bytes(k, f, t, n, d, l);
 }
+
+qmm_status qmm_set_kernel(qmm_kernel k) {
+  g_last_error[0] = 0;
+  if (k < QMM_KERNEL_AUTO || k > QMM_KERNEL_GROUPED_MATMUL) return fail(QMM_E_ARG, "unknown kernel setting");
+  forced_kernel();   // the environment is consumed first, so it cannot override this later
+  g_kernel.store(int(k), std::memory_order_relaxed);
+  return QMM_OK;
+}
+
+int qmm_get_kernel(void) { return forced_kernel(); }
 
 uint32_t qmm_layout_version(void) { return qmm::kLayoutVersion; }
 
@@ -219,22 +278,28 @@ qmm_status gemm_impl(const char* name, bool noalloc, qmm_format f, const void* p
   if (!aligned(packed, 256)) return fail(QMM_E_ALIGN, "packed must be 256-byte aligned");
   if (!aligned(x, 16)) return fail(QMM_E_ALIGN, "x must be 16-byte aligned");
   if (!aligned(y, 2)) return fail(QMM_E_ALIGN, "y must be 2-byte aligned");
-  const size_t need = qmm_workspace_bytes(f, t, n, d);
+  int kf;
+  if ((st = check_kernel(&kf))) return st;
+  if (kf == QMM_KERNEL_FEW_ROW && !qmm::skinny_fits(t, n, d, l))
+    return fail(QMM_E_UNSUPPORTED, "the few-row kernel takes 2 <= t <= 64 rows (kernel forced to few_row)");
+  const size_t need = gemm_ws_bytes(kf, f, t, n, d, l);
   if (noalloc) {
     if (need > qmm::kNoAllocScratchBytes)
       return fail(QMM_E_WORKSPACE, "the split-K partials of this shape exceed the 64 MiB static scratch of qmm_gemm_noalloc");
     ws = nullptr;
     ws_bytes = 0;
-    if (need && t > 1) {
+    if (need) {
       const int err = qmm::noalloc_scratch(stream, &ws);
       if (err) return hip_fail(err, name);
       ws_bytes = qmm::kNoAllocScratchBytes;
     }
   }
   if ((st = check_ws(need, ws, ws_bytes))) return st;
-  if (t == 1) return qmm_gemv(f, packed, n, d, x, y, nullptr, 0, stream);
+  if (t == 1 && !forces_tile(kf)) return qmm_gemv(f, packed, n, d, x, y, nullptr, 0, stream);
   if (f == QMM_AFFINE4_G64 && !ws)
-    return fail(QMM_E_WORKSPACE, "affine weights with t >= 2 need a workspace of qmm_workspace_bytes() bytes");
+    return fail(QMM_E_WORKSPACE, "affine weights on the matmul kernels need a workspace of qmm_workspace_bytes() bytes");
+  if (kf == QMM_KERNEL_FEW_ROW && !ws)
+    return fail(QMM_E_WORKSPACE, "the few-row kernel needs a workspace of qmm_workspace_bytes() bytes");
   if (need && ws && !aligned(ws, 16)) return fail(QMM_E_ALIGN, "ws must be 16-byte aligned");
   qmm::GemmArgs a{};
   a.f = f;
@@ -244,9 +309,12 @@ qmm_status gemm_impl(const char* name, bool noalloc, qmm_format f, const void* p
   a.d = int(d);
   a.x = x;
   a.y = y;
-  int err = ws && qmm::skinny_fits(t, n, d, l)
+  // the tile kernel is told only the workspace bytes it may use: without the
+  // K-split planes when it must not split
+  const size_t tile_bytes = kf == QMM_KERNEL_TILE_UNSPLIT ? need : ws_bytes;
+  int err = ws && !forces_tile(kf) && qmm::skinny_fits(t, n, d, l)
                 ? qmm::launch_skinny(a, static_cast<float*>(ws), stream)
-                : qmm::launch_gemm_ws(a, need ? static_cast<float*>(ws) : nullptr, need ? ws_bytes : 0, stream);
+                : qmm::launch_gemm_ws(a, need ? static_cast<float*>(ws) : nullptr, need ? tile_bytes : 0, stream);
   if (err) return hip_fail(err, name);
   return QMM_OK;
 }
@@ -292,11 +360,14 @@ qmm_status grouped(const char* name, bool swiglu, qmm_format f, const void* pack
   if (!aligned(row_index, 4) || !aligned(seg_expert, 4) || !aligned(seg_offsets, 4))
     return fail(QMM_E_ALIGN, "routing tables must be 4-byte aligned");
   if ((st = check_ws(0, ws, ws_bytes))) return st;
+  int kf;
+  if ((st = check_kernel(&kf))) return st;
   if (n_seg == 0 || m_total == 0) return QMM_OK;
   int err;
   // one row per segment takes the decode GEMV, unless the activation is
-  // fused or the rows are taken in order (the matmul kernel does both)
-  if (max_seg_rows == 1 && !swiglu && row_index && gemv_fits(n, d, l)) {
+  // fused or the rows are taken in order (the matmul kernel does both), or
+  // the matmul kernel is forced
+  if (max_seg_rows == 1 && !swiglu && row_index && gemv_fits(n, d, l) && kf != QMM_KERNEL_GROUPED_MATMUL) {
     qmm::GemvArgs a{};
     a.f = f;
     a.packed = static_cast<const uint8_t*>(packed_stack);

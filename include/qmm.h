@@ -104,7 +104,8 @@ size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
  * times slower for 2 <= t <= 64.  A non-NULL ws must be 16-byte aligned and
  * hold at least this many bytes (QMM_E_ALIGN, QMM_E_WORKSPACE).  Its contents
  * on entry do not matter, and calls sharing one workspace must be ordered on
- * one stream.  Host only. */
+ * one stream.  Under a forced kernel (qmm_set_kernel) the size is that
+ * kernel's.  Host only. */
 size_t qmm_workspace_bytes(qmm_format f, int64_t t, int64_t n, int64_t d);
 
 /* Pack canonical weights into the MI355X device layout.  The codes are the
@@ -317,6 +318,45 @@ qmm_status qmm_route(const qmm_bf16* x, int64_t t, int64_t d, const qmm_bf16* r,
  * elapsed time is the call's execution time.  Either may be NULL.  The arming
  * is consumed by that next call; a call rejected by validation leaves it armed. */
 qmm_status qmm_profile_next(void* start_event, void* stop_event);
+
+/* Kernel override for A/B runs: one matmul kernel forced in place of the
+ * library's own choice, so that each can be timed and checked on its own.
+ * The pages switch fused paths off or on from the environment for exactly
+ * this ("LLM Decode / Prefill 优化案例（Metal）", Steps 9 and 11), and run only
+ * some kernels on the GPU to check them in isolation ("Colibri Kimi K3 Metal
+ * 后端实现全解析", Phase 10).
+ *   QMM_KERNEL_AUTO            the library's choice (the default).
+ *   QMM_KERNEL_TILE            qmm_gemm / qmm_gemm_noalloc run the tile GEMM
+ *                              for every t >= 1 (t = 1 included), with its
+ *                              own tile height and K split.
+ *   QMM_KERNEL_TILE_UNSPLIT    the same, never split along K.
+ *   QMM_KERNEL_FEW_ROW         qmm_gemm runs the few-row split-K kernel; a
+ *                              shape it does not take (t = 1 or t > 64)
+ *                              returns QMM_E_UNSUPPORTED, and it needs a
+ *                              workspace for both formats.
+ *   QMM_KERNEL_GROUPED_MATMUL  qmm_grouped_gemm runs the matmul kernel also
+ *                              where every segment has one row.
+ * A setting that does not concern a call leaves it as under AUTO.
+ * qmm_workspace_bytes reports the workspace of the kernel the setting
+ * selects, so size workspaces after changing it.  The setting is
+ * process-wide and takes effect for calls that start after it returns.  Its
+ * initial value comes from the environment variable QMM_FORCE_KERNEL, read
+ * once at the first call that consults it: unset, "" or "auto", "tile",
+ * "tile_unsplit", "few_row", "grouped_matmul", or the digits 0..4.  Any other
+ * value makes qmm_gemm, qmm_gemm_noalloc and the grouped calls fail with
+ * QMM_E_ARG (a mistyped switch is reported, not ignored) until qmm_set_kernel
+ * is called.  qmm_set_kernel returns QMM_E_ARG for a value outside the enum;
+ * qmm_get_kernel returns the current setting, -1 for an invalid environment
+ * value.  Host only. */
+typedef enum {
+  QMM_KERNEL_AUTO = 0,
+  QMM_KERNEL_TILE = 1,
+  QMM_KERNEL_TILE_UNSPLIT = 2,
+  QMM_KERNEL_FEW_ROW = 3,
+  QMM_KERNEL_GROUPED_MATMUL = 4
+} qmm_kernel;
+qmm_status qmm_set_kernel(qmm_kernel k);
+int qmm_get_kernel(void);
 
 /* Measurement support: the achievable HBM read rate.  Reads every byte of the
  * device buffer `src` once (16-byte non-temporal loads, four in flight per

@@ -104,6 +104,75 @@ def test_noalloc_limit_is_checked_on_the_host():
     assert lib.qmm_gemm_noalloc(A, P, 0, 16, 64, P, P, None) == E_ARG
 
 
+@pytest.fixture
+def kernel_auto_after():
+    yield
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_AUTO)
+
+
+def test_kernel_override_sizes_and_refusals(kernel_auto_after):
+    """The workspace follows the forced kernel; a shape the forced kernel does
+    not take is refused on the host."""
+    lib = qmm.load()
+    up = lambda v: -(-v // 256) * 256
+    assert lib.qmm_set_kernel(5) == E_ARG and lib.qmm_set_kernel(-1) == E_ARG
+    assert qmm.qmm_get_kernel() == qmm.QMM_KERNEL_AUTO
+    skinny4 = 10 * 4 * 13824 * 4
+    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == skinny4
+    tile_aff = lambda t: up(t * 5120 * 2) + up(t * 4) + 13824 * 4
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_TILE)
+    assert qmm.qmm_get_kernel() == qmm.QMM_KERNEL_TILE
+    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == tile_aff(4)       # no split for t <= 64
+    assert qmm.qmm_workspace_bytes(A, 1, 13824, 5120) == tile_aff(1)       # t = 1 on the tile kernel too
+    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5120) == tile_aff(65) + 4 * 65 * 13824 * 4
+    assert qmm.qmm_workspace_bytes(M, 4, 13824, 5120) == 0
+    assert lib.qmm_gemm(A, P, 1, 16, 64, P, P, None, 0, None) == E_WS     # affine tile needs one at t = 1
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_TILE_UNSPLIT)
+    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5120) == tile_aff(65)
+    assert qmm.qmm_workspace_bytes(M, 256, 13824, 5120) == 0
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_FEW_ROW)
+    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == skinny4
+    assert qmm.qmm_workspace_bytes(M, 4, 13824, 5120) == skinny4
+    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5120) == 0
+    assert lib.qmm_gemm(A, P, 65, 16, 64, P, P, P, 1 << 20, None) == E_UNSUPPORTED
+    assert lib.qmm_gemm(A, P, 1, 16, 64, P, P, P, 1 << 20, None) == E_UNSUPPORTED
+    assert "few-row" in qmm.qmm_last_error()
+    assert lib.qmm_gemm(M, P, 4, 16, 64, P, P, None, 0, None) == E_WS     # few-row needs one for MXFP4 too
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_GROUPED_MATMUL)
+    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == skinny4           # no effect on qmm_gemm
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_AUTO)
+    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == skinny4
+
+
+@pytest.mark.parametrize("value,want", [("tile", 1), ("tile_unsplit", 2), ("few_row", 3),
+                                        ("grouped_matmul", 4), ("4", 4), ("auto", 0), ("", 0),
+                                        ("Tile", -1), ("fast", -1)])
+def test_kernel_override_from_the_environment(value, want):
+    """QMM_FORCE_KERNEL sets the initial value; an unknown one makes the
+    matmul calls fail with QMM_E_ARG until qmm_set_kernel is called."""
+    import subprocess
+    import sys
+    code = f"""
+import bit_weight_quantized_amd as qmm
+lib = qmm.load()
+P = 1 << 20
+assert qmm.qmm_get_kernel() == {want}, qmm.qmm_get_kernel()
+if {want} < 0:
+    assert qmm.qmm_workspace_bytes(1, 4, 16, 64) == 0
+    assert lib.qmm_gemm(1, P, 4, 16, 64, P, P, P, 1 << 20, None) == 1
+    assert "QMM_FORCE_KERNEL" in qmm.qmm_last_error()
+    stride = qmm.qmm_packed_bytes(2, 16, 64)
+    assert lib.qmm_grouped_gemm(2, P, stride, 1, 16, 64, P, 1, P, P, P, 1, 1, 1, P, None, 0, None) == 1
+    assert "QMM_FORCE_KERNEL" in qmm.qmm_last_error()
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_AUTO)
+    assert qmm.qmm_get_kernel() == 0
+    assert qmm.qmm_workspace_bytes(1, 4, 16, 64) == 256
+"""
+    env = dict(os.environ, QMM_FORCE_KERNEL=value)
+    r = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+
+
 def test_status_strings_and_version():
     assert qmm.qmm_status_string(0) == "ok"
     for s in range(1, 9):

@@ -647,6 +647,88 @@ def test_gemm_prefill_workload_full():
 
 
 # ---------------------------------------------------------------------------
+# Kernel override (qmm_set_kernel): each matmul kernel forced in turn
+# ---------------------------------------------------------------------------
+
+@pytest.fixture
+def kernel_auto_after():
+    yield
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_AUTO)
+
+
+FORCED = (qmm.QMM_KERNEL_AUTO, qmm.QMM_KERNEL_TILE, qmm.QMM_KERNEL_TILE_UNSPLIT, qmm.QMM_KERNEL_FEW_ROW)
+
+
+def run_gemm_forced(kernel, fmt, packed, n, d, x_bits):
+    """qmm_gemm under a forced kernel, with the workspace qmm_workspace_bytes
+    reports under that setting (NaN-filled), none if it reports 0."""
+    qmm.qmm_set_kernel(kernel)
+    t = x_bits.shape[0]
+    need = qmm.qmm_workspace_bytes(fmt, t, n, d)
+    ws = guarded((need // 4,), float("nan"), torch.float32) if need else None
+    y = nan_out(t, n)
+    qmm.qmm_gemm(fmt, packed, t, n, d, dev(x_bits), y, ws)
+    torch.cuda.synchronize()
+    return host_u16(y)
+
+
+@pytest.mark.parametrize("fmt,t,n,d", [(A, 1, 300, 1024), (A, 4, 300, 1024), (M, 4, 257, 1536),
+                                       (A, 64, 520, 2048), (M, 70, 300, 1024), (A, 130, 300, 2048),
+                                       (M, 1, 130, 576)])
+def test_forced_kernels_integer_exact(fmt, t, n, d, kernel_auto_after):
+    """Integer weights (affine scale 1 bias 0; MXFP4 with E8M0 127) and
+    integer activations: every sum is exact in fp32, so the GEMV, the few-row
+    kernel and the tile kernel (split along K or not) must all return the
+    oracle's sums rounded to bf16, bit for bit.  The few-row kernel refuses
+    t = 1 and t > 64."""
+    say("forced kernels integer exact", fmt, t, n, d)
+    rng = np.random.default_rng(40 + t)
+    x = synth.bf16_bits(rng.integers(-3, 4, size=(t, d)).astype(float))
+    if fmt == A:
+        w = integer_affine(60 + t, n, d)
+        p = pack_affine(w)
+        yr, _ = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(60 + t, n, d, 127, 1)
+        p = pack_mxfp4(w)
+        yr, _ = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    assert np.all(np.abs(yr) < 2 ** 24)
+    want = oracle.f64_to_bf16_bits(yr)
+    for k in FORCED:
+        if k == qmm.QMM_KERNEL_FEW_ROW and not 2 <= t <= 64:
+            qmm.qmm_set_kernel(k)
+            assert qmm.qmm_workspace_bytes(fmt, t, n, d) == 0
+            with pytest.raises(qmm.QmmError) as ei:
+                qmm.qmm_gemm(fmt, p, t, n, d, dev(x), nan_out(t, n), None)
+            assert ei.value.status == 4, ei.value   # QMM_E_UNSUPPORTED
+            continue
+        y = run_gemm_forced(k, fmt, p, n, d, x)
+        assert np.array_equal(y, want), f"kernel setting {k}"
+
+
+@pytest.mark.parametrize("fmt,t,n,d", [(A, 48, 1000, 1024), (M, 33, 300, 3584), (A, 200, 520, 2048),
+                                       (A, 3, 259, 576)])
+def test_forced_kernels_parity(fmt, t, n, d, kernel_auto_after):
+    """Random weights and activations under every kernel setting that takes
+    the shape, each within the oracle's bound."""
+    say("forced kernels parity", fmt, t, n, d)
+    x = synth.activations(6700 + t, synth.S_X, t, d)
+    if fmt == A:
+        w = synth.affine_weights(5700 + n, n, d)
+        p = pack_affine(w)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(7700 + n, n, d)
+        p = pack_mxfp4(w)
+        yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    for k in FORCED:
+        if k == qmm.QMM_KERNEL_FEW_ROW and not 2 <= t <= 64:
+            continue
+        y = run_gemm_forced(k, fmt, p, n, d, x)
+        assert_parity(y, yr, ar, f"forced kernel {k} fmt={fmt} {t}x{n}x{d}")
+
+
+# ---------------------------------------------------------------------------
 # Grouped (routed experts)
 # ---------------------------------------------------------------------------
 
@@ -690,6 +772,30 @@ def test_grouped_gemm_small(fmt, d):
     for max_rows in (max(sizes), 1):      # MFMA path, then the GEMV path on the same table
         y = run_grouped(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, max_rows)
         assert_parity(y, yr, ar, f"grouped fmt={fmt} d={d} max_rows={max_rows}")
+
+
+@pytest.mark.parametrize("fmt", [A, M])
+def test_grouped_forced_matmul_on_one_row_segments(fmt, kernel_auto_after):
+    """One row per segment takes the grouped GEMV; forced, the matmul kernel
+    takes the same table.  Integer weights and activations: both exact."""
+    say("grouped forced matmul", fmt)
+    n, d, n_exp, t = 300, 1024, 6, 16
+    ws = [integer_affine(930 + e, n, d) if fmt == A else rand_mxfp4(930 + e, n, d, 127, 1) for e in range(n_exp)]
+    stk, size = stack(fmt, ws)
+    rng = np.random.default_rng(31)
+    x = synth.bf16_bits(rng.integers(-3, 4, size=(t, d)).astype(float))
+    seg_expert = [5, 0, 3, 2, 1]
+    seg_offsets = np.arange(len(seg_expert) + 1)
+    row_index = np.asarray([7, 0, 15, 3, 9], np.int32)
+    deq = (lambda e: oracle.dequant_affine(ws[e].codes, ws[e].scale, ws[e].bias)) if fmt == A else \
+          (lambda e: oracle.dequant_mxfp4(ws[e].codes, ws[e].e8m0))
+    yr, _ = oracle.grouped(x, row_index, seg_expert, seg_offsets, deq)
+    assert np.all(np.abs(yr) < 2 ** 24)
+    want = oracle.f64_to_bf16_bits(yr)
+    for k in (qmm.QMM_KERNEL_AUTO, qmm.QMM_KERNEL_GROUPED_MATMUL):
+        qmm.qmm_set_kernel(k)
+        y = run_grouped(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, 1)
+        assert np.array_equal(y, want), f"kernel setting {k}"
 
 
 # ---------------------------------------------------------------------------
