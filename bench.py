@@ -17,8 +17,8 @@ in HBM:
   moe_ffn   the rest of the expert FFN on the same routed rows: gate_up with
             the SwiGLU activation fused, down on the activated rows, and the
             renormalised weighted combine back to the 512 tokens
-Weights of the decode row rotate over enough packed copies (> 2x the 256 MB
-Infinity Cache) that every launch reads HBM, not the cache.  After the timed
+Weights of the decode and prefill rows rotate over enough packed copies (> 2x
+the 256 MB Infinity Cache) that every launch reads HBM, not the cache.  After the timed
 steps, a plain streaming read of the decode row's byte count (qmm_stream_read,
 rotated the same way, timed the same way) is reported as the achievable read
 ceiling at that size (`stream_ceiling`), and when the prefill row runs, a
@@ -242,14 +242,16 @@ def main(argv=None) -> int:
         w2 = synth.affine_weights(synth.seed_of(2), n2, d2)
         p2 = torch.empty(qmm.qmm_packed_bytes(A, n2, d2), dtype=torch.uint8, device=dev)
         qmm.qmm_pack(A, n2, d2, T(w2.codes), T(w2.scale), T(w2.bias), p2)
-        p2s = [p2, p2.clone()]
+        # sixteen packed copies (637 MB, more than twice the 256 MB Infinity
+        # Cache): each call reads weights that the calls before it evicted
+        p2s = [p2] + [p2.clone() for _ in range(15)]
         x2 = T(synth.activations(synth.seed_of(2), synth.S_X, t2, d2))
         y2 = torch.empty(t2, n2, dtype=torch.int16, device=dev)
         # affine weights: the activations go to fp16 in the workspace first (the
         # pre-pass kernel is inside the stamped interval)
         ws2 = torch.empty(qmm.qmm_workspace_bytes(A, t2, n2, d2) // 4, dtype=torch.float32, device=dev)
         b2 = n2 * d2 * 36 // 64 + 2 * t2 * d2 + 2 * t2 * n2
-        work["prefill"] = [(lambda s: qmm.qmm_gemm(A, p2s[s % 2], t2, n2, d2, x2, y2, ws2),
+        work["prefill"] = [(lambda s: qmm.qmm_gemm(A, p2s[s % len(p2s)], t2, n2, d2, x2, y2, ws2),
                             "gemm", b2, 2.0 * t2 * n2 * d2)]
         ctx["cfg2"] = dict(name=c2["name"], w=w2, x=synth.activations(synth.seed_of(2), synth.S_X, t2, d2), y=y2,
                            t=t2, flops=2.0 * t2 * n2 * d2)
