@@ -7,7 +7,12 @@
 // packed layout the quad's 4 rows of one slab are 1 KiB contiguous, so each
 // wave code load is one contiguous 1 KiB, and since every wave walks the slabs
 // in the same order the whole GPU sweeps the weights front to back like a
-// streaming copy.  No work is split across waves: no cross-wave reduction.
+// streaming copy.  A matrix with few quads (n <= 6144) would leave most of
+// the chip with one short chain of slab loads per wave, so there the quad's
+// slabs are dealt to WQ = 2 or 4 waves of the workgroup (slab s to wave
+// s % WQ), each lane's per-slab partial sum goes to LDS, and one wave adds them
+// in slab order exactly as a single wave adds them in registers: the result is
+// bit for bit the same whatever WQ.
 //
 // Load order.  A wave's vector-memory loads complete in issue order, and a
 // wait names how many may still be outstanding, so every load is issued
@@ -45,7 +50,7 @@
 namespace qmm {
 namespace {
 
-constexpr int kWaves = 4;                 // quads per workgroup
+constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRing = 3;                  // code slabs in flight per lane (3 KiB per wave)
 constexpr int kPassSlabs = 12;            // slabs staged in LDS per pass
@@ -92,7 +97,7 @@ __device__ __forceinline__ float chunk_partial(const u32x4_t w, const uint8_t* x
   return __builtin_ldexpf(mxfp4_dot32(w, xp), int(m) - 127);
 }
 
-template <int FMT, bool GROUPED>
+template <int FMT, bool GROUPED, int WQ>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(
     const uint8_t* __restrict__ base, int64_t expert_stride, int n_experts, int64_t codes_off,
     int64_t meta_off, uint32_t codes_bytes, uint32_t meta_bytes, int n, int d,
@@ -111,12 +116,18 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
   const uint32_t m_base = x_trash + 16u;
   const uint32_t m_wave = uint32_t(pslabs) * QMB;
   const uint32_t m_trash = m_base + kWaves * m_wave;
+  // WQ > 1: per-slab partial sums of the pass, [slab][quad of the workgroup][lane],
+  // after the metadata trash slot
+  constexpr int QPW = kWaves / WQ;   // quads per workgroup
+  float* red = reinterpret_cast<float*>(smem + m_trash + 16u);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rsub = lane >> 4, c = lane & 15;
-  const int quad = blockIdx.x * kWaves + wave;
+  const int wk = wave % WQ;           // this wave's share of the quad's slabs: s % WQ == wk
+  const int ql = wave / WQ;
+  const int quad = blockIdx.x * QPW + ql;
   const int row = quad * 4 + rsub;
   const int lrow = min(row, n - 1);   // rows past n (last quad only) load row n - 1, store nothing
 
@@ -161,12 +172,15 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
 #pragma unroll
       for (int i = 0; i < ML; ++i) {
         const int pc = lane + 64 * i;
-        mv[i] = ld16(mr, 16 * pc < mbytes ? m0 + 16u * pc : kOOB);
+        const bool mine = WQ == 1 || (16 * pc / QMB) % WQ == wk;
+        mv[i] = ld16(mr, 16 * pc < mbytes && mine ? m0 + 16u * pc : kOOB);
       }
       // 3. the code ring: this lane's chunk of slab s (zeros past the slab's width)
-      auto code_off = [&](int s) -> uint32_t {
-        const int sg = p0 + s;
-        if (s >= ps) return kOOB;
+      // the wave's i-th slab of the pass is slab wk + WQ·i
+      const int cnt = ps > wk ? (ps - wk + WQ - 1) / WQ : 0;
+      auto code_off = [&](int i) -> uint32_t {
+        const int sg = p0 + wk + WQ * i;
+        if (i >= cnt) return kOOB;
         return 32 * c < L.width(sg) ? uint32_t(L.codes(sg, lrow)) + 16u * c : kOOB;
       };
       u32x4_t ring[kRing];
@@ -203,11 +217,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         __syncthreads();
       }
       // 5. consume slab s from ring slot s % kRing, refill it with slab s + kRing
-      for (int s0 = 0; s0 < ps; s0 += kRing) {
+      for (int i0 = 0; i0 < cnt; i0 += kRing) {
 #pragma unroll
         for (int j = 0; j < kRing; ++j) {
-          const int s = s0 + j;
-          if (s < ps) {
+          const int i = i0 + j;
+          if (i < cnt) {
+            const int s = wk + WQ * i;
             const int sg = p0 + s;
             const uint8_t* mp = mwave + s * QMB + rsub * L.meta_row(sg);
             const uint32_t m = FMT == QMM_AFFINE4_G64
@@ -215,26 +230,37 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
                                    : uint32_t(mp[c]);
             const float part = chunk_partial<FMT>(ring[j], smem + (s * 16 + c) * kChunkBytes, m);
             // chunks past a narrow last slab hold no weights (their metadata is not staged)
-            acc += 32 * c < L.width(sg) ? part : 0.f;
+            const float pv = 32 * c < L.width(sg) ? part : 0.f;
+            if constexpr (WQ == 1)
+              acc += pv;
+            else
+              red[(s * QPW + ql) * 64 + lane] = pv;
           }
-          ring[j] = ld16_stream(cr, code_off(s + kRing));
+          ring[j] = ld16_stream(cr, code_off(i + kRing));
         }
+      }
+      if constexpr (WQ > 1) {
+        // the pass's slab partials added in slab order, as one wave would
+        __syncthreads();
+        if (wk == 0)
+          for (int s = 0; s < ps; ++s) acc += red[(s * QPW + ql) * 64 + lane];
       }
       if (p0 + kPassSlabs < nslabs || (GROUPED && gr + 1 < r_end)) __syncthreads();
     }
     const float v = sum16(acc);
-    if (c == 0 && row < n) yrow[row] = f32_to_bf16((GROUPED && bad_row) ? __builtin_nanf("") : v);
+    if (wk == 0 && c == 0 && row < n) yrow[row] = f32_to_bf16((GROUPED && bad_row) ? __builtin_nanf("") : v);
   }
 }
 
-template <int FMT, bool GROUPED>
+template <int FMT, bool GROUPED, int WQ>
 void launch_fmt(const GemvArgs& a, const Layout& l, dim3 grid, hipStream_t s) {
   const uint32_t codes_bytes = uint32_t(int64_t(a.n) * (a.d / 2));
   const uint32_t meta_bytes = uint32_t(l.meta_bytes);
   const int nslabs = (a.d + kSlabCodes - 1) / kSlabCodes;
   const int ps = nslabs < kPassSlabs ? nslabs : kPassSlabs;
-  const size_t lds = size_t(ps) * 16 * kChunkBytes + 16 + size_t(kWaves) * ps * quad_meta_bytes<FMT>() + 16;
-  launch_kernel_lds((gemv_kernel<FMT, GROUPED>), grid, dim3(kThreads), lds, s, a.packed,
+  const size_t lds = size_t(ps) * 16 * kChunkBytes + 16 + size_t(kWaves) * ps * quad_meta_bytes<FMT>() + 16 +
+                     (WQ > 1 ? size_t(ps) * (kWaves / WQ) * 64 * 4 : 0);
+  launch_kernel_lds((gemv_kernel<FMT, GROUPED, WQ>), grid, dim3(kThreads), lds, s, a.packed,
                     a.expert_stride, a.n_experts, l.codes_offset, l.meta_offset, codes_bytes,
                     meta_bytes, a.n, a.d, a.x, a.t_x, a.row_index, a.seg_expert, a.seg_offsets,
                     a.m_total, a.y);
@@ -250,18 +276,33 @@ int launch_gemv(const GemvArgs& a, void* stream) {
     return int(hipErrorInvalidValue);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nseg = a.n_seg > 0 ? a.n_seg : 1;
-  const int wrows = 4 * kWaves;
-  dim3 grid(unsigned((a.n + wrows - 1) / wrows), unsigned(nseg));
+  // waves per quad: a few quads (measured at d = 5120: n = 512 .. 5120 gain
+  // 0.4 - 0.6 µs of 4 - 6 µs with four waves per quad; 7168 and 13824 lose
+  // with any split) are split along K while each wave keeps two slabs or more
+  const int quads = (a.n + 3) / 4;
+  const int nslabs = (a.d + kSlabCodes - 1) / kSlabCodes;
+  const int wq = a.n_seg > 0 || quads > 1536 ? 1 : nslabs >= 8 ? 4 : nslabs >= 4 ? 2 : 1;
+  dim3 grid(unsigned((int64_t(quads) * wq + kWaves - 1) / kWaves), unsigned(nseg));
   if (a.n_seg > 0) {
     if (a.f == QMM_AFFINE4_G64)
-      launch_fmt<QMM_AFFINE4_G64, true>(a, l, grid, s);
+      launch_fmt<QMM_AFFINE4_G64, true, 1>(a, l, grid, s);
     else
-      launch_fmt<QMM_MXFP4_G32, true>(a, l, grid, s);
+      launch_fmt<QMM_MXFP4_G32, true, 1>(a, l, grid, s);
+  } else if (wq == 4) {
+    if (a.f == QMM_AFFINE4_G64)
+      launch_fmt<QMM_AFFINE4_G64, false, 4>(a, l, grid, s);
+    else
+      launch_fmt<QMM_MXFP4_G32, false, 4>(a, l, grid, s);
+  } else if (wq == 2) {
+    if (a.f == QMM_AFFINE4_G64)
+      launch_fmt<QMM_AFFINE4_G64, false, 2>(a, l, grid, s);
+    else
+      launch_fmt<QMM_MXFP4_G32, false, 2>(a, l, grid, s);
   } else {
     if (a.f == QMM_AFFINE4_G64)
-      launch_fmt<QMM_AFFINE4_G64, false>(a, l, grid, s);
+      launch_fmt<QMM_AFFINE4_G64, false, 1>(a, l, grid, s);
     else
-      launch_fmt<QMM_MXFP4_G32, false>(a, l, grid, s);
+      launch_fmt<QMM_MXFP4_G32, false, 1>(a, l, grid, s);
   }
   return int(hipGetLastError());
 }

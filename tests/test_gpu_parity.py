@@ -247,6 +247,35 @@ def test_gemv_fused_projections(shapes, d):
         off += w.n
 
 
+@pytest.mark.parametrize("fmt,small,d", [(A, 999, 5184), (A, 77, 2048), (M, 130, 3584), (A, 5, 8704),
+                                         (M, 6, 20480)])
+def test_gemv_split_quads_bitwise(fmt, small, d):
+    """A matrix of few rows deals each quad's slabs to 2 or 4 waves and adds
+    their per-slab partials in slab order; a matrix of more than 6144 rows
+    keeps one wave per quad.  The first rows of a large matrix, packed as a
+    matrix of their own, must give the same bits both ways (narrow last slab,
+    several LDS passes, both formats), and meet the oracle."""
+    big = 6400
+    say("gemv split quads", fmt, small, big, d)
+    if fmt == A:
+        wb = synth.affine_weights(5300 + d, big, d)
+        ws = synth.Affine(wb.codes[:small], wb.scale[:small], wb.bias[:small])
+        pb, ps = pack_affine(wb), pack_affine(ws)
+    else:
+        wb = rand_mxfp4(5300 + d, big, d)
+        ws = synth.MXFP4(wb.codes[:small], wb.e8m0[:small])
+        pb, ps = pack_mxfp4(wb), pack_mxfp4(ws)
+    x = synth.activations(5400 + d, synth.S_X, 1, d)
+    yb = run_gemv(fmt, pb, wb, x[0])
+    ysm = run_gemv(fmt, ps, ws, x[0])
+    assert np.array_equal(yb[:small], ysm)
+    if fmt == A:
+        yr, ar = oracle.gemm_affine(x, ws.codes, ws.scale, ws.bias)
+    else:
+        yr, ar = oracle.gemm_mxfp4(x, ws.codes, ws.e8m0)
+    assert_parity(ysm, yr[0], ar[0], f"gemv split quads {small}x{d}")
+
+
 def run_gemv_int8(packed, n, d, x_bits):
     y = nan_out(n)
     qmm.qmm_gemv_int8(A, packed, n, d, dev(x_bits), y)
