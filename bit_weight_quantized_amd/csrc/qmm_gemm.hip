@@ -135,11 +135,20 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 // fp16 subnormals (q·2^-24 or q·2^-20, see affine_word_to_bf16x8_mix), and
 // v_fma_mix{lo,hi}_f16 form fp16(sv·(fp16) + b) with the fma in fp32, so
 // sv = s·2^(24 + f) (or 2^(20 + f)) and b = bias·2^f give fp16(2^f·(s·q + bias)).
-__device__ __forceinline__ uint32_t mix_f16x2(float sv, uint32_t p, float b) {
+// The two halves separately: a half written right after the other half of
+// the same register costs a wait state, so the tile kernel issues other
+// instructions between them.
+__device__ __forceinline__ uint32_t mix_f16_lo(float sv, uint32_t p, float b) {
   uint32_t r;
   asm("v_fma_mixlo_f16 %0, %1, %2, %3 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(sv), "v"(p), "v"(b));
+  return r;
+}
+__device__ __forceinline__ uint32_t mix_f16_hi(uint32_t r, float sv, uint32_t p, float b) {
   asm("v_fma_mixhi_f16 %0, %1, %2, %3 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "+v"(r) : "v"(sv), "v"(p), "v"(b));
   return r;
+}
+__device__ __forceinline__ uint32_t mix_f16x2(float sv, uint32_t p, float b) {
+  return mix_f16_hi(mix_f16_lo(sv, p, b), sv, p, b);
 }
 
 // bf16 pair r (codes 2r, 2r + 1) of an MXFP4 word; r folds to a constant
@@ -465,6 +474,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
     }
     return mxfp4_pair(v, sc[cb], r);
   };
+  // affine: the masked nibble pair, multiplier and bias of register e
+  auto mix_args = [&](const WChunk& c, const AffineMix* am, int e, uint32_t& pr, float& sv, float& bv) {
+    const int j = e >> 3, cb = (e >> 2) & 1, r = e & 3;
+    const uint32_t v = c.w[cb][j];
+    pr = (r >= 2 ? v >> 8 : v) & ((r & 1) ? 0x00F000F0u : 0x000F000Fu);
+    sv = (r & 1) ? am[cb].s20 : am[cb].s24;
+    bv = am[cb].b;
+  };
   auto consts = [&](const WChunk& c, AffineMix* am, float* sc) {
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -503,6 +520,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int i = p % RB, j = p / RB;
+      // this pair's share of the next step's B registers
+      const int e_lo = p >= kDq ? (p - kDq) * 32 / (NP - kDq) : 0;
+      const int e_hi = p >= kDq ? (p + 1 - kDq) * 32 / (NP - kDq) : 0;
+      // the weight reads issued at the stage start have two pairs to arrive
+      if (p == kDq) consts(wn, am, sc);
+      if constexpr (AFF) {
+        // affine: the low halves ahead of the pair's MFMAs, the high halves
+        // after them
+#pragma unroll
+        for (int e = e_lo; e < e_hi; ++e) {
+          uint32_t pr;
+          float sv, bv;
+          mix_args(wn, am, e, pr, sv, bv);
+          bnext[(e >> 2) & 1][e >> 3][e & 3] = mix_f16_lo(sv, pr, bv);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         if constexpr (AFF)
@@ -525,12 +559,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(const uint8_t* __restrict__ c
       }
       if (p < RB) copy_x(ks + kXDist, xs_wr, p);
       if (p == RB) copy_w(ks + 3, ws_wr);
-      // the weight reads issued at the stage start have two pairs to arrive
-      if (p == kDq) consts(wn, am, sc);
-      if (p >= kDq) {
+      if constexpr (AFF) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int e = (p - kDq) * 32 / (NP - kDq); e < (p + 1 - kDq) * 32 / (NP - kDq); ++e)
+      for (int e = e_lo; e < e_hi; ++e) {
+        if constexpr (AFF) {
+          uint32_t pr;
+          float sv, bv;
+          mix_args(wn, am, e, pr, sv, bv);
+          bnext[(e >> 2) & 1][e >> 3][e & 3] = mix_f16_hi(bnext[(e >> 2) & 1][e >> 3][e & 3], sv, pr, bv);
+        } else {
           bnext[(e >> 2) & 1][e >> 3][e & 3] = dequant_reg(wn, am, sc, e);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
