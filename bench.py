@@ -443,6 +443,29 @@ def main(argv=None) -> int:
                         "frac": round(2.0 * t2 * n2 * d2 / lus / 1e6 / BF16_PEAK_TFLOPS, 4)}
         del wt
 
+    # the engine clock and board power while one kernel runs back to back for
+    # ~0.2 s (sysfs, sampled on a host thread): the clock the chip holds under
+    # that load, against its peak
+    under_load = {}
+    hw = gpu_sysfs_dir()
+    if hw:
+        # (launch name in the step, label, calls: ~0.2 s each); the calls rerun
+        # the step's own launches, whose outputs they rewrite with the same values
+        by_name = {name: fn for (_, fn, name, _, _) in launches}
+        probes = [("gemv", "decode_gemv", 20000), ("gemm", "prefill_gemm", 700),
+                  ("grouped_gemm", "moe_prefill_grouped_gemm", 140)]
+        nsteps = args.steps + args.warmup
+        for key, label, count in probes:
+            if key not in by_name:
+                continue
+            fn = by_name[key]
+            torch.cuda.synchronize()
+            with ClockSampler(hw) as cs:
+                for i in range(count):
+                    fn(i % nsteps)
+                torch.cuda.synchronize()
+            under_load[label] = cs.summary()
+
     hev.close()
     out = {
         "metric": METRIC,
@@ -491,6 +514,7 @@ def main(argv=None) -> int:
     out["wall_s_timed"] = round(wall, 3)
 
     out["gpu"].update(hip_runtime())
+    out["gpu"]["under_load"] = under_load or None
     if not args.no_cpu_baseline and ctx:
         # GPU outputs of the last timed step to the host, then the oracle
         for c in ctx.values():
@@ -536,7 +560,98 @@ def hip_runtime():
             rocm = f.read().strip()
     except OSError:
         pass
-    return {"hip_runtime_library": lib, "rocm_release": rocm}
+    out = {"hip_runtime_library": lib, "rocm_release": rocm}
+    # peak engine and memory clocks as the runtime reports them (kHz;
+    # hipDeviceAttributeClockRate = 5, hipDeviceAttributeMemoryClockRate = 60)
+    try:
+        import ctypes
+        hip = ctypes.CDLL("libamdhip64.so")
+        dev, v = ctypes.c_int(), ctypes.c_int()
+        if hip.hipGetDevice(ctypes.byref(dev)) == 0:
+            for key, attr in (("peak_sclk_MHz", 5), ("peak_mclk_MHz", 60)):
+                if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev) == 0:
+                    out[key] = round(v.value / 1000)
+    except OSError:
+        pass
+    return out
+
+
+def gpu_sysfs_dir():
+    """The sysfs directory of the GPU this process runs on (found by the PCI
+    bus id HIP reports), or None where its clock table is not readable."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        dev = ctypes.c_int()
+        buf = ctypes.create_string_buffer(64)
+        if hip.hipGetDevice(ctypes.byref(dev)) or hip.hipDeviceGetPCIBusId(buf, 64, dev):
+            return None
+        d = "/sys/bus/pci/devices/" + buf.value.decode().strip().lower()
+    except (OSError, UnicodeDecodeError):
+        return None
+    return d if os.access(os.path.join(d, "pp_dpm_sclk"), os.R_OK) else None
+
+
+class ClockSampler:
+    """Samples the GPU's current engine clock (the "S:" line of the driver's
+    pp_dpm_sclk table, or its starred level) and board power (hwmon
+    power1_input or power1_average) every ~2 ms on a host thread while a
+    workload runs; reads sysfs only, never the GPU."""
+
+    def __init__(self, d):
+        import glob
+        import threading
+        self.sclk_path = os.path.join(d, "pp_dpm_sclk")
+        self.power_path = None
+        for name in ("power1_input", "power1_average"):
+            hits = sorted(glob.glob(os.path.join(d, "hwmon", "hwmon*", name)))
+            if hits:
+                self.power_path = hits[0]
+                break
+        self.sclk, self.power = [], []
+        self.stop_flag = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _sclk(self):
+        try:
+            with open(self.sclk_path) as f:
+                lines = f.read().splitlines()
+        except OSError:
+            return None
+        pick = [ln for ln in lines if ln.strip().startswith("S:")] or [ln for ln in lines if ln.rstrip().endswith("*")]
+        for ln in pick:
+            for tok in ln.replace(":", " ").split():
+                if tok.lower().endswith("mhz") and tok[:-3].isdigit():
+                    return float(tok[:-3])
+        return None
+
+    def _run(self):
+        while not self.stop_flag.is_set():
+            v = self._sclk()
+            if v:
+                self.sclk.append(v)
+            if self.power_path:
+                try:
+                    with open(self.power_path) as f:
+                        self.power.append(float(f.read().strip()) / 1e6)
+                except (OSError, ValueError):
+                    pass
+            time.sleep(0.002)
+
+    def __enter__(self):
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop_flag.set()
+        self.thread.join()
+
+    def summary(self):
+        if not self.sclk:
+            return None
+        return {"sclk_MHz_median": round(float(np.median(self.sclk))), "sclk_MHz_min": round(float(np.min(self.sclk))),
+                "power_W_median": round(float(np.median(self.power)), 1) if self.power else None,
+                "samples": len(self.sclk)}
 
 
 def host_info():
