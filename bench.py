@@ -99,10 +99,16 @@ class HipEvents:
 
 
 def kernel_sources_hash(files) -> str:
+    """Hash of the sources' code with comments and blank space taken out, so a
+    comment edit does not retire counters taken on the same code."""
+    import re
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)    # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                  # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

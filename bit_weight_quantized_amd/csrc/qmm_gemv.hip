@@ -216,7 +216,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(
         }
         __syncthreads();
       }
-      // 5. consume slab s from ring slot s % kRing, refill it with slab s + kRing
+      // 5. consume the wave's i-th slab from ring slot i % kRing, refill the slot
+      //    with its slab i + kRing
       for (int i0 = 0; i0 < cnt; i0 += kRing) {
 #pragma unroll
         for (int j = 0; j < kRing; ++j) {
