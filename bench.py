@@ -1,6 +1,6 @@
 """Benchmark of the 4-bit weight-quantized matmul hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-clock-probe]
 
 One step runs every row of the hot path once, each on inputs already resident
 in HBM:
@@ -137,6 +137,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--rotate", type=int, default=24, help="packed copies of the decode weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock-probe", action="store_true",
+                    help="skip the back-to-back runs that sample the engine clock and board power")
     ap.add_argument("--rows", default="decode,qkv,prefill,moe_dec,moe_pre,moe_ffn",
                     help="comma list of decode, qkv, prefill, moe_dec, moe_pre, moe_ffn (needs moe_pre); "
                          "'copy' adds a plain 256 MiB device copy used to calibrate HBM byte counters")
@@ -453,7 +455,7 @@ def main(argv=None) -> int:
     # ~0.2 s (sysfs, sampled on a host thread): the clock the chip holds under
     # that load, against its peak
     under_load = {}
-    hw = gpu_sysfs_dir()
+    hw = None if args.no_clock_probe else gpu_sysfs_dir()
     if hw:
         # (launch name in the step, label, calls: ~0.2 s each); the calls rerun
         # the step's own launches, whose outputs they rewrite with the same values
