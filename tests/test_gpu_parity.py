@@ -404,6 +404,58 @@ def test_gemm_256_row_tiles(fmt, d):
     assert_parity(y, yr, ar, f"gemm 256-row tiles {fmt} {t}x{n}x{d}")
 
 
+@pytest.mark.parametrize("fmt,t,n,d", [(A, 4, 130, 65536), (A, 70, 130, 65536), (A, 300, 97, 65536),
+                                       (M, 4, 130, 65536), (M, 300, 97, 65504)])
+def test_gemm_largest_d(fmt, t, n, d):
+    """The largest reduction axis the layout takes (d = 65536, 128 slabs; and a
+    narrow last slab for MXFP4): the few-row kernel, the tile kernel split along
+    K and unsplit, both formats, against the oracle."""
+    say("gemm largest d", fmt, t, n, d)
+    x = synth.activations(6900 + t, synth.S_X, t, d)
+    if fmt == A:
+        w = synth.affine_weights(5900 + n, n, d)
+        y = run_gemm(A, pack_affine(w), n, d, x)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(7900 + n, n, d)
+        need = qmm.qmm_workspace_bytes(M, t, n, d)
+        ws = guarded((need // 4,), float("nan"), torch.float32) if need else None
+        y = nan_out(t, n)
+        qmm.qmm_gemm(M, pack_mxfp4(w), t, n, d, dev(x), y, ws)
+        torch.cuda.synchronize()
+        y = host_u16(y)
+        yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    assert_parity(y, yr, ar, f"gemm largest d {fmt} {t}x{n}x{d}")
+
+
+@pytest.mark.parametrize("fmt,d", [(A, 20480), (M, 20480), (M, 65504)])
+def test_grouped_long_reduction(fmt, d):
+    """Grouped matmul and grouped GEMV over a long reduction axis (40 or 128
+    slabs, MXFP4 ending in a narrow slab): segments of 0, 1, 5 and 70 rows."""
+    say("grouped long d", fmt, d)
+    n, n_exp, t = 96, 3, 80
+    ws_ = [synth.affine_weights(950 + e, n, d) if fmt == A else rand_mxfp4(950 + e, n, d) for e in range(n_exp)]
+    stk, size = stack(fmt, ws_)
+    x = synth.activations(951, synth.S_X, t, d)
+    sizes = [0, 1, 5, 70]
+    seg_expert = [2, 0, 1, 2]
+    seg_offsets = np.concatenate([[0], np.cumsum(sizes)])
+    rng = np.random.default_rng(952)
+    row_index = np.concatenate([np.sort(rng.choice(t, sz, replace=False)) for sz in sizes]).astype(np.int32)
+    deq = (lambda e: oracle.dequant_affine(ws_[e].codes, ws_[e].scale, ws_[e].bias)) if fmt == A else \
+          (lambda e: oracle.dequant_mxfp4(ws_[e].codes, ws_[e].e8m0))
+    yr, ar = oracle.grouped(x, row_index, seg_expert, seg_offsets, deq)
+    y = run_grouped(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, max(sizes))
+    assert_parity(y, yr, ar, f"grouped long d fmt={fmt} d={d}")
+    # one row per segment: the grouped GEMV on the same weights
+    seg1 = [0, 2, 1]
+    off1 = np.arange(4)
+    rows1 = np.asarray([3, 77, 40], np.int32)
+    yr1, ar1 = oracle.grouped(x, rows1, seg1, off1, deq)
+    y1 = run_grouped(fmt, stk, size, n_exp, n, d, x, seg1, off1, rows1, 1)
+    assert_parity(y1, yr1, ar1, f"grouped GEMV long d fmt={fmt} d={d}")
+
+
 @pytest.mark.parametrize("seed", range(16))
 def test_gemm_random_shapes(seed):
     """Seeded random shapes across the GEMM's paths, two per (path, format):
