@@ -6,7 +6,7 @@ One step runs every row of the hot path once, each on inputs already resident
 in HBM:
   decode    affine GEMV, T=1, D=5120, N=13824 (the headline), then its
             deferred-dequantisation variant (int8 activations) and a batch of
-            8 rows (qmm_gemm split along K) on the same weights
+            8 rows (qmm_gemm: the multi-row kernel) on the same weights
   qkv       a Q/K/V triple (5120, 1024, 1024 rows of D=5120) sharing one x: one
             GEMV over the matrices packed as one, then the three separately
   prefill   affine GEMM, T=2048, D=5120, N=13824 (bf16 MFMA)
@@ -193,14 +193,19 @@ def main(argv=None) -> int:
                           # the deferred-dequantisation variant (int8 activations) on the same weights
                           (lambda s: qmm.qmm_gemv_int8(A, copies[(s + 12) % len(copies)], n1, d1, x1, y1i),
                            "gemv_int8", b1, 2.0 * n1 * d1)]
-        # a batch of 8 decode rows on the same weights: qmm_gemm split along K
-        # through a workspace (both of its kernels inside the stamped interval)
-        x8 = T(synth.activations(synth.seed_of(1), synth.S_X, 8, d1, sub=3))
+        # a batch of 8 decode rows on the same weights: qmm_gemm as chosen by
+        # the library (the multi-row kernel here; under a forced kernel, with
+        # the workspace that kernel asks for, every kernel of the call inside
+        # the stamped interval)
+        x8h = synth.activations(synth.seed_of(1), synth.S_X, 8, d1, sub=3)
+        x8 = T(x8h)
         y8 = torch.empty(8, n1, dtype=torch.int16, device=dev)
-        ws8 = torch.empty(qmm.qmm_workspace_bytes(A, 8, n1, d1) // 4, dtype=torch.float32, device=dev)
+        ctx["batch8"] = dict(w=w1, x=x8h, y=y8)
+        ws8b = qmm.qmm_workspace_bytes(A, 8, n1, d1)
+        ws8 = torch.empty(ws8b // 4, dtype=torch.float32, device=dev) if ws8b else None
         b8 = n1 * d1 * 36 // 64 + 2 * 8 * d1 + 2 * 8 * n1
         work["decode"].append((lambda s: qmm.qmm_gemm(A, copies[(s + 6) % len(copies)], 8, n1, d1, x8, y8, ws8),
-                               "gemm_t8_split_k", b8, 2.0 * 8 * n1 * d1))
+                               "gemm_t8", b8, 2.0 * 8 * n1 * d1))
         # the small GEMV workload (T=1, D=256, N=512): 73.7 KB of weights, held
         # in cache after the first launch -- latency, not bandwidth, is its measure
         c0 = synth.CONFIGS[0]
@@ -517,7 +522,7 @@ def main(argv=None) -> int:
     # a kernel forced through QMM_FORCE_KERNEL (A/B runs) is named in the line
     ks = qmm.qmm_get_kernel()
     out["kernel_setting"] = {0: "auto", 1: "tile", 2: "tile_unsplit", 3: "few_row",
-                             4: "grouped_matmul"}.get(ks, f"invalid ({ks})")
+                             4: "grouped_matmul", 5: "multi_row"}.get(ks, f"invalid ({ks})")
     out["setup_s"] = round(t_setup, 1)
     out["wall_s_timed"] = round(wall, 3)
 
@@ -727,6 +732,11 @@ def oracle_phase(ctx, single_thread=True):
                      "seconds_single_thread": None if st is None else round(st, 4),
                      "GBps_single_thread": None if st is None else round(c["bytes"] / st / 1e9, 4),
                      "sample": f"{reps} whole GEMVs"}
+    # the 8-row decode batch on config 1's weights: every output
+    if "batch8" in ctx:
+        c = ctx["batch8"]
+        yr, ar = oracle.gemm_affine(c["x"], c["w"].codes, c["w"].scale, c["w"].bias)
+        rec("decode_batch8", oracle.check(c["y"], yr, ar), yr.size, "every output of the 8-row batch")
     # config 2: the weights dequantised once, then 64 of the 2048 rows
     if "cfg2" in ctx:
         c = ctx["cfg2"]

@@ -19,7 +19,7 @@ __all__ = [
     "qmm_layout_version", "qmm_profile_next", "qmm_stream_read", "qmm_route",
     "qmm_grouped_gemm_swiglu", "qmm_moe_combine", "qmm_gemv_int8", "qmm_gemm_noalloc", "qmm_set_kernel", "qmm_get_kernel",
     "QMM_KERNEL_AUTO", "QMM_KERNEL_TILE", "QMM_KERNEL_TILE_UNSPLIT", "QMM_KERNEL_FEW_ROW",
-    "QMM_KERNEL_GROUPED_MATMUL", "EXPORTS",
+    "QMM_KERNEL_GROUPED_MATMUL", "QMM_KERNEL_MULTI_ROW", "EXPORTS",
 ]
 
 QMM_AFFINE4_G64 = 1
@@ -30,6 +30,7 @@ QMM_KERNEL_TILE = 1
 QMM_KERNEL_TILE_UNSPLIT = 2
 QMM_KERNEL_FEW_ROW = 3
 QMM_KERNEL_GROUPED_MATMUL = 4
+QMM_KERNEL_MULTI_ROW = 5
 
 STATUS = {0: "QMM_OK", 1: "QMM_E_ARG", 2: "QMM_E_SHAPE", 3: "QMM_E_ALIGN", 4: "QMM_E_UNSUPPORTED",
           5: "QMM_E_WORKSPACE", 6: "QMM_E_HIP", 7: "QMM_E_LAYOUT", 8: "QMM_E_VALUE"}

@@ -29,7 +29,7 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Wall",
           "-ffp-contract=off"]
 
 LIBS = {
-    "qmm": dict(sources=["qmm_pack.hip", "qmm_gemv.hip", "qmm_gemm.hip", "qmm_stream.hip", "qmm_route.hip", "qmm_combine.hip", "qmm_gemv_i8.hip", "qmm_skinny.hip", "qmm_noalloc.hip", "qmm_api.cpp"],
+    "qmm": dict(sources=["qmm_pack.hip", "qmm_gemv.hip", "qmm_gemm.hip", "qmm_stream.hip", "qmm_route.hip", "qmm_combine.hip", "qmm_gemv_i8.hip", "qmm_skinny.hip", "qmm_mrow.hip", "qmm_noalloc.hip", "qmm_api.cpp"],
                 srcdir=CSRC, out=os.path.join(PKG, "libqmm.so")),
     "synth": dict(sources=["synth_gen.hip"], srcdir=os.path.join(ROOT, "synth", "csrc"),
                   out=os.path.join(ROOT, "synth", "libsynth.so")),

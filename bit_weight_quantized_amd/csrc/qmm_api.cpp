@@ -11,6 +11,7 @@
 
 #include "qmm_deferred.h"
 #include "qmm_internal.h"
+#include "qmm_mrow.h"
 #include "qmm_skinny.h"
 
 namespace {
@@ -62,6 +63,7 @@ int parse_kernel(const char* v) {
   if (!strcmp(v, "tile_unsplit") || !strcmp(v, "2")) return QMM_KERNEL_TILE_UNSPLIT;
   if (!strcmp(v, "few_row") || !strcmp(v, "3")) return QMM_KERNEL_FEW_ROW;
   if (!strcmp(v, "grouped_matmul") || !strcmp(v, "4")) return QMM_KERNEL_GROUPED_MATMUL;
+  if (!strcmp(v, "multi_row") || !strcmp(v, "5")) return QMM_KERNEL_MULTI_ROW;
   return kKernelInvalid;
 }
 
@@ -78,11 +80,24 @@ int forced_kernel() {
 qmm_status check_kernel(int* k) {
   *k = forced_kernel();
   if (*k == kKernelInvalid)
-    return fail(QMM_E_ARG, "QMM_FORCE_KERNEL is not one of auto, tile, tile_unsplit, few_row, grouped_matmul (or 0..4)");
+    return fail(QMM_E_ARG, "QMM_FORCE_KERNEL is not one of auto, tile, tile_unsplit, few_row, grouped_matmul, multi_row (or 0..5)");
   return QMM_OK;
 }
 
 bool forces_tile(int k) { return k == QMM_KERNEL_TILE || k == QMM_KERNEL_TILE_UNSPLIT; }
+
+// Whether qmm_gemm runs the multi-row GEMV under kernel setting k: when
+// forced, or by default where it was measured faster than the few-row
+// split-K kernel.  Each of its workgroups stages every activation row, so
+// narrow matrices (few columns per workgroup) favour the split-K kernel:
+// MXFP4 weights take it from 5120 columns, or for up to 8 rows; affine
+// weights, whose per-group scale and bias cost more per code, from 8192.
+bool uses_mrow(int k, int f, int64_t t, int64_t n, int64_t d, const qmm::Layout& l) {
+  if (k == QMM_KERNEL_MULTI_ROW) return qmm::mrow_fits(f, t, n, d, l);
+  // (the grouped-matmul setting does not concern qmm_gemm: as under auto)
+  if ((k != QMM_KERNEL_AUTO && k != QMM_KERNEL_GROUPED_MATMUL) || !qmm::mrow_fits(f, t, n, d, l)) return false;
+  return f == QMM_MXFP4_G32 ? (n >= 5120 || t <= 8) : n >= 8192;
+}
 
 // Workspace of qmm_gemm under kernel setting k (0 where the call runs no
 // kernel that takes one, or where it fails).
@@ -94,6 +109,7 @@ size_t gemm_ws_bytes(int k, int f, int64_t t, int64_t n, int64_t d, const qmm::L
   }
   if (t < 2) return 0;
   if (k == QMM_KERNEL_FEW_ROW) return qmm::skinny_fits(t, n, d, l) ? qmm::skinny_workspace_bytes(t, n, d) : 0;
+  if (k == QMM_KERNEL_MULTI_ROW || uses_mrow(k, f, t, n, d, l)) return 0;
   return qmm::skinny_fits(t, n, d, l) ? qmm::skinny_workspace_bytes(t, n, d)
                                       : size_t(qmm::tile_ws_layout(f, t, n, d, l).total);
 }
@@ -128,7 +144,7 @@ size_t qmm_workspace_bytes(qmm_format f, int64_t t, int64_t n, int64_t d) {
 
 qmm_status qmm_set_kernel(qmm_kernel k) {
   g_last_error[0] = 0;
-  if (k < QMM_KERNEL_AUTO || k > QMM_KERNEL_GROUPED_MATMUL) return fail(QMM_E_ARG, "unknown kernel setting");
+  if (k < QMM_KERNEL_AUTO || k > QMM_KERNEL_MULTI_ROW) return fail(QMM_E_ARG, "unknown kernel setting");
   forced_kernel();   // the environment is consumed first, so it cannot override this later
   g_kernel.store(int(k), std::memory_order_relaxed);
   return QMM_OK;
@@ -282,6 +298,8 @@ qmm_status gemm_impl(const char* name, bool noalloc, qmm_format f, const void* p
   if ((st = check_kernel(&kf))) return st;
   if (kf == QMM_KERNEL_FEW_ROW && !qmm::skinny_fits(t, n, d, l))
     return fail(QMM_E_UNSUPPORTED, "the few-row kernel takes 2 <= t <= 64 rows (kernel forced to few_row)");
+  if (kf == QMM_KERNEL_MULTI_ROW && !qmm::mrow_fits(f, t, n, d, l))
+    return fail(QMM_E_UNSUPPORTED, "the multi-row kernel takes 2 <= t <= 16 rows whose padded rows fit in 160 KiB of LDS (kernel forced to multi_row)");
   const size_t need = gemm_ws_bytes(kf, f, t, n, d, l);
   if (noalloc) {
     if (need > qmm::kNoAllocScratchBytes)
@@ -296,11 +314,6 @@ qmm_status gemm_impl(const char* name, bool noalloc, qmm_format f, const void* p
   }
   if ((st = check_ws(need, ws, ws_bytes))) return st;
   if (t == 1 && !forces_tile(kf)) return qmm_gemv(f, packed, n, d, x, y, nullptr, 0, stream);
-  if (f == QMM_AFFINE4_G64 && !ws)
-    return fail(QMM_E_WORKSPACE, "affine weights on the matmul kernels need a workspace of qmm_workspace_bytes() bytes");
-  if (kf == QMM_KERNEL_FEW_ROW && !ws)
-    return fail(QMM_E_WORKSPACE, "the few-row kernel needs a workspace of qmm_workspace_bytes() bytes");
-  if (need && ws && !aligned(ws, 16)) return fail(QMM_E_ALIGN, "ws must be 16-byte aligned");
   qmm::GemmArgs a{};
   a.f = f;
   a.packed = static_cast<const uint8_t*>(packed);
@@ -309,6 +322,16 @@ qmm_status gemm_impl(const char* name, bool noalloc, qmm_format f, const void* p
   a.d = int(d);
   a.x = x;
   a.y = y;
+  if (uses_mrow(kf, f, t, n, d, l)) {
+    const int err = qmm::launch_mrow(a, stream);
+    if (err) return hip_fail(err, name);
+    return QMM_OK;
+  }
+  if (f == QMM_AFFINE4_G64 && !ws)
+    return fail(QMM_E_WORKSPACE, "affine weights on the matmul kernels need a workspace of qmm_workspace_bytes() bytes");
+  if (kf == QMM_KERNEL_FEW_ROW && !ws)
+    return fail(QMM_E_WORKSPACE, "the few-row kernel needs a workspace of qmm_workspace_bytes() bytes");
+  if (need && ws && !aligned(ws, 16)) return fail(QMM_E_ALIGN, "ws must be 16-byte aligned");
   // the tile kernel is told only the workspace bytes it may use: without the
   // K-split planes when it must not split
   const size_t tile_bytes = kf == QMM_KERNEL_TILE_UNSPLIT ? need : ws_bytes;

@@ -1,0 +1,54 @@
+// Launcher of the multi-row GEMV (qmm_mrow.hip): Y = X·Ŵᵀ for a few rows,
+// every weight byte read once, the rows held whole in LDS.
+#pragma once
+
+#include <stddef.h>
+
+#include "qmm_internal.h"
+
+namespace qmm {
+
+constexpr int kMrowMaxT = 16;                     // rows per launch: one 16-row MFMA block
+constexpr size_t kMrowMaxLds = size_t(160) << 10; // the LDS of one compute unit
+
+constexpr int kMrowMaxWaves = 8;                  // waves per workgroup (512 threads)
+constexpr size_t kMrowRedBytes = size_t(6) << 10;  // LDS for the partial sums: (kq − 1)·ncw ≤ 6 waves
+
+// Launch shape: `groups` workgroups, a multiple of the CU count (one resident
+// per CU), each taking cpw <= 128 consecutive columns with ncw column waves
+// (16 columns each) times kq wave groups that share out the slabs of d, kq as
+// large as 8 waves allow (and no larger than the slab count).
+struct MrowPlan {
+  int64_t groups;
+  int cpw, ncw, kq;
+};
+inline MrowPlan mrow_plan(int64_t n, int64_t d, int cus) {
+  const int64_t ns = (d + kSlabCodes - 1) / kSlabCodes;
+  MrowPlan p;
+  p.groups = (n + int64_t(cus) * 128 - 1) / (int64_t(cus) * 128) * cus;
+  p.cpw = int((n + p.groups - 1) / p.groups);
+  p.ncw = (p.cpw + 15) / 16;
+  p.kq = ns >= 4 && 4 * p.ncw <= kMrowMaxWaves ? 4 : ns >= 2 && 2 * p.ncw <= kMrowMaxWaves ? 2 : 1;
+  return p;
+}
+
+// LDS of one workgroup: the t rows padded to whole 512-code slabs (bf16);
+// for affine weights the sums of 16 rows (zeros past t) over each 64-code
+// group (fp32); the partial sums of the wave groups past the first.
+inline size_t mrow_lds_bytes(int f, int64_t t, int64_t d) {
+  const int64_t rs = (d + kSlabCodes - 1) / kSlabCodes * kSlabCodes;
+  return size_t(t * rs * 2 + (f == QMM_AFFINE4_G64 ? (rs / 64) * 16 * 4 : 0)) + kMrowRedBytes;
+}
+
+// Whether the kernel takes this shape: 2 <= t <= 16, the rows fit in LDS,
+// and the 32-bit buffer offsets cover the codes, metadata and activations.
+inline bool mrow_fits(int f, int64_t t, int64_t n, int64_t d, const Layout& l) {
+  return t >= 2 && t <= kMrowMaxT && mrow_lds_bytes(f, t, d) <= kMrowMaxLds &&
+         n * (d / 2) < (int64_t(1) << 31) && l.meta_bytes < (int64_t(1) << 31) &&
+         t * d * 2 < (int64_t(1) << 31);
+}
+
+// Y = X·Ŵᵀ for a shape mrow_fits accepts; no workspace.
+int launch_mrow(const GemmArgs& a, void* stream);
+
+}  // namespace qmm

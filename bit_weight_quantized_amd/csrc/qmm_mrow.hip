@@ -1,0 +1,266 @@
+// Multi-row GEMV: Y = X·Ŵᵀ for 2 <= T <= 16 activation rows (a batch of
+// decode tokens), the product of "Kapitsa 源码拆解 02：权重、矩阵与 Metal",
+// section "矩阵乘法中数据和参数", at a size where every weight byte is read once
+// and serves all T rows, with no partial sums in memory and no second kernel.
+//
+// Work split.  The columns are dealt out evenly to a multiple of the CU count
+// of workgroups (one resident per CU), at most 128 columns each.  A wave owns
+// 16 columns; the workgroup's column waves are repeated kq times (8 waves in
+// all), wave group kq taking slabs kq, kq + KQ, ... of d with two slabs in
+// flight per lane, and the groups' partial sums meet in LDS in a fixed order.
+// Each workgroup first copies the T activation rows (zeros past d, padded to
+// whole slabs) to LDS by DMA, 16-byte pieces swizzled within each 256-byte
+// group so that the 16 rows of one MFMA operand read sit in distinct banks.
+// The rows enter v_mfma_f32_16x16x32_bf16 as its 16-row A operand (rows past
+// T read row T - 1 and their outputs are dropped); lane (column c, chunk g)
+// loads the 32-code chunk g of each 128-code step of its column.
+//
+// Affine weights enter as the exact bf16 values 128 + q and each 64-code
+// group's scale and bias follow in fp32: s·Σx(128 + q) + (b − 128·s)·Σx, with
+// Σx per row and group summed once per workgroup.  A step's two groups are
+// kept apart by regrouping the loaded words across lanes (v_permlane32_swap)
+// so that every MFMA sees one group.  MXFP4 weights convert exactly to bf16
+// with their E8M0 scale.  No weight is rounded.
+#include <hip/hip_runtime.h>
+
+#include "qmm_device.h"
+#include "qmm_internal.h"
+#include "qmm_launch.h"
+#include "qmm_lds_copy.h"
+#include "qmm_mrow.h"
+
+namespace qmm {
+namespace {
+
+constexpr uint32_t kOOB = 0x80000000u;   // OR-ed into a buffer offset: past every range
+constexpr int kMrRing = 2;               // slabs in flight per lane
+
+// element offset of 16-byte piece c of row r (row stride rs elements)
+__device__ __forceinline__ int mr_at(int r, int rs, int c) { return r * rs + ((c ^ (r & 15)) << 3); }
+
+template <int FMT, int KQ>
+__global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t* __restrict__ codes,
+                                                   const uint8_t* __restrict__ meta,
+                                                   uint32_t codes_bytes, uint32_t meta_bytes, int t,
+                                                   int n, int d, int cpw, int ncw,
+                                                   const uint16_t* __restrict__ x,
+                                                   uint16_t* __restrict__ y) {
+  constexpr bool AFF = FMT == QMM_AFFINE4_G64;
+  constexpr int MP = AFF ? 2 : 1;   // 16-byte metadata pieces of one column per slab
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  const Slabs L{n, d, FMT};
+  const int ns = L.count();
+  const int rs = ns * kSlabCodes;   // LDS row stride in elements (rows padded to whole slabs)
+  const int ng = ns * 8;            // 64-code groups per padded row
+  float* xsum = reinterpret_cast<float*>(xs + t * rs);   // [ng][16 rows] (affine; rows past t zero)
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(xsum + (AFF ? ng * 16 : 0));   // [KQ - 1][ncw][64]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nw = ncw * KQ;                    // waves in the workgroup
+  const int cw = wave % ncw, kq = wave / ncw;   // column block of the wave, its share of the slabs
+  const int col_l = lane & 15, g = lane >> 4;
+  // the workgroup's columns [c0, c1), at most 16·ncw: wave cw takes c0 + 16cw ..
+  // c0 + 16cw + 15; a lane past c1 re-reads column c1 - 1 and stores nothing,
+  // a wave wholly past it loads nothing
+  const int c0 = blockIdx.x * cpw, c1 = min(c0 + cpw, n);
+  const int col = c0 + 16 * cw + col_l;
+  const int lcol = min(col, c1 - 1);
+  const bool active = 16 * cw < c1 - c0;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, codes_bytes);
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(meta, meta_bytes);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, uint32_t(t) * uint32_t(d) * 2u);
+
+  // 1. the activation rows to LDS by DMA, no registers involved: copy i of
+  //    the workgroup fills LDS bytes [1024i, 1024i + 1024), lane l slot
+  //    q = 64i + l, that is row r = q / (rs/8), position c' = q % (rs/8), which
+  //    holds piece c = c' ^ (r & 15) of the row (zeros past d)
+  const int prow = rs / 8;   // 16-byte pieces per row, a multiple of 64
+  const uint32_t xbase = lds_addr(xs);
+  for (int i = wave; i < t * prow / 64; i += nw) {
+    const int q = 64 * i + lane, r = q / prow, c = (q - r * prow) ^ (r & 15);
+    copy16_to_lds(xrs, 8 * c < d ? (uint32_t(r) * uint32_t(d) + 8u * uint32_t(c)) * 2u : kOOB,
+                  xbase + 1024u * uint32_t(i));
+  }
+
+  // 2. the code ring over the wave's slabs kq, kq + KQ, kq + 2KQ, ...: slab
+  //    s's four pieces (step j: codes 128j + 32g .. +31 of the slab) and its
+  //    metadata, issued in the order they are used
+  u32x4_t rc[kMrRing][4];
+  u32x4_t rm[kMrRing][MP];
+  auto issue = [&](u32x4_t (&c4)[4], u32x4_t (&m)[MP], int s) {
+    const bool in = active && s < ns;
+    const int w = in ? L.width(s) : 0;
+    const uint32_t cb = in ? uint32_t(L.codes(s, lcol)) : 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = 128 * j + 32 * g;
+      c4[j] = buf_load16(crs, kk < w ? cb + uint32_t(kk >> 1) : kOOB);
+    }
+    const int mrow = in ? L.meta_row(s) : 0;
+    const uint32_t mb = in ? uint32_t(L.meta(s, lcol)) : 0u;
+#pragma unroll
+    for (int i = 0; i < MP; ++i) m[i] = buf_load16(mrs, 16 * i < mrow ? mb + 16u * uint32_t(i) : kOOB);
+  };
+#pragma unroll
+  for (int j = 0; j < kMrRing; ++j) issue(rc[j], rm[j], kq + j * KQ);
+
+  // 3. the wave's copies landed: they were issued before the ring, so the
+  //    wait the compiler places for the first slab (its own loads, which it
+  //    counts) covers them; then every wave's copies are visible
+  asm volatile("" ::"v"(rc[0][0]), "v"(rc[0][1]), "v"(rc[0][2]), "v"(rc[0][3]), "v"(rm[0][0]), "v"(rm[0][MP - 1]));
+  __syncthreads();
+  if constexpr (AFF) {
+    // each row's sum over each 64-code group (consecutive threads take
+    // consecutive rows of one group: their pieces sit in distinct banks)
+    for (int q = tid; q < ng * 16; q += 64 * nw) {
+      const int r = q & 15, gr = q >> 4;
+      float sum[4] = {0.f, 0.f, 0.f, 0.f};   // four chains: dword k of every piece
+      if (r < t) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&xs[mr_at(r, rs, 8 * gr + c)]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) sum[k] = (sum[k] + bf16_lo(v[k])) + bf16_hi(v[k]);
+        }
+      }
+      xsum[q] = (sum[0] + sum[1]) + (sum[2] + sum[3]);
+    }
+    __syncthreads();
+  }
+
+  // 4. the slabs: MFMA A operands from LDS (row col_l, clamped to the last
+  //    row), B operands from the ring
+  // (128 + q) pairs as (w & mask) | magic: one v_and_or_b32 that the compiler
+  // emits itself once the two constants sit in registers it cannot fold back
+  // into literals (an inline-asm v_and_or_b32 would get no wait states before
+  // the MFMA that reads its result)
+  uint32_t pmask, pmagic;
+  asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(pmask));
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(pmagic));
+  // the lane's A-operand pieces: piece 16k + p0 (p0 < 16) of row r sits at
+  // 16k + (p0 ^ (r & 15)), so each address is a per-lane base plus the
+  // step's uniform offset.  Affine: piece p0 = 8h + 4(g & 1) + 2 + jj − 2(g >> 1)
+  // of the step (see the regrouping below); MXFP4: p0 = 4g + j.
+  const int arow = min(col_l, t - 1);
+  int aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p0 = AFF ? 8 * (i >> 1) + 4 * (g & 1) + 2 + (i & 1) - 2 * (g >> 1) : 4 * g + i;
+    aoff[i] = arow * rs + ((p0 ^ (arow & 15)) << 3);
+  }
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto slab = [&](const u32x4_t (&c4)[4], const u32x4_t (&m)[MP], int s) {
+    const int w = L.width(s);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      if (128 * st >= w) break;   // a narrow last slab ends early (uniform)
+      const int e0 = (s * 64 + st * 16) * 8;   // the step's first activation element
+      if constexpr (AFF) {
+        // groups 2st and 2st + 1 of the slab: dwords 2st, 2st + 1 of the column's metadata
+        // (a last slab may end after group 2st: its second group's dword
+        // belongs to another column and is replaced by zero)
+        const uint32_t m0 = m[st >> 1][(2 * st) & 3];
+        const uint32_t m1 = 128 * st + 64 < w ? m[st >> 1][(2 * st + 1) & 3] : 0u;
+        const float gs0 = bf16_lo(m0), gc0 = __builtin_fmaf(-128.0f, bf16_lo(m0), bf16_hi(m0));
+        const float gs1 = bf16_lo(m1), gc1 = __builtin_fmaf(-128.0f, bf16_lo(m1), bf16_hi(m1));
+        // regroup the step's words so that each register holds one group in
+        // every lane: lanes 32..63 (chunks 2, 3: group 2st + 1) trade word J - 2
+        // for word J (J = 2, 3) of lanes 0..31 (chunks 0, 1: group 2st), the
+        // same column.  Then wg[0][*] is group 2st, wg[1][*] group 2st + 1, and
+        // lane g's word wg[h][J - 2] holds the codes of piece
+        // 8h + 4(g & 1) + J - 2(g >> 1) of the step.
+        const auto s20 = __builtin_amdgcn_permlane32_swap(c4[st][2], c4[st][0], false, false);
+        const auto s31 = __builtin_amdgcn_permlane32_swap(c4[st][3], c4[st][1], false, false);
+        const uint32_t wg[2][2] = {{s20[0], s31[0]}, {s20[1], s31[1]}};
+        f32x4_t pg[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            u32x4_t b;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) b[r] = ((wg[h][jj] >> (4 * r)) & pmask) | pmagic;
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xs[aoff[2 * h + jj] + e0]);
+            pg[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                            __builtin_bit_cast(bf16x8_t, b), pg[h], 0, 0, 0);
+          }
+        // the lane's rows 4g + r: acc += s·P + (b − 128·s)·Σx, group 2st then 2st + 1
+        const f32x4_t xg0 = *reinterpret_cast<const f32x4_t*>(&xsum[(s * 8 + 2 * st) * 16 + 4 * g]);
+        const f32x4_t xg1 = *reinterpret_cast<const f32x4_t*>(&xsum[(s * 8 + 2 * st + 1) * 16 + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = acc[r];
+          v = __builtin_fmaf(gs0, pg[0][r], v);
+          v = __builtin_fmaf(gc0, xg0[r], v);
+          v = __builtin_fmaf(gs1, pg[1][r], v);
+          v = __builtin_fmaf(gc1, xg1[r], v);
+          acc[r] = v;
+        }
+      } else {
+        // group 4st + g of the slab: byte 4st + g of the column's metadata
+        const float sc = e8m0_scale((m[0][st] >> (8 * g)) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xs[aoff[j] + e0]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                        __builtin_bit_cast(bf16x8_t, mxfp4_word_to_bf16x8(c4[st][j], sc)),
+                                                        acc, 0, 0, 0);
+        }
+      }
+    }
+  };
+  for (int s0 = kq; active && s0 < ns; s0 += kMrRing * KQ) {
+#pragma unroll
+    for (int j = 0; j < kMrRing; ++j) {
+      const int s = s0 + j * KQ;
+      if (s < ns) slab(rc[j], rm[j], s);
+      issue(rc[j], rm[j], s + kMrRing * KQ);
+    }
+  }
+
+  // 5. the KQ shares of each column block summed in order kq = 0, 1, ...;
+  //    lane holds column col, rows 4g .. 4g + 3
+  if constexpr (KQ > 1) {
+    if (kq > 0) red[((kq - 1) * ncw + cw) * 64 + lane] = acc;
+    __syncthreads();
+    if (kq > 0) return;
+#pragma unroll
+    for (int k = 1; k < KQ; ++k) acc += red[((k - 1) * ncw + cw) * 64 + lane];
+  }
+  if (col < c1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * g + r;
+      if (row < t) y[int64_t(row) * n + col] = f32_to_bf16(acc[r]);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_mrow(const GemmArgs& a, void* stream) {
+  Layout l;
+  if (!layout_of(a.f, a.n, a.d, &l)) return int(hipErrorInvalidValue);
+  if (!mrow_fits(a.f, a.t, a.n, a.d, l)) return int(hipErrorInvalidValue);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  DevInfo di{};
+  const int cus = device_info(&di) == 0 && di.cus > 0 ? di.cus : 256;
+  const MrowPlan p = mrow_plan(a.n, a.d, cus);
+  const dim3 grid(unsigned((a.n + p.cpw - 1) / p.cpw)), block(unsigned(64 * p.ncw * p.kq));
+  const size_t lds = mrow_lds_bytes(a.f, a.t, a.d);
+  const uint8_t* codes = a.packed + l.codes_offset;
+  const uint8_t* meta = a.packed + l.meta_offset;
+  const uint32_t cb = uint32_t(int64_t(a.n) * (a.d / 2)), mb = uint32_t(l.meta_bytes);
+  auto go = [&](auto kern) {
+    launch_kernel_lds(kern, grid, block, lds, s, codes, meta, cb, mb, a.t, a.n, a.d, p.cpw, p.ncw, a.x, a.y);
+  };
+  if (a.f == QMM_AFFINE4_G64)
+    p.kq == 4 ? go(mrow_kernel<QMM_AFFINE4_G64, 4>) : p.kq == 2 ? go(mrow_kernel<QMM_AFFINE4_G64, 2>) : go(mrow_kernel<QMM_AFFINE4_G64, 1>);
+  else
+    p.kq == 4 ? go(mrow_kernel<QMM_MXFP4_G32, 4>) : p.kq == 2 ? go(mrow_kernel<QMM_MXFP4_G32, 2>) : go(mrow_kernel<QMM_MXFP4_G32, 1>);
+  return int(hipGetLastError());
+}
+
+}  // namespace qmm

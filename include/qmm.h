@@ -91,17 +91,20 @@ size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
  * per format and shape by a call like this one, as the explicit per-format
  * byte counts that fixed the NULL-scale crash of "Colibri Kimi K3 Metal
  * 后端实现全解析", Phase 10 (fmt_scale_bytes).
- *   2 <= t <= 64 rows: one fp32 [t][n] plane per 512-code slab of d,
- *     ceil(d/512)·t·n·4 bytes (2.2 MB for t = 4, n = 13824, d = 5120).
+ *   2 <= t <= 16 rows on the multi-row kernel (see qmm_gemm: MXFP4 weights
+ *     with n >= 5120 or t <= 8, affine weights with n >= 8192, while the t
+ *     rows fit the kernel's LDS): 0.
+ *   other 2 <= t <= 64 rows: one fp32 [t][n] plane per 512-code slab of d,
+ *     ceil(d/512)·t·n·4 bytes (0.66 MB for t = 4, n = 4096, d = 5120).
  *   t > 64, affine weights: the activations converted to fp16 (t·d·2 bytes),
  *     one int32 exponent per row and per weight column, each rounded up to
  *     256 bytes (21.0 MB for t = 2048, n = 13824, d = 5120), plus, while the
  *     tile kernel has few tiles (128-row tiles over at most 128 workgroups)
  *     and d is a multiple of 512, up to four K-split planes of t·n·4 bytes.
  *   t > 64, MXFP4 weights: those K-split planes, else 0.
- * Affine weights with t >= 2 REQUIRE this workspace (QMM_E_WORKSPACE without
- * one).  For MXFP4 it is optional: ws = NULL runs the tile kernel, several
- * times slower for 2 <= t <= 64.  A non-NULL ws must be 16-byte aligned and
+ * Affine weights REQUIRE this workspace where it is not 0 (QMM_E_WORKSPACE
+ * without one).  For MXFP4 it is optional: ws = NULL runs the tile kernel,
+ * several times slower for 2 <= t <= 64.  A non-NULL ws must be 16-byte aligned and
  * hold at least this many bytes (QMM_E_ALIGN, QMM_E_WORKSPACE).  Its contents
  * on entry do not matter, and calls sharing one workspace must be ordered on
  * one stream.  Under a forced kernel (qmm_set_kernel) the size is that
@@ -166,10 +169,17 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
  * activation rows share each weight read, unlike the one-row decode).
  *   x bf16[t][d] row-major; y bf16[t][n] row-major (written whole);
  *   ws, ws_bytes: the workspace of qmm_workspace_bytes(f, t, n, d), required
- *   for affine weights with t >= 2 (see there), optional for MXFP4.
+ *   for affine weights where that is not 0 (see there), optional for MXFP4.
  * t = 1 runs the GEMV kernel.  Otherwise MFMA with fp32 accumulation, every
  * output rounded once to bf16:
- *   2 <= t <= 64 (with the workspace): split along d, each 512-code slab's
+ *   2 <= t <= 16, multi-row kernel (MXFP4 weights with n >= 5120 or t <= 8,
+ *     affine weights with n >= 8192, while its LDS fits 160 KiB: the t rows
+ *     padded to whole 512-code slabs, t·ceil(d/512) KiB, plus 6 KiB, plus
+ *     ceil(d/512)/2 KiB for affine weights; at d = 5120 affine t <= 14,
+ *     MXFP4 t <= 15): every
+ *     weight read once for all rows, no workspace, one kernel.  Affine codes enter bf16 MFMAs as the exact
+ *     values 128 + q and each group's scale and bias follow in fp32.
+ *   other 2 <= t <= 64 (with the workspace): split along d, each 512-code slab's
  *     fp32 partial sums in the workspace, added in slab order by a second
  *     kernel.  Affine codes enter bf16 MFMAs as the exact values 128 + q and
  *     each group's scale and bias follow in fp32, so no weight is rounded.
@@ -336,13 +346,18 @@ qmm_status qmm_profile_next(void* start_event, void* stop_event);
  *                              workspace for both formats.
  *   QMM_KERNEL_GROUPED_MATMUL  qmm_grouped_gemm runs the matmul kernel also
  *                              where every segment has one row.
+ *   QMM_KERNEL_MULTI_ROW       qmm_gemm runs the multi-row kernel for every
+ *                              shape it takes (2 <= t <= 16, rows within its
+ *                              LDS), others return QMM_E_UNSUPPORTED; no
+ *                              workspace.
  * A setting that does not concern a call leaves it as under AUTO.
  * qmm_workspace_bytes reports the workspace of the kernel the setting
  * selects, so size workspaces after changing it.  The setting is
  * process-wide and takes effect for calls that start after it returns.  Its
  * initial value comes from the environment variable QMM_FORCE_KERNEL, read
  * once at the first call that consults it: unset, "" or "auto", "tile",
- * "tile_unsplit", "few_row", "grouped_matmul", or the digits 0..4.  Any other
+ * "tile_unsplit", "few_row", "grouped_matmul", "multi_row", or the digits
+ * 0..5.  Any other
  * value makes qmm_gemm, qmm_gemm_noalloc and the grouped calls fail with
  * QMM_E_ARG (a mistyped switch is reported, not ignored) until qmm_set_kernel
  * is called.  qmm_set_kernel returns QMM_E_ARG for a value outside the enum;
@@ -353,7 +368,8 @@ typedef enum {
   QMM_KERNEL_TILE = 1,
   QMM_KERNEL_TILE_UNSPLIT = 2,
   QMM_KERNEL_FEW_ROW = 3,
-  QMM_KERNEL_GROUPED_MATMUL = 4
+  QMM_KERNEL_GROUPED_MATMUL = 4,
+  QMM_KERNEL_MULTI_ROW = 5
 } qmm_kernel;
 qmm_status qmm_set_kernel(qmm_kernel k);
 int qmm_get_kernel(void);

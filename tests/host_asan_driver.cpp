@@ -48,6 +48,7 @@ int read_header(const void*, PackedHeader* h, void*) {
 }
 int launch_route(const RouteArgs&, void*) { return reach("route"); }
 int launch_skinny(const GemmArgs&, float* ws, void*) { g_ws = ws; return reach("skinny"); }
+int launch_mrow(const GemmArgs&, void*) { return reach("mrow"); }
 int launch_combine(const CombineArgs&, void*) { return reach("combine"); }
 int launch_gemm_ws(const GemmArgs&, float* ws, size_t bytes, void*) {
   g_ws = ws;
@@ -103,11 +104,21 @@ int main() {
 
   // GEMM: kernel selection by t and workspace
   EXPECT(qmm_gemm(A, P(), 1, 16, 64, B(), B(), nullptr, 0, nullptr) == QMM_OK && g_called == "gemv");
-  const size_t need8 = qmm_workspace_bytes(A, 8, 13824, 5120);
-  EXPECT(need8 == size_t(10) * 8 * 13824 * 4);
-  EXPECT(qmm_gemm(A, P(), 8, 13824, 5120, B(), B(), P(), need8, nullptr) == QMM_OK && g_called == "skinny");
-  EXPECT(qmm_gemm(A, P(), 8, 13824, 5120, B(), B(), P(), need8 - 1, nullptr) == QMM_E_WORKSPACE);
-  EXPECT(qmm_gemm(A, P(), 8, 13824, 5120, B(), B(), P(8), need8, nullptr) == QMM_E_ALIGN);
+  // a few rows on a wide matrix: the multi-row kernel, no workspace (one
+  // passed is ignored)
+  EXPECT(qmm_workspace_bytes(A, 8, 13824, 5120) == 0);
+  EXPECT(qmm_gemm(A, P(), 8, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow");
+  EXPECT(qmm_gemm(A, P(), 8, 13824, 5120, B(), B(), P(8), 16, nullptr) == QMM_OK && g_called == "mrow");
+  EXPECT(qmm_gemm(M, P(), 4, 1024, 5120, B(), B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow");
+  g_fail = 1;   // a launch error is reported as a HIP status
+  EXPECT(qmm_gemm(A, P(), 8, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_E_HIP);
+  // narrower: the few-row split-K kernel through the workspace
+  const size_t need8 = qmm_workspace_bytes(A, 8, 4096, 5120);
+  EXPECT(need8 == size_t(10) * 8 * 4096 * 4);
+  EXPECT(qmm_gemm(A, P(), 8, 4096, 5120, B(), B(), P(), need8, nullptr) == QMM_OK && g_called == "skinny");
+  EXPECT(qmm_gemm(A, P(), 8, 4096, 5120, B(), B(), P(), need8 - 1, nullptr) == QMM_E_WORKSPACE);
+  EXPECT(qmm_gemm(A, P(), 8, 4096, 5120, B(), B(), P(8), need8, nullptr) == QMM_E_ALIGN);
+  EXPECT(qmm_gemm(A, P(), 8, 4096, 5120, B(), B(), nullptr, 0, nullptr) == QMM_E_WORKSPACE);
   g_called = "none";
   EXPECT(qmm_gemm(A, P(), 0, 16, 64, B(), B(), nullptr, 0, nullptr) == QMM_E_ARG && g_called == "none");
   EXPECT(qmm_gemm(A, P(), (int64_t(1) << 24) + 1, 16, 64, B(), B(), nullptr, 0, nullptr) == QMM_E_SHAPE);
@@ -127,11 +138,21 @@ int main() {
   g_called = "none";
   EXPECT(qmm_gemm_noalloc(A, P(), 64, 65536, 5120, B(), B(), nullptr) == QMM_E_WORKSPACE && g_called == "none");
   EXPECT(strstr(qmm_last_error(), "64 MiB") != nullptr);
-  EXPECT(qmm_gemm_noalloc(A, P(), 8, 13824, 5120, B(), B(), nullptr) == QMM_OK && g_called == "skinny");
+  EXPECT(qmm_gemm_noalloc(A, P(), 8, 13824, 5120, B(), B(), nullptr) == QMM_OK && g_called == "mrow");
+  EXPECT(qmm_gemm_noalloc(A, P(), 8, 4096, 5120, B(), B(), nullptr) == QMM_OK && g_called == "skinny");
   EXPECT(g_ws == g_scratch);
   g_fail = 1;   // the scratch lookup fails: a HIP status, with the HIP text
-  EXPECT(qmm_gemm_noalloc(A, P(), 8, 13824, 5120, B(), B(), nullptr) == QMM_E_HIP);
+  EXPECT(qmm_gemm_noalloc(A, P(), 8, 4096, 5120, B(), B(), nullptr) == QMM_E_HIP);
   EXPECT(strstr(qmm_last_error(), "qmm_gemm_noalloc") != nullptr);
+  // the multi-row kernel forced: narrow matrices too; shapes it does not
+  // take are refused before any launch
+  EXPECT(qmm_set_kernel(QMM_KERNEL_MULTI_ROW) == QMM_OK);
+  EXPECT(qmm_gemm(A, P(), 8, 1024, 5120, B(), B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow");
+  g_called = "none";
+  EXPECT(qmm_gemm(A, P(), 17, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_E_UNSUPPORTED && g_called == "none");
+  EXPECT(qmm_gemm(A, P(), 15, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_E_UNSUPPORTED && g_called == "none");
+  EXPECT(strstr(qmm_last_error(), "multi-row") != nullptr);
+  EXPECT(qmm_set_kernel(QMM_KERNEL_AUTO) == QMM_OK);
 
   // a launch failure is reported as QMM_E_HIP with the HIP text appended
   g_fail = 1;

@@ -60,9 +60,18 @@ def test_packed_bytes_rejects_bad_shapes():
 
 
 def test_workspace_contract():
-    # split-K partials of qmm_gemm for 2 <= t <= 64: one fp32 [t][n] plane per
-    # 512-code slab of d; nothing for other t or invalid shapes
-    assert qmm.qmm_workspace_bytes(A, 2, 13824, 5120) == 10 * 2 * 13824 * 4
+    # the multi-row kernel (2 <= t <= 16, rows within its LDS; MXFP4 from 5120
+    # columns or up to 8 rows, affine from 8192 columns) takes none
+    assert qmm.qmm_workspace_bytes(A, 2, 13824, 5120) == 0
+    assert qmm.qmm_workspace_bytes(A, 14, 13824, 5120) == 0
+    assert qmm.qmm_workspace_bytes(M, 8, 1024, 5120) == 0
+    assert qmm.qmm_workspace_bytes(M, 15, 5120, 5120) == 0
+    # split-K partials of qmm_gemm for the other 2 <= t <= 64: one fp32 [t][n]
+    # plane per 512-code slab of d; nothing for other t or invalid shapes
+    assert qmm.qmm_workspace_bytes(A, 2, 4096, 5120) == 10 * 2 * 4096 * 4
+    assert qmm.qmm_workspace_bytes(A, 15, 13824, 5120) == 10 * 15 * 13824 * 4   # 15 rows exceed its LDS
+    assert qmm.qmm_workspace_bytes(M, 12, 1024, 5120) == 10 * 12 * 1024 * 4
+    assert qmm.qmm_workspace_bytes(A, 17, 13824, 5120) == 10 * 17 * 13824 * 4
     assert qmm.qmm_workspace_bytes(M, 64, 300, 1088) == 3 * 64 * 300 * 4
     for t in (1, 2048, 300):
         assert qmm.qmm_workspace_bytes(M, t, 13824, 5120) == 0
@@ -115,10 +124,10 @@ def test_kernel_override_sizes_and_refusals(kernel_auto_after):
     not take is refused on the host."""
     lib = qmm.load()
     up = lambda v: -(-v // 256) * 256
-    assert lib.qmm_set_kernel(5) == E_ARG and lib.qmm_set_kernel(-1) == E_ARG
+    assert lib.qmm_set_kernel(6) == E_ARG and lib.qmm_set_kernel(-1) == E_ARG
     assert qmm.qmm_get_kernel() == qmm.QMM_KERNEL_AUTO
     skinny4 = 10 * 4 * 13824 * 4
-    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == skinny4
+    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == 0                 # the multi-row kernel
     tile_aff = lambda t: up(t * 5120 * 2) + up(t * 4) + 13824 * 4
     qmm.qmm_set_kernel(qmm.QMM_KERNEL_TILE)
     assert qmm.qmm_get_kernel() == qmm.QMM_KERNEL_TILE
@@ -138,15 +147,26 @@ def test_kernel_override_sizes_and_refusals(kernel_auto_after):
     assert lib.qmm_gemm(A, P, 1, 16, 64, P, P, P, 1 << 20, None) == E_UNSUPPORTED
     assert "few-row" in qmm.qmm_last_error()
     assert lib.qmm_gemm(M, P, 4, 16, 64, P, P, None, 0, None) == E_WS     # few-row needs one for MXFP4 too
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_MULTI_ROW)
+    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == 0
+    assert qmm.qmm_workspace_bytes(A, 4, 1024, 5120) == 0                  # narrow matrices too
+    assert qmm.qmm_workspace_bytes(A, 17, 13824, 5120) == 0                # refused below
+    assert lib.qmm_gemm(A, P, 17, 16, 64, P, P, None, 0, None) == E_UNSUPPORTED
+    assert "multi-row" in qmm.qmm_last_error()
+    assert lib.qmm_gemm(A, P, 1, 16, 64, P, P, None, 0, None) == E_UNSUPPORTED
+    assert lib.qmm_gemm(A, P, 15, 16, 5120, P, P, None, 0, None) == E_UNSUPPORTED   # rows beyond its LDS
+    assert lib.qmm_gemm_noalloc(A, P, 17, 16, 64, P, P, None) == E_UNSUPPORTED
     qmm.qmm_set_kernel(qmm.QMM_KERNEL_GROUPED_MATMUL)
-    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == skinny4           # no effect on qmm_gemm
+    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == 0                 # no effect on qmm_gemm
+    assert qmm.qmm_workspace_bytes(A, 4, 4096, 5120) == 10 * 4 * 4096 * 4
     qmm.qmm_set_kernel(qmm.QMM_KERNEL_AUTO)
-    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == skinny4
+    assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == 0
+    assert qmm.qmm_workspace_bytes(A, 4, 4096, 5120) == 10 * 4 * 4096 * 4
 
 
 @pytest.mark.parametrize("value,want", [("tile", 1), ("tile_unsplit", 2), ("few_row", 3),
-                                        ("grouped_matmul", 4), ("4", 4), ("auto", 0), ("", 0),
-                                        ("Tile", -1), ("fast", -1)])
+                                        ("grouped_matmul", 4), ("4", 4), ("multi_row", 5), ("5", 5),
+                                        ("auto", 0), ("", 0), ("Tile", -1), ("fast", -1), ("6", -1)])
 def test_kernel_override_from_the_environment(value, want):
     """QMM_FORCE_KERNEL sets the initial value; an unknown one makes the
     matmul calls fail with QMM_E_ARG until qmm_set_kernel is called."""

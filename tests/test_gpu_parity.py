@@ -358,6 +358,21 @@ def run_gemm(fmt, packed, n, d, x_bits):
     return host_u16(y)
 
 
+def run_gemm_tile(fmt, packed, n, d, x_bits):
+    """qmm_gemm on the tile kernel (forced), with the workspace it asks for."""
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_TILE)
+    try:
+        t = x_bits.shape[0]
+        need = qmm.qmm_workspace_bytes(fmt, t, n, d)
+        ws = guarded((need // 4,), float("nan"), torch.float32) if need else None
+        y = nan_out(t, n)
+        qmm.qmm_gemm(fmt, packed, t, n, d, dev(x_bits), y, ws)
+        torch.cuda.synchronize()
+    finally:
+        qmm.qmm_set_kernel(qmm.QMM_KERNEL_AUTO)
+    return host_u16(y)
+
+
 @pytest.mark.parametrize("t,n,d", [(2, 5, 64), (3, 300, 320), (130, 257, 576), (129, 512, 1024),
                                    (300, 520, 640), (257, 256, 256), (513, 100, 5120),
                                    # d a multiple of 512 (whole-region weight descriptors), both
@@ -460,9 +475,10 @@ def test_grouped_long_reduction(fmt, d):
 def test_gemm_random_shapes(seed):
     """Seeded random shapes across the GEMM's paths, two per (path, format):
     the GEMV (t = 1), the split-K kernel (2 <= t <= 64 with a workspace), for
-    the same t without one the MXFP4 tile kernel (affine weights always take
-    their workspace), and t > 64 with a workspace (the tile kernel, split along
-    K when its tiles are few); d a multiple of 512 or ending in a narrow slab
+    the same t without one the MXFP4 multi-row kernel (t <= 8 where its LDS
+    holds the rows) or tile kernel (affine weights always take their
+    workspace), and t > 64 with a workspace (the tile kernel, split along K
+    when its tiles are few); d a multiple of 512 or ending in a narrow slab
     (MXFP4 also in a half K step), n and t ragged."""
     rng = np.random.default_rng(900 + seed)
     fmt = A if (seed // 4) % 2 == 0 else M
@@ -492,12 +508,13 @@ def test_gemm_random_shapes(seed):
 
 def test_mxfp4_e8m0_range_limits():
     """E8M0 252 (the largest exponent at which every MXFP4 weight is a finite
-    bf16): the GEMV, the tile GEMM, the split-K GEMM and the grouped kernels all
-    pass parity, with activations small enough that the outputs stay finite.
-    E8M0 253 with codes of magnitude 4 and 6 (weights of 2^128 and 1.5·2^128,
-    beyond bf16 and fp32): the GEMV, which scales its fp32 chunk sums, still
-    passes; the MFMA paths, whose operands are bf16 weights, cannot represent
-    that row (its values are recorded, not checked) and pass on the others."""
+    bf16): the GEMV, the multi-row, tile and split-K GEMMs and the grouped
+    kernels all pass parity, with activations small enough that the outputs
+    stay finite.  E8M0 253 with codes of magnitude 4 and 6 (weights of 2^128
+    and 1.5·2^128, beyond bf16 and fp32): the GEMV, which scales its fp32
+    chunk sums, still passes; the MFMA paths, whose operands are bf16 weights,
+    cannot represent that row (its values are recorded, not checked) and pass
+    on the others."""
     say("mxfp4 E8M0 252 / 253")
     n, d, t = 40, 128, 3
     w = rand_mxfp4(9400, n, d)
@@ -507,7 +524,8 @@ def test_mxfp4_e8m0_range_limits():
     yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
     assert np.all(np.isfinite(yr)) and np.max(np.abs(yr)) > 2.0 ** 100
     assert_parity(run_gemv(M, p, w, x[0]), yr[0], ar[0], "gemv E8M0 252")
-    assert_parity(run_gemm(M, p, n, d, x), yr, ar, "gemm E8M0 252")
+    assert_parity(run_gemm_multi_row(M, p, n, d, x), yr, ar, "gemm multi-row E8M0 252")
+    assert_parity(run_gemm_tile(M, p, n, d, x), yr, ar, "gemm tile E8M0 252")
     assert_parity(run_gemm_split(M, p, n, d, x), yr, ar, "gemm split-k E8M0 252")
     stk, size = stack(M, [w])
     yg = run_grouped(M, stk, size, 1, n, d, x, [0], [0, t], np.arange(t), t)
@@ -520,10 +538,11 @@ def test_mxfp4_e8m0_range_limits():
     yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
     assert np.all(np.isfinite(yr))
     assert_parity(run_gemv(M, p, w, x[0]), yr[0], ar[0], "gemv E8M0 253")
-    yg = run_gemm(M, p, n, d, x)
-    say("gemm E8M0 253 row 0 (weights beyond bf16, not checked):", oracle.bf16_to_f64(yg[:, 0]).tolist(),
-        "exact:", yr[:, 0].tolist())
-    assert_parity(yg[:, 1:], yr[:, 1:], ar[:, 1:], "gemm E8M0 253, other rows")
+    for name, run in (("multi-row", run_gemm_multi_row), ("tile", run_gemm_tile), ("split-k", run_gemm_split)):
+        yg = run(M, p, n, d, x)
+        say(f"gemm {name} E8M0 253 row 0 (weights beyond bf16, not checked):",
+            oracle.bf16_to_f64(yg[:, 0]).tolist(), "exact:", yr[:, 0].tolist())
+        assert_parity(yg[:, 1:], yr[:, 1:], ar[:, 1:], f"gemm {name} E8M0 253, other rows")
 
 
 def halfway_affine(n, d):
@@ -556,12 +575,14 @@ def halfway_x(t, d):
 
 
 @pytest.mark.parametrize("t,n,d", [(1, 300, 1024), (8, 300, 1024), (20, 300, 1024), (40, 300, 1024),
-                                   (100, 600, 1024), (130, 300, 576), (300, 520, 5120), (2048, 4352, 512)])
+                                   (100, 600, 1024), (130, 300, 576), (300, 520, 5120), (2048, 4352, 512),
+                                   (8, 9000, 1024), (16, 8200, 2048)])
 def test_affine_weights_not_rounded(t, n, d):
     """Weights exactly halfway between two bf16 numbers, activations signed so
     that rounding them would add up: bf16 operands land at 1.94x the
-    tolerance.  Every affine matmul path (GEMV, few-row kernel with one, two
-    and four row blocks, tile kernel split and unsplit) must stay within it."""
+    tolerance.  Every affine matmul path (GEMV, multi-row kernel, few-row
+    kernel with one, two and four row blocks, tile kernel split and unsplit)
+    must stay within it."""
     say("affine halfway weights", t, n, d)
     w, q_dn, q_up = halfway_affine(n, d)
     x = halfway_x(t, d)
@@ -603,15 +624,21 @@ def test_gemm_integer_exact():
 
 
 def run_gemm_split(fmt, packed, n, d, x_bits):
-    """qmm_gemm with the workspace that enables the split-K path (2 <= t <= 64),
-    NaN-filled first: its contents on entry must not matter."""
-    t = x_bits.shape[0]
-    need = qmm.qmm_workspace_bytes(fmt, t, n, d)
-    assert need == -(-d // 512) * t * n * 4
-    ws = guarded((need // 4,), float("nan"), torch.float32)
-    y = nan_out(t, n)
-    qmm.qmm_gemm(fmt, packed, t, n, d, dev(x_bits), y, ws)
-    torch.cuda.synchronize()
+    """qmm_gemm on the few-row split-K kernel (2 <= t <= 64; forced, since a
+    wide enough matrix or few enough MXFP4 rows would take the multi-row
+    kernel), with its workspace NaN-filled first: its contents on entry must
+    not matter."""
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_FEW_ROW)
+    try:
+        t = x_bits.shape[0]
+        need = qmm.qmm_workspace_bytes(fmt, t, n, d)
+        assert need == -(-d // 512) * t * n * 4
+        ws = guarded((need // 4,), float("nan"), torch.float32)
+        y = nan_out(t, n)
+        qmm.qmm_gemm(fmt, packed, t, n, d, dev(x_bits), y, ws)
+        torch.cuda.synchronize()
+    finally:
+        qmm.qmm_set_kernel(qmm.QMM_KERNEL_AUTO)
     return host_u16(y)
 
 
@@ -737,7 +764,24 @@ def kernel_auto_after():
     qmm.qmm_set_kernel(qmm.QMM_KERNEL_AUTO)
 
 
-FORCED = (qmm.QMM_KERNEL_AUTO, qmm.QMM_KERNEL_TILE, qmm.QMM_KERNEL_TILE_UNSPLIT, qmm.QMM_KERNEL_FEW_ROW)
+FORCED = (qmm.QMM_KERNEL_AUTO, qmm.QMM_KERNEL_TILE, qmm.QMM_KERNEL_TILE_UNSPLIT, qmm.QMM_KERNEL_FEW_ROW,
+          qmm.QMM_KERNEL_MULTI_ROW)
+
+
+def mrow_lds_bytes(fmt, t, d):
+    """LDS of the multi-row kernel's workgroup: the rows padded to whole
+    512-code slabs, the affine group sums of 16 rows, 6 KiB of partials."""
+    rs = -(-d // 512) * 512
+    return t * rs * 2 + ((rs // 64) * 16 * 4 if fmt == A else 0) + 6 * 1024
+
+
+def kernel_takes(k, fmt, t, d):
+    """Whether a forced kernel setting takes qmm_gemm of this shape."""
+    if k == qmm.QMM_KERNEL_FEW_ROW:
+        return 2 <= t <= 64
+    if k == qmm.QMM_KERNEL_MULTI_ROW:
+        return 2 <= t <= 16 and mrow_lds_bytes(fmt, t, d) <= 160 * 1024
+    return True
 
 
 def run_gemm_forced(kernel, fmt, packed, n, d, x_bits):
@@ -759,9 +803,10 @@ def run_gemm_forced(kernel, fmt, packed, n, d, x_bits):
 def test_forced_kernels_integer_exact(fmt, t, n, d, kernel_auto_after):
     """Integer weights (affine scale 1 bias 0; MXFP4 with E8M0 127) and
     integer activations: every sum is exact in fp32, so the GEMV, the few-row
-    kernel and the tile kernel (split along K or not) must all return the
-    oracle's sums rounded to bf16, bit for bit.  The few-row kernel refuses
-    t = 1 and t > 64."""
+    kernel, the multi-row kernel and the tile kernel (split along K or not)
+    must all return the oracle's sums rounded to bf16, bit for bit.  The
+    few-row kernel refuses t = 1 and t > 64, the multi-row kernel t = 1 and
+    t > 16."""
     say("forced kernels integer exact", fmt, t, n, d)
     rng = np.random.default_rng(40 + t)
     x = synth.bf16_bits(rng.integers(-3, 4, size=(t, d)).astype(float))
@@ -776,7 +821,7 @@ def test_forced_kernels_integer_exact(fmt, t, n, d, kernel_auto_after):
     assert np.all(np.abs(yr) < 2 ** 24)
     want = oracle.f64_to_bf16_bits(yr)
     for k in FORCED:
-        if k == qmm.QMM_KERNEL_FEW_ROW and not 2 <= t <= 64:
+        if not kernel_takes(k, fmt, t, d):
             qmm.qmm_set_kernel(k)
             assert qmm.qmm_workspace_bytes(fmt, t, n, d) == 0
             with pytest.raises(qmm.QmmError) as ei:
@@ -788,7 +833,7 @@ def test_forced_kernels_integer_exact(fmt, t, n, d, kernel_auto_after):
 
 
 @pytest.mark.parametrize("fmt,t,n,d", [(A, 48, 1000, 1024), (M, 33, 300, 3584), (A, 200, 520, 2048),
-                                       (A, 3, 259, 576)])
+                                       (A, 3, 259, 576), (M, 12, 700, 2048)])
 def test_forced_kernels_parity(fmt, t, n, d, kernel_auto_after):
     """Random weights and activations under every kernel setting that takes
     the shape, each within the oracle's bound."""
@@ -803,10 +848,103 @@ def test_forced_kernels_parity(fmt, t, n, d, kernel_auto_after):
         p = pack_mxfp4(w)
         yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
     for k in FORCED:
-        if k == qmm.QMM_KERNEL_FEW_ROW and not 2 <= t <= 64:
+        if not kernel_takes(k, fmt, t, d):
             continue
         y = run_gemm_forced(k, fmt, p, n, d, x)
         assert_parity(y, yr, ar, f"forced kernel {k} fmt={fmt} {t}x{n}x{d}")
+
+
+# ---------------------------------------------------------------------------
+# Multi-row GEMV (2 <= t <= 16, no workspace)
+# ---------------------------------------------------------------------------
+
+def run_gemm_multi_row(fmt, packed, n, d, x_bits):
+    """qmm_gemm with the multi-row kernel forced: no workspace."""
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_MULTI_ROW)
+    try:
+        t = x_bits.shape[0]
+        assert qmm.qmm_workspace_bytes(fmt, t, n, d) == 0
+        y = nan_out(t, n)
+        qmm.qmm_gemm(fmt, packed, t, n, d, dev(x_bits), y, None)
+        torch.cuda.synchronize()
+    finally:
+        qmm.qmm_set_kernel(qmm.QMM_KERNEL_AUTO)
+    return host_u16(y)
+
+
+def auto_picks_multi_row(fmt, t, n, d):
+    """The library's own choice for qmm_gemm (no workspace asked for)."""
+    return kernel_takes(qmm.QMM_KERNEL_MULTI_ROW, fmt, t, d) and (n >= 5120 or t <= 8 if fmt == M else n >= 8192)
+
+
+# launch shapes covered: 1 to 8 column waves per workgroup; the slabs shared
+# by 4, 2 or 1 wave groups; more workgroups than 256 CUs (n > 32768); one
+# narrow slab; a narrow last slab; n not a multiple of 4 or 16; t from 2 to 16
+# (the most rows each format's LDS holds at d = 5120); the decode matrix
+MULTI_ROW_SHAPES = [(A, 2, 5, 64), (A, 3, 300, 320), (A, 16, 1000, 1024), (A, 8, 257, 1088),
+                    (A, 5, 4099, 5184), (A, 14, 13824, 5120), (A, 8, 13824, 5120), (A, 7, 16385, 2048),
+                    (A, 2, 33000, 640), (A, 16, 3000, 4096), (A, 11, 9001, 1536), (A, 4, 27648, 2048),
+                    (M, 2, 7, 32), (M, 5, 300, 96), (M, 16, 257, 3584), (M, 15, 13824, 5120),
+                    (M, 9, 16500, 1056), (M, 4, 1024, 5152), (M, 13, 33001, 512), (M, 8, 5121, 2080),
+                    (M, 3, 32768, 1024)]
+
+
+@pytest.mark.parametrize("fmt,t,n,d", MULTI_ROW_SHAPES)
+def test_gemm_multi_row(fmt, t, n, d, kernel_auto_after):
+    """The multi-row kernel against the oracle; where the library picks it by
+    itself, the call without a forced setting gives the same bits."""
+    say("gemm multi-row", fmt, t, n, d)
+    x = synth.activations(9100 + t, synth.S_X, t, d)
+    if fmt == A:
+        w = synth.affine_weights(9200 + n, n, d)
+        p = pack_affine(w)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(9300 + n, n, d)
+        p = pack_mxfp4(w)
+        yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    y = run_gemm_multi_row(fmt, p, n, d, x)
+    assert_parity(y, yr, ar, f"gemm multi-row fmt={fmt} {t}x{n}x{d}")
+    if auto_picks_multi_row(fmt, t, n, d):
+        assert qmm.qmm_workspace_bytes(fmt, t, n, d) == 0
+        ya = nan_out(t, n)
+        qmm.qmm_gemm(fmt, p, t, n, d, dev(x), ya, None)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(ya), y)
+
+
+@pytest.mark.parametrize("fmt,t,n,d", [(A, 8, 13824, 5120), (A, 16, 3000, 4096), (A, 13, 1000, 5184),
+                                       (M, 15, 13824, 5120), (M, 6, 20000, 1536)])
+def test_gemm_multi_row_integer_exact(fmt, t, n, d, kernel_auto_after):
+    """Integer weights and activations: the multi-row kernel returns the
+    oracle's exact sums rounded to bf16, bit for bit the few-row kernel's."""
+    say("gemm multi-row integer exact", fmt, t, n, d)
+    rng = np.random.default_rng(70 + t)
+    x = synth.bf16_bits(rng.integers(-3, 4, size=(t, d)).astype(float))
+    if fmt == A:
+        w = integer_affine(80 + t, n, d)
+        p = pack_affine(w)
+        yr, _ = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(80 + t, n, d, 127, 1)
+        p = pack_mxfp4(w)
+        yr, _ = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    assert np.all(np.abs(yr) < 2 ** 24)
+    want = oracle.f64_to_bf16_bits(yr)
+    assert np.array_equal(run_gemm_multi_row(fmt, p, n, d, x), want)
+    assert np.array_equal(run_gemm_forced(qmm.QMM_KERNEL_FEW_ROW, fmt, p, n, d, x), want)
+
+
+def test_gemm_multi_row_repeated_and_shrinking(kernel_auto_after):
+    """Calls in a row on one stream, the second with fewer rows and columns
+    and a shorter reduction: nothing carries over between launches."""
+    say("gemm multi-row repeated")
+    for t, n, d in [(12, 13824, 5120), (3, 999, 1088), (12, 13824, 5120)]:
+        x = synth.activations(9400 + t, synth.S_X, t, d)
+        w = synth.affine_weights(9500 + n, n, d)
+        y = run_gemm_multi_row(A, pack_affine(w), n, d, x)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+        assert_parity(y, yr, ar, f"gemm multi-row repeated {t}x{n}x{d}")
 
 
 # ---------------------------------------------------------------------------

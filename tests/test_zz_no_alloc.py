@@ -72,11 +72,12 @@ def both(fmt, p, t, n, d, x):
     return y0.cpu().numpy().view(np.uint16), y1.cpu().numpy().view(np.uint16)
 
 
-# (format, n, d, first t, second t): few-row split-K (2 <= t <= 64), the tile
-# kernel split along K (t > 64 with few tiles, d a multiple of 512), and the
-# affine tile kernel unsplit (its fp16 activations in the scratch)
-CASES = [(A, 13824, 5120, 40, 8), (M, 1000, 3584, 64, 3), (A, 1000, 2048, 200, 70),
-         (M, 700, 3072, 97, 66), (A, 4352, 1024, 2048, 300)]
+# (format, n, d, first t, second t): few-row split-K (16 < t <= 64, and
+# narrow affine matrices below that), the tile kernel split along K (t > 64
+# with few tiles, d a multiple of 512), and the affine tile kernel unsplit
+# (its fp16 activations in the scratch)
+CASES = [(A, 13824, 5120, 40, 20), (M, 1000, 3584, 64, 17), (A, 4096, 2048, 12, 3),
+         (A, 1000, 2048, 200, 70), (M, 700, 3072, 97, 66), (A, 4352, 1024, 2048, 300)]
 
 
 @pytest.mark.parametrize("fmt,n,d,t1,t2", CASES)
@@ -108,3 +109,24 @@ def test_noalloc_single_row_and_limit():
     with pytest.raises(qmm.QmmError) as ei:
         qmm.qmm_gemm_noalloc(A, 1 << 20, 64, big_n, 5120, 1 << 20, 1 << 20)
     assert ei.value.name == "QMM_E_WORKSPACE"
+
+
+@pytest.mark.parametrize("fmt,n,d,t", [(A, 13824, 5120, 8), (M, 1000, 3584, 3)])
+def test_noalloc_multi_row_takes_no_scratch(fmt, n, d, t):
+    """Shapes on the multi-row kernel need no workspace: the allocation-free
+    call runs the same kernel as qmm_gemm, bit for bit, twice in a row."""
+    p, ref = packed_weights(fmt, 9400 + n, n, d)
+    assert qmm.qmm_workspace_bytes(fmt, t, n, d) == 0
+    x = synth.activations(9500 + t, synth.S_X, t, d)
+    xd = dev(x)
+    outs = []
+    for _ in range(2):
+        y0 = torch.full((t, n), 0x7FC0, dtype=torch.int16, device=DEV)
+        qmm.qmm_gemm_noalloc(fmt, p, t, n, d, xd, y0)
+        y1 = torch.full((t, n), 0x7FC0, dtype=torch.int16, device=DEV)
+        qmm.qmm_gemm(fmt, p, t, n, d, xd, y1, None)
+        torch.cuda.synchronize()
+        outs.append((y0.cpu().numpy().view(np.uint16), y1.cpu().numpy().view(np.uint16)))
+    assert all(np.array_equal(a, b) for a, b in outs) and np.array_equal(outs[0][0], outs[1][0])
+    yr, ar = ref(x)
+    assert oracle.check(outs[0][0], yr, ar)["ok"]
