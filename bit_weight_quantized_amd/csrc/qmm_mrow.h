@@ -32,12 +32,19 @@ inline MrowPlan mrow_plan(int64_t n, int64_t d, int cus) {
   return p;
 }
 
-// LDS of one workgroup: the t rows padded to whole 512-code slabs (bf16);
-// for affine weights the sums of 16 rows (zeros past t) over each 64-code
-// group (fp32); the partial sums of the wave groups past the first.
+// Affine weights with at most this many rows put a step's two 64-code groups
+// in the two 8-row halves of one MFMA (one row of zeros more in LDS).
+constexpr int kMrowG2MaxT = 8;
+
+// LDS of one workgroup: the t rows padded to whole 512-code slabs (bf16),
+// plus a row of zeros for affine weights with t <= 8; for affine weights the
+// sums of 16 rows (zeros past t) over each 64-code group (fp32); the partial
+// sums of the wave groups past the first.
 inline size_t mrow_lds_bytes(int f, int64_t t, int64_t d) {
   const int64_t rs = (d + kSlabCodes - 1) / kSlabCodes * kSlabCodes;
-  return size_t(t * rs * 2 + (f == QMM_AFFINE4_G64 ? (rs / 64) * 16 * 4 : 0)) + kMrowRedBytes;
+  const bool aff = f == QMM_AFFINE4_G64;
+  const int64_t rows = t + (aff && t <= kMrowG2MaxT ? 1 : 0);
+  return size_t(rows * rs * 2 + (aff ? (rs / 64) * 16 * 4 : 0)) + kMrowRedBytes;
 }
 
 // Whether the kernel takes this shape: 2 <= t <= 16, the rows fit in LDS,

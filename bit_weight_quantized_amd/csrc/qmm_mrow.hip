@@ -38,7 +38,7 @@ constexpr int kMrRing = 2;               // slabs in flight per lane
 // element offset of 16-byte piece c of row r (row stride rs elements)
 __device__ __forceinline__ int mr_at(int r, int rs, int c) { return r * rs + ((c ^ (r & 15)) << 3); }
 
-template <int FMT, int KQ>
+template <int FMT, int KQ, bool G2>
 __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ meta,
                                                    uint32_t codes_bytes, uint32_t meta_bytes, int t,
@@ -46,13 +46,15 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
                                                    const uint16_t* __restrict__ x,
                                                    uint16_t* __restrict__ y) {
   constexpr bool AFF = FMT == QMM_AFFINE4_G64;
+  static_assert(!G2 || AFF, "two groups per MFMA: affine weights only");
   constexpr int MP = AFF ? 2 : 1;   // 16-byte metadata pieces of one column per slab
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   const Slabs L{n, d, FMT};
   const int ns = L.count();
   const int rs = ns * kSlabCodes;   // LDS row stride in elements (rows padded to whole slabs)
   const int ng = ns * 8;            // 64-code groups per padded row
-  float* xsum = reinterpret_cast<float*>(xs + t * rs);   // [ng][16 rows] (affine; rows past t zero)
+  const int xrows = t + (G2 ? 1 : 0);   // G2: a row of zeros after the t rows
+  float* xsum = reinterpret_cast<float*>(xs + xrows * rs);   // [ng][16 rows] (affine; rows past t zero)
   f32x4_t* red = reinterpret_cast<f32x4_t*>(xsum + (AFF ? ng * 16 : 0));   // [KQ - 1][ncw][64]
 
   const int tid = threadIdx.x;
@@ -75,12 +77,13 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
   // 1. the activation rows to LDS by DMA, no registers involved: copy i of
   //    the workgroup fills LDS bytes [1024i, 1024i + 1024), lane l slot
   //    q = 64i + l, that is row r = q / (rs/8), position c' = q % (rs/8), which
-  //    holds piece c = c' ^ (r & 15) of the row (zeros past d)
+  //    holds piece c = c' ^ (r & 15) of the row (zeros past d, and in the
+  //    zero row)
   const int prow = rs / 8;   // 16-byte pieces per row, a multiple of 64
   const uint32_t xbase = lds_addr(xs);
-  for (int i = wave; i < t * prow / 64; i += nw) {
+  for (int i = wave; i < xrows * prow / 64; i += nw) {
     const int q = 64 * i + lane, r = q / prow, c = (q - r * prow) ^ (r & 15);
-    copy16_to_lds(xrs, 8 * c < d ? (uint32_t(r) * uint32_t(d) + 8u * uint32_t(c)) * 2u : kOOB,
+    copy16_to_lds(xrs, r < t && 8 * c < d ? (uint32_t(r) * uint32_t(d) + 8u * uint32_t(c)) * 2u : kOOB,
                   xbase + 1024u * uint32_t(i));
   }
 
@@ -141,13 +144,17 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
   asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(pmagic));
   // the lane's A-operand pieces: piece 16k + p0 (p0 < 16) of row r sits at
   // 16k + (p0 ^ (r & 15)), so each address is a per-lane base plus the
-  // step's uniform offset.  Affine: piece p0 = 8h + 4(g & 1) + 2 + jj − 2(g >> 1)
-  // of the step (see the regrouping below); MXFP4: p0 = 4g + j.
-  const int arow = min(col_l, t - 1);
+  // step's uniform offset.  MXFP4 and G2: p0 = 4g + j, word j of the lane's
+  // chunk; affine otherwise: p0 = 8h + 4(g & 1) + 2 + jj − 2(g >> 1) (see the
+  // regrouping below).  G2 (t <= 8): the MFMA's rows 0..7 are the x rows
+  // against group 2st of the step, rows 8..15 the same x rows against group
+  // 2st + 1; A row i reads x row i & 7 on the lanes of its group's chunks
+  // (g >> 1 == i >> 3) and the zero row on the others.
+  const int arow = G2 ? ((col_l >> 3) == (g >> 1) ? min(col_l & 7, t - 1) : t) : min(col_l, t - 1);
   int aoff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int p0 = AFF ? 8 * (i >> 1) + 4 * (g & 1) + 2 + (i & 1) - 2 * (g >> 1) : 4 * g + i;
+    const int p0 = AFF && !G2 ? 8 * (i >> 1) + 4 * (g & 1) + 2 + (i & 1) - 2 * (g >> 1) : 4 * g + i;
     aoff[i] = arow * rs + ((p0 ^ (arow & 15)) << 3);
   }
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -157,7 +164,28 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
     for (int st = 0; st < 4; ++st) {
       if (128 * st >= w) break;   // a narrow last slab ends early (uniform)
       const int e0 = (s * 64 + st * 16) * 8;   // the step's first activation element
-      if constexpr (AFF) {
+      if constexpr (G2) {
+        // the lane's chunk g lies in group 2st + h, h = g >> 1; its rows
+        // 4(g & 1) .. + 3 of the MFMA sum that group only (the narrow last
+        // slab's missing second group: zero metadata, zero sums)
+        const int h = g >> 1;
+        const uint32_t mh = h ? (128 * st + 64 < w ? m[st >> 1][(2 * st + 1) & 3] : 0u) : m[st >> 1][(2 * st) & 3];
+        const float gs = bf16_lo(mh), gc = __builtin_fmaf(-128.0f, bf16_lo(mh), bf16_hi(mh));
+        f32x4_t pg = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x4_t b;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) b[r] = ((c4[st][j] >> (4 * r)) & pmask) | pmagic;
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&xs[aoff[j] + e0]);
+          pg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), pg, 0, 0, 0);
+        }
+        // acc += s·P + (b − 128·s)·Σx for x rows 4(g & 1) + r, group 2st + h
+        const f32x4_t xg = *reinterpret_cast<const f32x4_t*>(&xsum[(s * 8 + 2 * st + h) * 16 + 4 * (g & 1)]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = __builtin_fmaf(gc, xg[r], __builtin_fmaf(gs, pg[r], acc[r]));
+      } else if constexpr (AFF) {
         // groups 2st and 2st + 1 of the slab: dwords 2st, 2st + 1 of the column's metadata
         // (a last slab may end after group 2st: its second group's dword
         // belongs to another column and is replaced by zero)
@@ -220,8 +248,17 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
     }
   }
 
-  // 5. the KQ shares of each column block summed in order kq = 0, 1, ...;
-  //    lane holds column col, rows 4g .. 4g + 3
+  // 5. G2: lanes g and g ^ 2 hold the two halves of x rows 4(g & 1) + r
+  //    (groups 2st and 2st + 1 of every step): added, the first half first
+  if constexpr (G2) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]), __float_as_uint(acc[r]), false, false);
+      acc[r] = lane < 32 ? acc[r] + __uint_as_float(sw[1]) : __uint_as_float(sw[0]) + acc[r];
+    }
+  }
+  // 6. the KQ shares of each column block summed in order kq = 0, 1, ...;
+  //    lane holds column col, rows 4g .. 4g + 3 (G2: rows 4(g & 1) + r, g < 2)
   if constexpr (KQ > 1) {
     if (kq > 0) red[((kq - 1) * ncw + cw) * 64 + lane] = acc;
     __syncthreads();
@@ -229,10 +266,10 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
 #pragma unroll
     for (int k = 1; k < KQ; ++k) acc += red[((k - 1) * ncw + cw) * 64 + lane];
   }
-  if (col < c1) {
+  if (col < c1 && (!G2 || g < 2)) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = 4 * g + r;
+      const int row = 4 * (G2 ? g & 1 : g) + r;
       if (row < t) y[int64_t(row) * n + col] = f32_to_bf16(acc[r]);
     }
   }
@@ -256,10 +293,13 @@ int launch_mrow(const GemmArgs& a, void* stream) {
   auto go = [&](auto kern) {
     launch_kernel_lds(kern, grid, block, lds, s, codes, meta, cb, mb, a.t, a.n, a.d, p.cpw, p.ncw, a.x, a.y);
   };
-  if (a.f == QMM_AFFINE4_G64)
-    p.kq == 4 ? go(mrow_kernel<QMM_AFFINE4_G64, 4>) : p.kq == 2 ? go(mrow_kernel<QMM_AFFINE4_G64, 2>) : go(mrow_kernel<QMM_AFFINE4_G64, 1>);
+  constexpr int AF = QMM_AFFINE4_G64, MX = QMM_MXFP4_G32;
+  if (a.f == AF && a.t <= kMrowG2MaxT)
+    p.kq == 4 ? go(mrow_kernel<AF, 4, true>) : p.kq == 2 ? go(mrow_kernel<AF, 2, true>) : go(mrow_kernel<AF, 1, true>);
+  else if (a.f == AF)
+    p.kq == 4 ? go(mrow_kernel<AF, 4, false>) : p.kq == 2 ? go(mrow_kernel<AF, 2, false>) : go(mrow_kernel<AF, 1, false>);
   else
-    p.kq == 4 ? go(mrow_kernel<QMM_MXFP4_G32, 4>) : p.kq == 2 ? go(mrow_kernel<QMM_MXFP4_G32, 2>) : go(mrow_kernel<QMM_MXFP4_G32, 1>);
+    p.kq == 4 ? go(mrow_kernel<MX, 4, false>) : p.kq == 2 ? go(mrow_kernel<MX, 2, false>) : go(mrow_kernel<MX, 1, false>);
   return int(hipGetLastError());
 }
 

@@ -174,9 +174,9 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
  * output rounded once to bf16:
  *   2 <= t <= 16, multi-row kernel (MXFP4 weights with n >= 5120 or t <= 8,
  *     affine weights with n >= 8192, while its LDS fits 160 KiB: the t rows
- *     padded to whole 512-code slabs, t·ceil(d/512) KiB, plus 6 KiB, plus
- *     ceil(d/512)/2 KiB for affine weights; at d = 5120 affine t <= 14,
- *     MXFP4 t <= 15): every
+ *     padded to whole 512-code slabs, t·ceil(d/512) KiB (one row more for
+ *     affine weights with t <= 8), plus 6 KiB, plus ceil(d/512)/2 KiB for
+ *     affine weights; at d = 5120 affine t <= 14, MXFP4 t <= 15): every
  *     weight read once for all rows, no workspace, one kernel.  Affine codes enter bf16 MFMAs as the exact
  *     values 128 + q and each group's scale and bias follow in fp32.
  *   other 2 <= t <= 64 (with the workspace): split along d, each 512-code slab's

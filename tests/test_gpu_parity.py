@@ -770,9 +770,11 @@ FORCED = (qmm.QMM_KERNEL_AUTO, qmm.QMM_KERNEL_TILE, qmm.QMM_KERNEL_TILE_UNSPLIT,
 
 def mrow_lds_bytes(fmt, t, d):
     """LDS of the multi-row kernel's workgroup: the rows padded to whole
-    512-code slabs, the affine group sums of 16 rows, 6 KiB of partials."""
+    512-code slabs (one more, of zeros, for affine weights with t <= 8), the
+    affine group sums of 16 rows, 6 KiB of partials."""
     rs = -(-d // 512) * 512
-    return t * rs * 2 + ((rs // 64) * 16 * 4 if fmt == A else 0) + 6 * 1024
+    rows = t + (1 if fmt == A and t <= 8 else 0)
+    return rows * rs * 2 + ((rs // 64) * 16 * 4 if fmt == A else 0) + 6 * 1024
 
 
 def kernel_takes(k, fmt, t, d):
