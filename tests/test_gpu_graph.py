@@ -1,8 +1,9 @@
 """HIP graph capture of the hot path (needs an MI355X).
 
 A decode GEMV, a prefill GEMM (also split along K through a workspace, 4 and 70
-rows) and a whole routed MoE layer (route -> gate_up with SwiGLU -> down ->
-combine) are recorded once into a HIP graph through
+rows), 6 rows through the multi-row kernel and a whole routed MoE layer (route
+-> gate_up with SwiGLU -> down -> combine) are recorded once into a HIP graph
+through
 torch.cuda.CUDAGraph and replayed: the matmul, routing and combine calls only
 enqueue kernels on the caller's stream (no allocation, copy, memset or
 synchronization), so a replay must reproduce an eager run on the same inputs
@@ -72,6 +73,12 @@ def test_graph_replay_matches_eager():
         qmm.qmm_pack(M, 2 * ni, dm, dev(g.codes), dev(g.e8m0), None, gu.data_ptr() + e * gsz)
         w = synth.mxfp4_weights(903, dm, ni, synth.S_DN_CODES, synth.S_DN_E8M0, e)
         qmm.qmm_pack(M, dm, ni, dev(w.codes), dev(w.e8m0), None, dn.data_ptr() + e * dsz)
+    # 6 rows of an MXFP4 matrix: the multi-row kernel (one kernel, no workspace)
+    nr, dr, tr = 700, 1024, 6
+    wr = synth.mxfp4_weights(907, nr, dr, synth.S_GU_CODES, synth.S_GU_E8M0, 0)
+    pr = torch.empty(qmm.qmm_packed_bytes(M, nr, dr), dtype=torch.uint8, device=DEV)
+    qmm.qmm_pack(M, nr, dr, dev(wr.codes), dev(wr.e8m0), None, pr)
+    assert qmm.qmm_workspace_bytes(M, tr, nr, dr) == 0
     _, r, bias = synth.router_inputs(904, t=t, d=dm, experts=ne)
     r_d, bias_d = dev(r), torch.from_numpy(np.asarray(bias, np.float32)).to(DEV)
 
@@ -81,6 +88,7 @@ def test_graph_replay_matches_eager():
     xu = torch.empty(tg, du, dtype=torch.int16, device=DEV)
     wsu = torch.empty(qmm.qmm_workspace_bytes(A, tg, ng, du) // 4, dtype=torch.float32, device=DEV)
     xm = torch.empty(t, dm, dtype=torch.int16, device=DEV)
+    xr = torch.empty(tr, dr, dtype=torch.int16, device=DEV)
     # the GEMM split along K (two kernels each, fp32 partials in a workspace):
     # 4 rows through the few-row kernel, 70 rows through the split tile kernel
     ws4 = torch.empty(qmm.qmm_workspace_bytes(A, 4, ng, dg) // 4, dtype=torch.float32, device=DEV)
@@ -91,6 +99,7 @@ def test_graph_replay_matches_eager():
         "gemm": (torch.empty(tg, ng, dtype=torch.int16, device=DEV), 0x7FC0),
         "gemm_split4": (torch.empty(4, ng, dtype=torch.int16, device=DEV), 0x7FC0),
         "gemm_split70": (torch.empty(tg, ng, dtype=torch.int16, device=DEV), 0x7FC0),
+        "gemm_multi_row6": (torch.empty(tr, nr, dtype=torch.int16, device=DEV), 0x7FC0),
         "scores": (torch.empty(t, ne, dtype=torch.float32, device=DEV), float("nan")),
         "topk": (torch.empty(t, k, dtype=torch.int32, device=DEV), -7),
         "seg_expert": (torch.empty(ne, dtype=torch.int32, device=DEV), -7),
@@ -107,6 +116,7 @@ def test_graph_replay_matches_eager():
         xg.copy_(dev(synth.activations(seed, synth.S_X, tg, dg, sub=1)))
         xu.copy_(dev(synth.activations(seed, synth.S_X, tg, du, sub=3)))
         xm.copy_(dev(synth.activations(seed, synth.S_X, t, dm, sub=2)))
+        xr.copy_(dev(synth.activations(seed, synth.S_X, tr, dr, sub=4)))
 
     def reset():
         for buf, fill in outs.values():
@@ -117,6 +127,7 @@ def test_graph_replay_matches_eager():
         qmm.qmm_gemm(A, pu, tg, ng, du, xu, O["gemm"], wsu)
         qmm.qmm_gemm(A, pg, 4, ng, dg, xg, O["gemm_split4"], ws4)
         qmm.qmm_gemm(A, pg, tg, ng, dg, xg, O["gemm_split70"], ws70)
+        qmm.qmm_gemm(M, pr, tr, nr, dr, xr, O["gemm_multi_row6"], None)
         qmm.qmm_route(xm, t, dm, r_d, ne, bias_d, k, O["scores"], O["topk"], O["seg_expert"],
                       O["seg_offsets"], O["row_index"])
         qmm.qmm_grouped_gemm_swiglu(M, gu, gsz, ne, 2 * ni, dm, xm, t, O["row_index"], O["seg_expert"],
