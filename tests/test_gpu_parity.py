@@ -937,6 +937,35 @@ def test_gemm_multi_row_integer_exact(fmt, t, n, d, kernel_auto_after):
     assert np.array_equal(run_gemm_forced(qmm.QMM_KERNEL_FEW_ROW, fmt, p, n, d, x), want)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_gemm_multi_row_random_shapes(seed, kernel_auto_after):
+    """Seeded random shapes on the multi-row kernel (forced): t from 2 to 16,
+    n from 1 to 40000 (one to eight column waves per workgroup, one or two
+    workgroups per CU), d any multiple of the group up to what the rows' LDS
+    allows, both formats."""
+    rng = np.random.default_rng(1900 + seed)
+    fmt = A if seed % 2 == 0 else M
+    g = 64 if fmt == A else 32
+    t = int(rng.integers(2, 17))
+    n = int(rng.choice([rng.integers(1, 300), rng.integers(300, 9000), rng.integers(9000, 40001)]))
+    d = g * int(rng.integers(1, 6144 // g + 1))
+    while not kernel_takes(qmm.QMM_KERNEL_MULTI_ROW, fmt, t, d):
+        d -= g * 8 if d > g * 8 else 0
+        t = max(2, t - 1)
+    say("gemm multi-row random", seed, "fmt", fmt, "t n d", t, n, d)
+    x = synth.activations(1910 + seed, synth.S_X, t, d)
+    if fmt == A:
+        w = synth.affine_weights(1920 + seed, n, d)
+        p = pack_affine(w)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(1920 + seed, n, d)
+        p = pack_mxfp4(w)
+        yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    y = run_gemm_multi_row(fmt, p, n, d, x)
+    assert_parity(y, yr, ar, f"gemm multi-row random {seed}: fmt {fmt} {t}x{n}x{d}")
+
+
 def test_gemm_multi_row_repeated_and_shrinking(kernel_auto_after):
     """Calls in a row on one stream, the second with fewer rows and columns
     and a shorter reduction: nothing carries over between launches."""
