@@ -89,13 +89,16 @@ bool forces_tile(int k) { return k == QMM_KERNEL_TILE || k == QMM_KERNEL_TILE_UN
 // Whether qmm_gemm runs the multi-row GEMV under kernel setting k: when
 // forced, or by default where it was measured faster than the few-row
 // split-K kernel.  Each of its workgroups stages every activation row, so
-// narrow matrices (few columns per workgroup) favour the split-K kernel:
-// MXFP4 weights take it from 5120 columns, or for up to 8 rows; affine
-// weights, whose per-group scale and bias cost more per code, from 8192.
+// narrow matrices (few columns per workgroup) favour the split-K kernel.
+// Rows held in LDS (t <= 16): MXFP4 weights from 5120 columns, or for up to
+// 8 rows; affine weights, whose per-group scale and bias cost more per code,
+// from 8192.  Rows streamed (17 <= t <= 64): from 6144 columns, or from 2048
+// where d <= 2048 (the split-K kernel then has few slabs to share out).
 bool uses_mrow(int k, int f, int64_t t, int64_t n, int64_t d, const qmm::Layout& l) {
   if (k == QMM_KERNEL_MULTI_ROW) return qmm::mrow_fits(f, t, n, d, l);
   // (the grouped-matmul setting does not concern qmm_gemm: as under auto)
   if ((k != QMM_KERNEL_AUTO && k != QMM_KERNEL_GROUPED_MATMUL) || !qmm::mrow_fits(f, t, n, d, l)) return false;
+  if (t > qmm::kMrowMaxT) return n >= 6144 || (d <= 2048 && n >= 2048);
   return f == QMM_MXFP4_G32 ? (n >= 5120 || t <= 8) : n >= 8192;
 }
 
@@ -299,7 +302,7 @@ qmm_status gemm_impl(const char* name, bool noalloc, qmm_format f, const void* p
   if (kf == QMM_KERNEL_FEW_ROW && !qmm::skinny_fits(t, n, d, l))
     return fail(QMM_E_UNSUPPORTED, "the few-row kernel takes 2 <= t <= 64 rows (kernel forced to few_row)");
   if (kf == QMM_KERNEL_MULTI_ROW && !qmm::mrow_fits(f, t, n, d, l))
-    return fail(QMM_E_UNSUPPORTED, "the multi-row kernel takes 2 <= t <= 16 rows whose padded rows fit in 160 KiB of LDS (kernel forced to multi_row)");
+    return fail(QMM_E_UNSUPPORTED, "the multi-row kernel takes 2 <= t <= 16 rows whose padded rows fit in 160 KiB of LDS, or 17 <= t <= 64 (kernel forced to multi_row)");
   const size_t need = gemm_ws_bytes(kf, f, t, n, d, l);
   if (noalloc) {
     if (need > qmm::kNoAllocScratchBytes)

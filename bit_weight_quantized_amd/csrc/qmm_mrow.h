@@ -1,5 +1,6 @@
 // Launcher of the multi-row GEMV (qmm_mrow.hip): Y = X·Ŵᵀ for a few rows,
-// every weight byte read once, the rows held whole in LDS.
+// every weight byte read once, the rows held whole in LDS (up to 16) or
+// streamed through it slab by slab (up to 64).
 #pragma once
 
 #include <stddef.h>
@@ -47,11 +48,34 @@ inline size_t mrow_lds_bytes(int f, int64_t t, int64_t d) {
   return size_t(rows * rs * 2 + (aff ? (rs / 64) * 16 * 4 : 0)) + kMrowRedBytes;
 }
 
-// Whether the kernel takes this shape: 2 <= t <= 16, the rows fit in LDS,
-// and the 32-bit buffer offsets cover the codes, metadata and activations.
+// The streaming form, for kMrowMaxT < t <= kMrowStreamMaxT: the rows pass
+// through two LDS buffers of one 512-code slab each, RB = ceil(t / 16) blocks
+// of 16 rows; four waves of 16 columns per workgroup, so at most 64 columns.
+constexpr int kMrowStreamMaxT = 64;
+constexpr int kMrowStreamCols = 64;
+inline int mrow_stream_blocks(int64_t t) { return int((t + 15) / 16); }
+inline MrowPlan mrow_stream_plan(int64_t n, int cus) {
+  MrowPlan p;
+  p.groups = (n + int64_t(cus) * kMrowStreamCols - 1) / (int64_t(cus) * kMrowStreamCols) * cus;
+  p.cpw = int((n + p.groups - 1) / p.groups);
+  p.ncw = 4;
+  p.kq = 1;
+  return p;
+}
+// two slab buffers of 16·RB rows (bf16); for affine weights each buffer's
+// sums of those rows over its eight 64-code groups (fp32)
+inline size_t mrow_stream_lds_bytes(int f, int64_t t) {
+  const int64_t rows = 16 * int64_t(mrow_stream_blocks(t));
+  return size_t(2 * rows * kSlabCodes * 2 + (f == QMM_AFFINE4_G64 ? 2 * 8 * rows * 4 : 0));
+}
+
+// Whether the kernel takes this shape: 2 <= t <= 16 with the rows in LDS, or
+// up to kMrowStreamMaxT rows streamed, and the 32-bit buffer offsets cover
+// the codes, metadata and activations.
 inline bool mrow_fits(int f, int64_t t, int64_t n, int64_t d, const Layout& l) {
-  return t >= 2 && t <= kMrowMaxT && mrow_lds_bytes(f, t, d) <= kMrowMaxLds &&
-         n * (d / 2) < (int64_t(1) << 31) && l.meta_bytes < (int64_t(1) << 31) &&
+  const bool shape = t >= 2 && t <= kMrowMaxT ? mrow_lds_bytes(f, t, d) <= kMrowMaxLds
+                                              : t > kMrowMaxT && t <= kMrowStreamMaxT;
+  return shape && n * (d / 2) < (int64_t(1) << 31) && l.meta_bytes < (int64_t(1) << 31) &&
          t * d * 2 < (int64_t(1) << 31);
 }
 

@@ -1,4 +1,4 @@
-// Multi-row GEMV: Y = X·Ŵᵀ for 2 <= T <= 16 activation rows (a batch of
+// Multi-row GEMV: Y = X·Ŵᵀ for 2 <= T <= 64 activation rows (a batch of
 // decode tokens), the product of "Kapitsa 源码拆解 02：权重、矩阵与 Metal",
 // section "矩阵乘法中数据和参数", at a size where every weight byte is read once
 // and serves all T rows, with no partial sums in memory and no second kernel.
@@ -10,7 +10,8 @@
 // flight per lane, and the groups' partial sums meet in LDS in a fixed order.
 // Each workgroup first copies the T activation rows (zeros past d, padded to
 // whole slabs) to LDS by DMA, 16-byte pieces swizzled within each 256-byte
-// group so that the 16 rows of one MFMA operand read sit in distinct banks.
+// group so that the 16 rows of one MFMA operand read sit in distinct banks
+// (more than 16 rows do not fit: they take the streaming form further down).
 // The rows enter v_mfma_f32_16x16x32_bf16 as its 16-row A operand (rows past
 // T read row T - 1 and their outputs are dropped); lane (column c, chunk g)
 // loads the 32-code chunk g of each 128-code step of its column.
@@ -275,6 +276,233 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
   }
 }
 
+// Streaming form for 17 <= T <= 64 rows (RB = ceil(T / 16) row blocks of the
+// MFMA's 16-row A operand): the rows no longer fit in LDS whole, so they pass
+// through two slab buffers.  Eight waves: four column waves of 16 columns (up
+// to 64 columns per workgroup) times two halves of each slab (its 128-code
+// steps 0, 1 and 2, 3), the two halves' sums meeting in LDS at the end.  Each
+// lane keeps its half of four slabs' codes in flight, and the workgroup the
+// rows of the next two slabs: while slab s is multiplied from one buffer,
+// the rows of slab s + 2 are loaded into registers and those of slab s + 1,
+// which landed meanwhile, are stored into the other buffer (zeros past T and
+// past d), with their affine group sums taken across lanes on the way; one
+// barrier per slab.  Every weight is read once for all rows and each of its
+// operands feeds RB MFMAs.
+constexpr int kStRing = 4;   // slabs of codes in flight per lane
+constexpr int kStXd = 2;     // slabs of rows in flight (divides kStRing)
+static_assert(kStRing % 2 == 0 && kStRing % kStXd == 0, "buffer and ring slots repeat every kStRing slabs");
+
+template <int FMT, int RB>
+__global__ __launch_bounds__(512) void mrow_stream_kernel(const uint8_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ meta,
+                                                          uint32_t codes_bytes, uint32_t meta_bytes, int t,
+                                                          int n, int d, int cpw,
+                                                          const uint16_t* __restrict__ x,
+                                                          uint16_t* __restrict__ y) {
+  constexpr bool AFF = FMT == QMM_AFFINE4_G64;
+  constexpr int XR = 16 * RB;             // rows of a slab buffer
+  constexpr int XB = XR * kSlabCodes;     // elements of a slab buffer
+  constexpr int XP = XR * 64 / 512;       // 16-byte pieces of a slab per thread
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  float* xsum = reinterpret_cast<float*>(xs + 2 * XB);   // affine: [buffer][group][row]
+  const Slabs L{n, d, FMT};
+  const int ns = L.count();
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cw = wave & 3, kh = wave >> 2;   // column wave, half of the slab
+  const int col_l = lane & 15, g = lane >> 4;
+  const int c0 = blockIdx.x * cpw, c1 = min(c0 + cpw, n);
+  const int col = c0 + 16 * cw + col_l;
+  const int lcol = min(col, c1 - 1);
+  const bool active = 16 * cw < c1 - c0;
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(codes, codes_bytes);
+  const __amdgpu_buffer_rsrc_t mrs = make_rsrc(meta, meta_bytes);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, uint32_t(t) * uint32_t(d) * 2u);
+
+  // the rows of slab s: a wave's i-th piece is piece `lane` of row wave + 8i
+  // (zeros past t and past d), stored at position lane ^ (row & 15)
+  auto xload = [&](u32x4_t (&v)[XP], int s) {
+    const int k = s * kSlabCodes + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int r = wave + 8 * i;
+      v[i] = buf_load16(xrs, r < t && k < d ? (uint32_t(r) * uint32_t(d) + uint32_t(k)) * 2u : kOOB);
+    }
+  };
+  auto xstore = [&](const u32x4_t (&v)[XP], int b) {
+#pragma unroll
+    for (int i = 0; i < XP; ++i) {
+      const int r = wave + 8 * i;
+      *reinterpret_cast<u32x4_t*>(&xs[b * XB + mr_at(r, kSlabCodes, lane)]) = v[i];
+      if constexpr (AFF) {
+        // the row's sum over 64-code group lane / 8: eight pieces, eight lanes
+        float p = ((bf16_lo(v[i][0]) + bf16_hi(v[i][0])) + (bf16_lo(v[i][1]) + bf16_hi(v[i][1]))) +
+                  ((bf16_lo(v[i][2]) + bf16_hi(v[i][2])) + (bf16_lo(v[i][3]) + bf16_hi(v[i][3])));
+        p += dpp_f<0xB1>(p);    // quad_perm [1,0,3,2]
+        p += dpp_f<0x4E>(p);    // quad_perm [2,3,0,1]
+        p += dpp_f<0x141>(p);   // row_half_mirror
+        if ((lane & 7) == 0) xsum[(b * 8 + (lane >> 3)) * XR + r] = p;
+      }
+    }
+  };
+
+  // the code ring: the lane's chunk of steps 2kh and 2kh + 1 of slab s and
+  // the metadata of those steps (affine: dwords 4kh .. 4kh + 3, groups 4kh ..
+  // 4kh + 3; MXFP4: the slab's four dwords)
+  u32x4_t rc[kStRing][2];
+  u32x4_t rm[kStRing];
+  auto issue = [&](u32x4_t (&c2)[2], u32x4_t& m, int s) {
+    const bool in = active && s < ns;
+    const int w = in ? L.width(s) : 0;
+    const uint32_t cb = in ? uint32_t(L.codes(s, lcol)) : 0u;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kk = 128 * (2 * kh + j) + 32 * g;
+      c2[j] = buf_load16(crs, kk < w ? cb + uint32_t(kk >> 1) : kOOB);
+    }
+    const int mrow = in ? L.meta_row(s) : 0;
+    const uint32_t mb = in ? uint32_t(L.meta(s, lcol)) : 0u;
+    const int mo = AFF ? 16 * kh : 0;
+    m = buf_load16(mrs, mo < mrow ? mb + uint32_t(mo) : kOOB);
+  };
+
+  // rows of slab s in xv[s % kStXd] until stored into LDS buffer s & 1.
+  // Every step issues the same loads (past the last slab they read nothing),
+  // so that the compiler's count of loads in flight stays exact: a load under
+  // a branch makes it wait for all of them before the next MFMA.
+  u32x4_t xv[kStXd][XP];
+#pragma unroll
+  for (int i = 0; i < kStXd; ++i) xload(xv[i], i);
+#pragma unroll
+  for (int j = 0; j < kStRing; ++j) issue(rc[j], rm[j], j);
+  xstore(xv[0], 0);
+  __syncthreads();
+
+  uint32_t pmask, pmagic;   // see mrow_kernel
+  asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(pmask));
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(pmagic));
+  // A-operand offsets of row block 0 (row col_l) in step 0; block rb adds 16·rb
+  // rows, step st 128·st elements
+  int aoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p0 = AFF ? 8 * (i >> 1) + 4 * (g & 1) + 2 + (i & 1) - 2 * (g >> 1) : 4 * g + i;
+    aoff[i] = col_l * kSlabCodes + ((p0 ^ col_l) << 3);
+  }
+  f32x4_t acc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto slab = [&](const u32x4_t (&c2)[2], const u32x4_t& m, int s, int b) {
+    const int w = L.width(s);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int st = 2 * kh + j;
+      if (128 * st >= w) break;   // a narrow last slab ends early (uniform)
+      const int e0 = b * XB + st * 128;   // the step's first element in row 0 of the buffer
+      if constexpr (AFF) {
+        const uint32_t m0 = m[2 * j];
+        const uint32_t m1 = 128 * st + 64 < w ? m[2 * j + 1] : 0u;
+        const float gs[2] = {bf16_lo(m0), bf16_lo(m1)};
+        const float gc[2] = {__builtin_fmaf(-128.0f, bf16_lo(m0), bf16_hi(m0)),
+                             __builtin_fmaf(-128.0f, bf16_lo(m1), bf16_hi(m1))};
+        // each register one group in every lane (see mrow_kernel)
+        const auto s20 = __builtin_amdgcn_permlane32_swap(c2[j][2], c2[j][0], false, false);
+        const auto s31 = __builtin_amdgcn_permlane32_swap(c2[j][3], c2[j][1], false, false);
+        const uint32_t wg[2][2] = {{s20[0], s31[0]}, {s20[1], s31[1]}};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // the group's A operands and row sums first: one LDS wait per group
+          u32x4_t a[2][RB];
+          f32x4_t xg[RB];
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              a[jj][rb] = *reinterpret_cast<const u32x4_t*>(&xs[aoff[2 * h + jj] + rb * 16 * kSlabCodes + e0]);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            xg[rb] = *reinterpret_cast<const f32x4_t*>(&xsum[(b * 8 + 2 * st + h) * XR + 16 * rb + 4 * g]);
+          __builtin_amdgcn_sched_barrier(0);   // (the scheduler would interleave them one by one)
+          f32x4_t pg[RB];
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) pg[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            u32x4_t bq;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bq[r] = ((wg[h][jj] >> (4 * r)) & pmask) | pmagic;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              pg[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[jj][rb]),
+                                                               __builtin_bit_cast(bf16x8_t, bq), pg[rb], 0, 0, 0);
+          }
+          // rows 16rb + 4g + r: acc += s·P + (b − 128·s)·Σx for group 2st + h
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[rb][r] = __builtin_fmaf(gc[h], xg[rb][r], __builtin_fmaf(gs[h], pg[rb][r], acc[rb][r]));
+          }
+        }
+      } else {
+        const float sc = e8m0_scale((m[st] >> (8 * g)) & 0xFFu);
+#pragma unroll
+        for (int hq = 0; hq < 4; hq += 2) {
+          // two words' A operands first: one LDS wait per pair
+          u32x4_t a[2][RB];
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              a[q][rb] = *reinterpret_cast<const u32x4_t*>(&xs[aoff[hq + q] + rb * 16 * kSlabCodes + e0]);
+          __builtin_amdgcn_sched_barrier(0);   // (the scheduler would interleave them one by one)
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const u32x4_t bq = mxfp4_word_to_bf16x8(c2[j][hq + q], sc);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[q][rb]),
+                                                                __builtin_bit_cast(bf16x8_t, bq), acc[rb], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+  for (int s0 = 0; s0 < ns; s0 += kStRing) {
+#pragma unroll
+    for (int j = 0; j < kStRing; ++j) {
+      const int s = s0 + j;   // s % kStXd == j % kStXd, s & 1 == j & 1
+      xload(xv[j % kStXd], s + kStXd);
+      if (active && s < ns) slab(rc[j], rm[j], s, j & 1);
+      issue(rc[j], rm[j], s + kStRing);
+      if (s + 1 < ns) xstore(xv[(j + 1) % kStXd], (j + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+  // the second half's sums join the first's through LDS (the slab buffers
+  // are free after the last barrier), then the first half stores
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(xs);   // [RB][4 column waves][64 lanes]
+  if (kh == 1 && active) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) red[(rb * 4 + cw) * 64 + lane] = acc[rb];
+  }
+  __syncthreads();
+  if (kh == 0 && col < c1) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const f32x4_t o = red[(rb * 4 + cw) * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rb + 4 * g + r;
+        if (row < t) y[int64_t(row) * n + col] = f32_to_bf16(acc[rb][r] + o[r]);
+      }
+    }
+  }
+}
+
 }  // namespace
 
 int launch_mrow(const GemmArgs& a, void* stream) {
@@ -284,16 +512,30 @@ int launch_mrow(const GemmArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   DevInfo di{};
   const int cus = device_info(&di) == 0 && di.cus > 0 ? di.cus : 256;
-  const MrowPlan p = mrow_plan(a.n, a.d, cus);
-  const dim3 grid(unsigned((a.n + p.cpw - 1) / p.cpw)), block(unsigned(64 * p.ncw * p.kq));
-  const size_t lds = mrow_lds_bytes(a.f, a.t, a.d);
   const uint8_t* codes = a.packed + l.codes_offset;
   const uint8_t* meta = a.packed + l.meta_offset;
   const uint32_t cb = uint32_t(int64_t(a.n) * (a.d / 2)), mb = uint32_t(l.meta_bytes);
+  constexpr int AF = QMM_AFFINE4_G64, MX = QMM_MXFP4_G32;
+  if (a.t > kMrowMaxT) {
+    const MrowPlan p = mrow_stream_plan(a.n, cus);
+    const dim3 grid(unsigned((a.n + p.cpw - 1) / p.cpw)), block(512);
+    const size_t lds = mrow_stream_lds_bytes(a.f, a.t);
+    auto go = [&](auto kern) {
+      launch_kernel_lds(kern, grid, block, lds, s, codes, meta, cb, mb, a.t, a.n, a.d, p.cpw, a.x, a.y);
+    };
+    const int rb = mrow_stream_blocks(a.t);
+    if (a.f == AF)
+      rb == 2 ? go(mrow_stream_kernel<AF, 2>) : rb == 3 ? go(mrow_stream_kernel<AF, 3>) : go(mrow_stream_kernel<AF, 4>);
+    else
+      rb == 2 ? go(mrow_stream_kernel<MX, 2>) : rb == 3 ? go(mrow_stream_kernel<MX, 3>) : go(mrow_stream_kernel<MX, 4>);
+    return int(hipGetLastError());
+  }
+  const MrowPlan p = mrow_plan(a.n, a.d, cus);
+  const dim3 grid(unsigned((a.n + p.cpw - 1) / p.cpw)), block(unsigned(64 * p.ncw * p.kq));
+  const size_t lds = mrow_lds_bytes(a.f, a.t, a.d);
   auto go = [&](auto kern) {
     launch_kernel_lds(kern, grid, block, lds, s, codes, meta, cb, mb, a.t, a.n, a.d, p.cpw, p.ncw, a.x, a.y);
   };
-  constexpr int AF = QMM_AFFINE4_G64, MX = QMM_MXFP4_G32;
   if (a.f == AF && a.t <= kMrowG2MaxT)
     p.kq == 4 ? go(mrow_kernel<AF, 4, true>) : p.kq == 2 ? go(mrow_kernel<AF, 2, true>) : go(mrow_kernel<AF, 1, true>);
   else if (a.f == AF)

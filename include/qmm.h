@@ -91,9 +91,10 @@ size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
  * per format and shape by a call like this one, as the explicit per-format
  * byte counts that fixed the NULL-scale crash of "Colibri Kimi K3 Metal
  * 后端实现全解析", Phase 10 (fmt_scale_bytes).
- *   2 <= t <= 16 rows on the multi-row kernel (see qmm_gemm: MXFP4 weights
- *     with n >= 5120 or t <= 8, affine weights with n >= 8192, while the t
- *     rows fit the kernel's LDS): 0.
+ *   2 <= t <= 64 rows on the multi-row kernel (see qmm_gemm: for t <= 16
+ *     MXFP4 weights with n >= 5120 or t <= 8, affine weights with
+ *     n >= 8192, while the t rows fit the kernel's LDS; for 17 <= t <= 64
+ *     n >= 6144, or n >= 2048 with d <= 2048): 0.
  *   other 2 <= t <= 64 rows: one fp32 [t][n] plane per 512-code slab of d,
  *     ceil(d/512)·t·n·4 bytes (0.66 MB for t = 4, n = 4096, d = 5120).
  *   t > 64, affine weights: the activations converted to fp16 (t·d·2 bytes),
@@ -179,6 +180,10 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
  *     affine weights; at d = 5120 affine t <= 14, MXFP4 t <= 15): every
  *     weight read once for all rows, no workspace, one kernel.  Affine codes enter bf16 MFMAs as the exact
  *     values 128 + q and each group's scale and bias follow in fp32.
+ *   17 <= t <= 64 with n >= 6144, or n >= 2048 and d <= 2048: the same
+ *     kernel with the rows streamed through LDS one 512-code slab at a
+ *     time (two buffers of 16·ceil(t/16) rows, at most 132 KiB): every
+ *     weight read once for all rows, no workspace, one kernel.
  *   other 2 <= t <= 64 (with the workspace): split along d, each 512-code slab's
  *     fp32 partial sums in the workspace, added in slab order by a second
  *     kernel.  Affine codes enter bf16 MFMAs as the exact values 128 + q and
@@ -347,8 +352,9 @@ qmm_status qmm_profile_next(void* start_event, void* stop_event);
  *   QMM_KERNEL_GROUPED_MATMUL  qmm_grouped_gemm runs the matmul kernel also
  *                              where every segment has one row.
  *   QMM_KERNEL_MULTI_ROW       qmm_gemm runs the multi-row kernel for every
- *                              shape it takes (2 <= t <= 16, rows within its
- *                              LDS), others return QMM_E_UNSUPPORTED; no
+ *                              shape it takes (2 <= t <= 16 with the rows
+ *                              within its LDS, or 17 <= t <= 64 streamed),
+ *                              others return QMM_E_UNSUPPORTED; no
  *                              workspace.
  * A setting that does not concern a call leaves it as under AUTO.
  * qmm_workspace_bytes reports the workspace of the kernel the setting

@@ -136,10 +136,16 @@ int main() {
   // the allocation-free GEMM: the static scratch replaces the workspace; too
   // large a shape is refused before the scratch is looked up
   g_called = "none";
-  EXPECT(qmm_gemm_noalloc(A, P(), 64, 65536, 5120, B(), B(), nullptr) == QMM_E_WORKSPACE && g_called == "none");
+  EXPECT(qmm_gemm_noalloc(A, P(), 64, 6000, 32768, B(), B(), nullptr) == QMM_E_WORKSPACE && g_called == "none");
   EXPECT(strstr(qmm_last_error(), "64 MiB") != nullptr);
   EXPECT(qmm_gemm_noalloc(A, P(), 8, 13824, 5120, B(), B(), nullptr) == QMM_OK && g_called == "mrow");
   EXPECT(qmm_gemm_noalloc(A, P(), 8, 4096, 5120, B(), B(), nullptr) == QMM_OK && g_called == "skinny");
+  // 17 <= t <= 64: streamed multi-row rows from 6144 columns (or 2048 where
+  // d <= 2048), the few-row kernel below
+  EXPECT(qmm_gemm_noalloc(A, P(), 40, 13824, 5120, B(), B(), nullptr) == QMM_OK && g_called == "mrow");
+  EXPECT(qmm_gemm_noalloc(M, P(), 40, 2048, 2048, B(), B(), nullptr) == QMM_OK && g_called == "mrow");
+  EXPECT(qmm_gemm_noalloc(M, P(), 40, 2047, 2048, B(), B(), nullptr) == QMM_OK && g_called == "skinny");
+  EXPECT(qmm_gemm_noalloc(A, P(), 40, 6143, 5120, B(), B(), nullptr) == QMM_OK && g_called == "skinny");
   EXPECT(g_ws == g_scratch);
   g_fail = 1;   // the scratch lookup fails: a HIP status, with the HIP text
   EXPECT(qmm_gemm_noalloc(A, P(), 8, 4096, 5120, B(), B(), nullptr) == QMM_E_HIP);
@@ -149,7 +155,10 @@ int main() {
   EXPECT(qmm_set_kernel(QMM_KERNEL_MULTI_ROW) == QMM_OK);
   EXPECT(qmm_gemm(A, P(), 8, 1024, 5120, B(), B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow");
   g_called = "none";
-  EXPECT(qmm_gemm(A, P(), 17, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_E_UNSUPPORTED && g_called == "none");
+  EXPECT(qmm_gemm(A, P(), 17, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow");
+  EXPECT(qmm_gemm(M, P(), 64, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow");
+  g_called = "none";
+  EXPECT(qmm_gemm(A, P(), 65, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_E_UNSUPPORTED && g_called == "none");
   EXPECT(qmm_gemm(A, P(), 15, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_E_UNSUPPORTED && g_called == "none");
   EXPECT(strstr(qmm_last_error(), "multi-row") != nullptr);
   EXPECT(qmm_set_kernel(QMM_KERNEL_AUTO) == QMM_OK);

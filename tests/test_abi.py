@@ -61,17 +61,23 @@ def test_packed_bytes_rejects_bad_shapes():
 
 def test_workspace_contract():
     # the multi-row kernel (2 <= t <= 16, rows within its LDS; MXFP4 from 5120
-    # columns or up to 8 rows, affine from 8192 columns) takes none
+    # columns or up to 8 rows, affine from 8192 columns; 17 <= t <= 64 from
+    # 6144 columns, or from 2048 where d <= 2048) takes none
     assert qmm.qmm_workspace_bytes(A, 2, 13824, 5120) == 0
     assert qmm.qmm_workspace_bytes(A, 14, 13824, 5120) == 0
     assert qmm.qmm_workspace_bytes(M, 8, 1024, 5120) == 0
     assert qmm.qmm_workspace_bytes(M, 15, 5120, 5120) == 0
+    assert qmm.qmm_workspace_bytes(A, 17, 13824, 5120) == 0
+    assert qmm.qmm_workspace_bytes(M, 64, 6144, 8192) == 0
+    assert qmm.qmm_workspace_bytes(A, 40, 2048, 2048) == 0
     # split-K partials of qmm_gemm for the other 2 <= t <= 64: one fp32 [t][n]
     # plane per 512-code slab of d; nothing for other t or invalid shapes
     assert qmm.qmm_workspace_bytes(A, 2, 4096, 5120) == 10 * 2 * 4096 * 4
     assert qmm.qmm_workspace_bytes(A, 15, 13824, 5120) == 10 * 15 * 13824 * 4   # 15 rows exceed its LDS
     assert qmm.qmm_workspace_bytes(M, 12, 1024, 5120) == 10 * 12 * 1024 * 4
-    assert qmm.qmm_workspace_bytes(A, 17, 13824, 5120) == 10 * 17 * 13824 * 4
+    assert qmm.qmm_workspace_bytes(A, 17, 4096, 5120) == 10 * 17 * 4096 * 4
+    assert qmm.qmm_workspace_bytes(M, 64, 6143, 2560) == 5 * 64 * 6143 * 4
+    assert qmm.qmm_workspace_bytes(A, 40, 2047, 2048) == 4 * 40 * 2047 * 4
     assert qmm.qmm_workspace_bytes(M, 64, 300, 1088) == 3 * 64 * 300 * 4
     for t in (1, 2048, 300):
         assert qmm.qmm_workspace_bytes(M, t, 13824, 5120) == 0
@@ -106,8 +112,8 @@ def test_noalloc_limit_is_checked_on_the_host():
     # the allocation-free GEMM refuses shapes whose split-K partials exceed its
     # 64 MiB static scratch before looking up the scratch or launching anything
     lib = qmm.load()
-    assert qmm.qmm_workspace_bytes(A, 64, 65536, 5120) > 64 << 20
-    assert lib.qmm_gemm_noalloc(A, P, 64, 65536, 5120, P, P, None) == E_WS
+    assert qmm.qmm_workspace_bytes(A, 64, 6000, 32768) > 64 << 20
+    assert lib.qmm_gemm_noalloc(A, P, 64, 6000, 32768, P, P, None) == E_WS
     assert "64 MiB" in qmm.qmm_last_error()
     assert lib.qmm_gemm_noalloc(A, P + 8, 8, 16, 64, P, P, None) == E_ALIGN
     assert lib.qmm_gemm_noalloc(A, P, 0, 16, 64, P, P, None) == E_ARG
@@ -150,12 +156,14 @@ def test_kernel_override_sizes_and_refusals(kernel_auto_after):
     qmm.qmm_set_kernel(qmm.QMM_KERNEL_MULTI_ROW)
     assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == 0
     assert qmm.qmm_workspace_bytes(A, 4, 1024, 5120) == 0                  # narrow matrices too
-    assert qmm.qmm_workspace_bytes(A, 17, 13824, 5120) == 0                # refused below
-    assert lib.qmm_gemm(A, P, 17, 16, 64, P, P, None, 0, None) == E_UNSUPPORTED
+    assert qmm.qmm_workspace_bytes(A, 17, 13824, 5120) == 0                # streamed rows
+    assert qmm.qmm_workspace_bytes(M, 64, 13824, 5120) == 0
+    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5120) == 0                # refused below
+    assert lib.qmm_gemm(A, P, 65, 16, 64, P, P, None, 0, None) == E_UNSUPPORTED
     assert "multi-row" in qmm.qmm_last_error()
     assert lib.qmm_gemm(A, P, 1, 16, 64, P, P, None, 0, None) == E_UNSUPPORTED
     assert lib.qmm_gemm(A, P, 15, 16, 5120, P, P, None, 0, None) == E_UNSUPPORTED   # rows beyond its LDS
-    assert lib.qmm_gemm_noalloc(A, P, 17, 16, 64, P, P, None) == E_UNSUPPORTED
+    assert lib.qmm_gemm_noalloc(A, P, 65, 16, 64, P, P, None) == E_UNSUPPORTED
     qmm.qmm_set_kernel(qmm.QMM_KERNEL_GROUPED_MATMUL)
     assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == 0                 # no effect on qmm_gemm
     assert qmm.qmm_workspace_bytes(A, 4, 4096, 5120) == 10 * 4 * 4096 * 4

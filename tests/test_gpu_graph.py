@@ -79,6 +79,12 @@ def test_graph_replay_matches_eager():
     pr = torch.empty(qmm.qmm_packed_bytes(M, nr, dr), dtype=torch.uint8, device=DEV)
     qmm.qmm_pack(M, nr, dr, dev(wr.codes), dev(wr.e8m0), None, pr)
     assert qmm.qmm_workspace_bytes(M, tr, nr, dr) == 0
+    # 40 rows streamed through the multi-row kernel (no workspace either)
+    ns, ds, ts = 2100, 1024, 40
+    ws_ = synth.affine_weights(908, ns, ds)
+    ps = torch.empty(qmm.qmm_packed_bytes(A, ns, ds), dtype=torch.uint8, device=DEV)
+    qmm.qmm_pack(A, ns, ds, dev(ws_.codes), dev(ws_.scale), dev(ws_.bias), ps)
+    assert qmm.qmm_workspace_bytes(A, ts, ns, ds) == 0
     _, r, bias = synth.router_inputs(904, t=t, d=dm, experts=ne)
     r_d, bias_d = dev(r), torch.from_numpy(np.asarray(bias, np.float32)).to(DEV)
 
@@ -89,6 +95,7 @@ def test_graph_replay_matches_eager():
     wsu = torch.empty(qmm.qmm_workspace_bytes(A, tg, ng, du) // 4, dtype=torch.float32, device=DEV)
     xm = torch.empty(t, dm, dtype=torch.int16, device=DEV)
     xr = torch.empty(tr, dr, dtype=torch.int16, device=DEV)
+    xs = torch.empty(ts, ds, dtype=torch.int16, device=DEV)
     # the GEMM split along K (two kernels each, fp32 partials in a workspace):
     # 4 rows through the few-row kernel, 70 rows through the split tile kernel
     ws4 = torch.empty(qmm.qmm_workspace_bytes(A, 4, ng, dg) // 4, dtype=torch.float32, device=DEV)
@@ -100,6 +107,7 @@ def test_graph_replay_matches_eager():
         "gemm_split4": (torch.empty(4, ng, dtype=torch.int16, device=DEV), 0x7FC0),
         "gemm_split70": (torch.empty(tg, ng, dtype=torch.int16, device=DEV), 0x7FC0),
         "gemm_multi_row6": (torch.empty(tr, nr, dtype=torch.int16, device=DEV), 0x7FC0),
+        "gemm_multi_row40": (torch.empty(ts, ns, dtype=torch.int16, device=DEV), 0x7FC0),
         "scores": (torch.empty(t, ne, dtype=torch.float32, device=DEV), float("nan")),
         "topk": (torch.empty(t, k, dtype=torch.int32, device=DEV), -7),
         "seg_expert": (torch.empty(ne, dtype=torch.int32, device=DEV), -7),
@@ -117,6 +125,7 @@ def test_graph_replay_matches_eager():
         xu.copy_(dev(synth.activations(seed, synth.S_X, tg, du, sub=3)))
         xm.copy_(dev(synth.activations(seed, synth.S_X, t, dm, sub=2)))
         xr.copy_(dev(synth.activations(seed, synth.S_X, tr, dr, sub=4)))
+        xs.copy_(dev(synth.activations(seed, synth.S_X, ts, ds, sub=5)))
 
     def reset():
         for buf, fill in outs.values():
@@ -128,6 +137,7 @@ def test_graph_replay_matches_eager():
         qmm.qmm_gemm(A, pg, 4, ng, dg, xg, O["gemm_split4"], ws4)
         qmm.qmm_gemm(A, pg, tg, ng, dg, xg, O["gemm_split70"], ws70)
         qmm.qmm_gemm(M, pr, tr, nr, dr, xr, O["gemm_multi_row6"], None)
+        qmm.qmm_gemm(A, ps, ts, ns, ds, xs, O["gemm_multi_row40"], None)
         qmm.qmm_route(xm, t, dm, r_d, ne, bias_d, k, O["scores"], O["topk"], O["seg_expert"],
                       O["seg_offsets"], O["row_index"])
         qmm.qmm_grouped_gemm_swiglu(M, gu, gsz, ne, 2 * ni, dm, xm, t, O["row_index"], O["seg_expert"],

@@ -782,7 +782,7 @@ def kernel_takes(k, fmt, t, d):
     if k == qmm.QMM_KERNEL_FEW_ROW:
         return 2 <= t <= 64
     if k == qmm.QMM_KERNEL_MULTI_ROW:
-        return 2 <= t <= 16 and mrow_lds_bytes(fmt, t, d) <= 160 * 1024
+        return 2 <= t <= 16 and mrow_lds_bytes(fmt, t, d) <= 160 * 1024 or 17 <= t <= 64
     return True
 
 
@@ -807,8 +807,7 @@ def test_forced_kernels_integer_exact(fmt, t, n, d, kernel_auto_after):
     integer activations: every sum is exact in fp32, so the GEMV, the few-row
     kernel, the multi-row kernel and the tile kernel (split along K or not)
     must all return the oracle's sums rounded to bf16, bit for bit.  The
-    few-row kernel refuses t = 1 and t > 64, the multi-row kernel t = 1 and
-    t > 16."""
+    few-row and multi-row kernels refuse t = 1 and t > 64."""
     say("forced kernels integer exact", fmt, t, n, d)
     rng = np.random.default_rng(40 + t)
     x = synth.bf16_bits(rng.integers(-3, 4, size=(t, d)).astype(float))
@@ -835,7 +834,8 @@ def test_forced_kernels_integer_exact(fmt, t, n, d, kernel_auto_after):
 
 
 @pytest.mark.parametrize("fmt,t,n,d", [(A, 48, 1000, 1024), (M, 33, 300, 3584), (A, 200, 520, 2048),
-                                       (A, 3, 259, 576), (M, 12, 700, 2048)])
+                                       (A, 3, 259, 576), (M, 12, 700, 2048), (M, 64, 1100, 5120),
+                                       (A, 17, 700, 4096)])
 def test_forced_kernels_parity(fmt, t, n, d, kernel_auto_after):
     """Random weights and activations under every kernel setting that takes
     the shape, each within the oracle's bound."""
@@ -876,7 +876,11 @@ def run_gemm_multi_row(fmt, packed, n, d, x_bits):
 
 def auto_picks_multi_row(fmt, t, n, d):
     """The library's own choice for qmm_gemm (no workspace asked for)."""
-    return kernel_takes(qmm.QMM_KERNEL_MULTI_ROW, fmt, t, d) and (n >= 5120 or t <= 8 if fmt == M else n >= 8192)
+    if not kernel_takes(qmm.QMM_KERNEL_MULTI_ROW, fmt, t, d):
+        return False
+    if t > 16:
+        return n >= 6144 or (d <= 2048 and n >= 2048)
+    return n >= 5120 or t <= 8 if fmt == M else n >= 8192
 
 
 # launch shapes covered: 1 to 8 column waves per workgroup; the slabs shared
@@ -966,11 +970,92 @@ def test_gemm_multi_row_random_shapes(seed, kernel_auto_after):
     assert_parity(y, yr, ar, f"gemm multi-row random {seed}: fmt {fmt} {t}x{n}x{d}")
 
 
+# the streaming form (17 <= t <= 64, two or four row blocks of 16): one
+# narrow slab; a narrow last slab; fewer than 16 columns; a workgroup of one
+# to four column waves; more workgroups than 256 CUs (n > 16384); t just past
+# each row block; the decode matrix at 32, 48 and 64 rows
+MULTI_ROW_STREAM_SHAPES = [(A, 17, 300, 64), (A, 32, 1000, 1088), (A, 64, 13824, 5120), (A, 48, 4099, 5184),
+                           (A, 33, 33000, 640), (A, 50, 3, 128), (A, 40, 16385, 2048), (M, 17, 7, 32),
+                           (M, 64, 257, 3584), (M, 49, 13824, 5120), (M, 63, 16500, 1056), (M, 20, 5121, 2080),
+                           (M, 32, 13824, 5120), (M, 35, 40000, 96)]
+
+
+@pytest.mark.parametrize("fmt,t,n,d", MULTI_ROW_STREAM_SHAPES)
+def test_gemm_multi_row_streamed(fmt, t, n, d, kernel_auto_after):
+    """The multi-row kernel's streaming form against the oracle; where the
+    library picks it by itself, the call without a forced setting gives the
+    same bits."""
+    say("gemm multi-row streamed", fmt, t, n, d)
+    x = synth.activations(9600 + t, synth.S_X, t, d)
+    if fmt == A:
+        w = synth.affine_weights(9700 + n, n, d)
+        p = pack_affine(w)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(9800 + n, n, d)
+        p = pack_mxfp4(w)
+        yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    y = run_gemm_multi_row(fmt, p, n, d, x)
+    assert_parity(y, yr, ar, f"gemm multi-row streamed fmt={fmt} {t}x{n}x{d}")
+    if auto_picks_multi_row(fmt, t, n, d):
+        assert qmm.qmm_workspace_bytes(fmt, t, n, d) == 0
+        ya = nan_out(t, n)
+        qmm.qmm_gemm(fmt, p, t, n, d, dev(x), ya, None)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_u16(ya), y)
+
+
+@pytest.mark.parametrize("fmt,t,n,d", [(A, 64, 13824, 5120), (A, 37, 1000, 5184), (M, 64, 13824, 5120),
+                                       (M, 18, 6000, 1568)])
+def test_gemm_multi_row_streamed_integer_exact(fmt, t, n, d, kernel_auto_after):
+    """Integer weights and activations through the streaming form: the
+    oracle's exact sums rounded to bf16, bit for bit the few-row kernel's."""
+    say("gemm multi-row streamed integer exact", fmt, t, n, d)
+    rng = np.random.default_rng(170 + t)
+    x = synth.bf16_bits(rng.integers(-3, 4, size=(t, d)).astype(float))
+    if fmt == A:
+        w = integer_affine(180 + t, n, d)
+        p = pack_affine(w)
+        yr, _ = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(180 + t, n, d, 127, 1)
+        p = pack_mxfp4(w)
+        yr, _ = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    assert np.all(np.abs(yr) < 2 ** 24)
+    want = oracle.f64_to_bf16_bits(yr)
+    assert np.array_equal(run_gemm_multi_row(fmt, p, n, d, x), want)
+    assert np.array_equal(run_gemm_forced(qmm.QMM_KERNEL_FEW_ROW, fmt, p, n, d, x), want)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_gemm_multi_row_streamed_random_shapes(seed, kernel_auto_after):
+    """Seeded random shapes on the streaming form: t from 17 to 64, n from 1
+    to 40000, d any multiple of the group up to 6144, both formats."""
+    rng = np.random.default_rng(2900 + seed)
+    fmt = A if seed % 2 == 0 else M
+    g = 64 if fmt == A else 32
+    t = int(rng.integers(17, 65))
+    n = int(rng.choice([rng.integers(1, 300), rng.integers(300, 9000), rng.integers(9000, 40001)]))
+    d = g * int(rng.integers(1, 6144 // g + 1))
+    say("gemm multi-row streamed random", seed, "fmt", fmt, "t n d", t, n, d)
+    x = synth.activations(2910 + seed, synth.S_X, t, d)
+    if fmt == A:
+        w = synth.affine_weights(2920 + seed, n, d)
+        p = pack_affine(w)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(2920 + seed, n, d)
+        p = pack_mxfp4(w)
+        yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    y = run_gemm_multi_row(fmt, p, n, d, x)
+    assert_parity(y, yr, ar, f"gemm multi-row streamed random {seed}: fmt {fmt} {t}x{n}x{d}")
+
+
 def test_gemm_multi_row_repeated_and_shrinking(kernel_auto_after):
     """Calls in a row on one stream, the second with fewer rows and columns
     and a shorter reduction: nothing carries over between launches."""
     say("gemm multi-row repeated")
-    for t, n, d in [(12, 13824, 5120), (3, 999, 1088), (12, 13824, 5120)]:
+    for t, n, d in [(12, 13824, 5120), (3, 999, 1088), (12, 13824, 5120), (64, 13824, 5120), (20, 999, 1088)]:
         x = synth.activations(9400 + t, synth.S_X, t, d)
         w = synth.affine_weights(9500 + n, n, d)
         y = run_gemm_multi_row(A, pack_affine(w), n, d, x)

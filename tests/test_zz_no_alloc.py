@@ -72,11 +72,11 @@ def both(fmt, p, t, n, d, x):
     return y0.cpu().numpy().view(np.uint16), y1.cpu().numpy().view(np.uint16)
 
 
-# (format, n, d, first t, second t): few-row split-K (16 < t <= 64, and
-# narrow affine matrices below that), the tile kernel split along K (t > 64
+# (format, n, d, first t, second t): few-row split-K (16 < t <= 64 on
+# matrices of under 6144 columns, and narrow affine matrices below that), the tile kernel split along K (t > 64
 # with few tiles, d a multiple of 512), and the affine tile kernel unsplit
 # (its fp16 activations in the scratch)
-CASES = [(A, 13824, 5120, 40, 20), (M, 1000, 3584, 64, 17), (A, 4096, 2048, 12, 3),
+CASES = [(A, 4096, 5120, 40, 20), (M, 1000, 3584, 64, 17), (A, 4096, 2048, 12, 3),
          (A, 1000, 2048, 200, 70), (M, 700, 3072, 97, 66), (A, 4352, 1024, 2048, 300)]
 
 
@@ -104,14 +104,15 @@ def test_noalloc_single_row_and_limit():
     yr, ar = ref(x)
     assert oracle.check(y.cpu().numpy().view(np.uint16), yr, ar)["ok"]
     # partials beyond the 64 MiB scratch are refused before any launch
-    big_n = 65536
-    assert qmm.qmm_workspace_bytes(A, 64, big_n, 5120) > 64 << 20
+    big_n, big_d = 6000, 32768
+    assert qmm.qmm_workspace_bytes(A, 64, big_n, big_d) > 64 << 20
     with pytest.raises(qmm.QmmError) as ei:
-        qmm.qmm_gemm_noalloc(A, 1 << 20, 64, big_n, 5120, 1 << 20, 1 << 20)
+        qmm.qmm_gemm_noalloc(A, 1 << 20, 64, big_n, big_d, 1 << 20, 1 << 20)
     assert ei.value.name == "QMM_E_WORKSPACE"
 
 
-@pytest.mark.parametrize("fmt,n,d,t", [(A, 13824, 5120, 8), (M, 1000, 3584, 3)])
+@pytest.mark.parametrize("fmt,n,d,t", [(A, 13824, 5120, 8), (M, 1000, 3584, 3), (M, 13824, 5120, 33),
+                                       (A, 2100, 1024, 40)])
 def test_noalloc_multi_row_takes_no_scratch(fmt, n, d, t):
     """Shapes on the multi-row kernel need no workspace: the allocation-free
     call runs the same kernel as qmm_gemm, bit for bit, twice in a row."""
