@@ -5,8 +5,9 @@
 One step runs every row of the hot path once, each on inputs already resident
 in HBM:
   decode    affine GEMV, T=1, D=5120, N=13824 (the headline), then its
-            deferred-dequantisation variant (int8 activations) and a batch of
-            8 rows (qmm_gemm: the multi-row kernel) on the same weights
+            deferred-dequantisation variant (int8 activations) and batches of
+            8 and 32 rows (qmm_gemm: the multi-row kernel, its rows held in
+            LDS, then streamed) on the same weights
   qkv       a Q/K/V triple (5120, 1024, 1024 rows of D=5120) sharing one x: one
             GEMV over the matrices packed as one, then the three separately
   prefill   affine GEMM, T=2048, D=5120, N=13824 (bf16 MFMA)
@@ -206,6 +207,16 @@ def main(argv=None) -> int:
         b8 = n1 * d1 * 36 // 64 + 2 * 8 * d1 + 2 * 8 * n1
         work["decode"].append((lambda s: qmm.qmm_gemm(A, copies[(s + 6) % len(copies)], 8, n1, d1, x8, y8, ws8),
                                "gemm_t8", b8, 2.0 * 8 * n1 * d1))
+        # and a batch of 32 rows (the multi-row kernel with its rows streamed)
+        x32h = synth.activations(synth.seed_of(1), synth.S_X, 32, d1, sub=4)
+        x32 = T(x32h)
+        y32 = torch.empty(32, n1, dtype=torch.int16, device=dev)
+        ctx["batch32"] = dict(w=w1, x=x32h, y=y32)
+        ws32b = qmm.qmm_workspace_bytes(A, 32, n1, d1)
+        ws32 = torch.empty(ws32b // 4, dtype=torch.float32, device=dev) if ws32b else None
+        b32 = n1 * d1 * 36 // 64 + 2 * 32 * d1 + 2 * 32 * n1
+        work["decode"].append((lambda s: qmm.qmm_gemm(A, copies[(s + 18) % len(copies)], 32, n1, d1, x32, y32, ws32),
+                               "gemm_t32", b32, 2.0 * 32 * n1 * d1))
         # the small GEMV workload (T=1, D=256, N=512): 73.7 KB of weights, held
         # in cache after the first launch -- latency, not bandwidth, is its measure
         c0 = synth.CONFIGS[0]
@@ -489,7 +500,7 @@ def main(argv=None) -> int:
         "dtype": "bf16", "data": "synthetic (seeded counter-based generator; no weights or datasets)",
         "config": {"workload": synth.CONFIGS[1]["name"], "t": 1, "d": d1, "n": n1,
                    "format": "affine4_g64", "rotation_copies": args.rotate,
-                   "step": "decode GEMV (+ int8 variant, + 8-row batch) + fused Q/K/V GEMV (and the three separately) + prefill GEMM"
+                   "step": "decode GEMV (+ int8 variant, + 8- and 32-row batches) + fused Q/K/V GEMV (and the three separately) + prefill GEMM"
                            " + MoE decode grouped GEMV x2 + MoE prefill route + grouped GEMM"
                            " + expert FFN (gate_up with SwiGLU, down, combine)"
                    if rows == ["decode", "qkv", "prefill", "moe_dec", "moe_pre", "moe_ffn"] else ",".join(rows)},
@@ -737,6 +748,10 @@ def oracle_phase(ctx, single_thread=True):
         c = ctx["batch8"]
         yr, ar = oracle.gemm_affine(c["x"], c["w"].codes, c["w"].scale, c["w"].bias)
         rec("decode_batch8", oracle.check(c["y"], yr, ar), yr.size, "every output of the 8-row batch")
+    if "batch32" in ctx:
+        c = ctx["batch32"]
+        yr, ar = oracle.gemm_affine(c["x"], c["w"].codes, c["w"].scale, c["w"].bias)
+        rec("decode_batch32", oracle.check(c["y"], yr, ar), yr.size, "every output of the 32-row batch")
     # config 2: the weights dequantised once, then 64 of the 2048 rows
     if "cfg2" in ctx:
         c = ctx["cfg2"]
