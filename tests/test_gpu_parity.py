@@ -970,14 +970,16 @@ def test_gemm_multi_row_random_shapes(seed, kernel_auto_after):
     assert_parity(y, yr, ar, f"gemm multi-row random {seed}: fmt {fmt} {t}x{n}x{d}")
 
 
-# the streaming form (17 <= t <= 64, two or four row blocks of 16): one
+# the streaming form (17 <= t <= 64, two to four row blocks of 16): one
 # narrow slab; a narrow last slab; fewer than 16 columns; a workgroup of one
 # to four column waves; more workgroups than 256 CUs (n > 16384); t just past
-# each row block; the decode matrix at 32, 48 and 64 rows
+# each row block; the decode matrix at 32, 48 and 64 rows; d = 65536
 MULTI_ROW_STREAM_SHAPES = [(A, 17, 300, 64), (A, 32, 1000, 1088), (A, 64, 13824, 5120), (A, 48, 4099, 5184),
                            (A, 33, 33000, 640), (A, 50, 3, 128), (A, 40, 16385, 2048), (M, 17, 7, 32),
                            (M, 64, 257, 3584), (M, 49, 13824, 5120), (M, 63, 16500, 1056), (M, 20, 5121, 2080),
-                           (M, 32, 13824, 5120), (M, 35, 40000, 96)]
+                           (M, 32, 13824, 5120), (M, 35, 40000, 96),
+                           # the largest reduction axis (128 slabs; MXFP4 ending in a narrow slab)
+                           (A, 64, 130, 65536), (A, 17, 700, 65536), (M, 33, 97, 65504)]
 
 
 @pytest.mark.parametrize("fmt,t,n,d", MULTI_ROW_STREAM_SHAPES)
