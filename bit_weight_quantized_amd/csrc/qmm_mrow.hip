@@ -285,7 +285,8 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
 // rows of the next two slabs: while slab s is multiplied from one buffer,
 // the rows of slab s + 2 are loaded into registers and those of slab s + 1,
 // which landed meanwhile, are stored into the other buffer (zeros past T and
-// past d), with their affine group sums taken across lanes on the way; one
+// past d), with their affine group sums taken on the way (bf16 dots against
+// (1, 1), then across the eight lanes of a group); one
 // barrier per slab.  Every weight is read once for all rows and each of its
 // operands feeds RB MFMAs.
 constexpr int kStRing = 4;   // slabs of codes in flight per lane
@@ -337,9 +338,10 @@ __global__ __launch_bounds__(512) void mrow_stream_kernel(const uint8_t* __restr
       const int r = wave + 8 * i;
       *reinterpret_cast<u32x4_t*>(&xs[b * XB + mr_at(r, kSlabCodes, lane)]) = v[i];
       if constexpr (AFF) {
-        // the row's sum over 64-code group lane / 8: eight pieces, eight lanes
-        float p = ((bf16_lo(v[i][0]) + bf16_hi(v[i][0])) + (bf16_lo(v[i][1]) + bf16_hi(v[i][1]))) +
-                  ((bf16_lo(v[i][2]) + bf16_hi(v[i][2])) + (bf16_lo(v[i][3]) + bf16_hi(v[i][3])));
+        // the row's sum over 64-code group lane / 8: eight pieces, eight
+        // lanes; a piece's pairs as bf16 dots against (1, 1)
+        constexpr uint32_t kOnes = 0x3F803F80u;
+        float p = dot2_bf16(v[i][3], kOnes, dot2_bf16(v[i][2], kOnes, dot2_bf16(v[i][1], kOnes, dot2_bf16(v[i][0], kOnes, 0.f))));
         p += dpp_f<0xB1>(p);    // quad_perm [1,0,3,2]
         p += dpp_f<0x4E>(p);    // quad_perm [2,3,0,1]
         p += dpp_f<0x141>(p);   // row_half_mirror
