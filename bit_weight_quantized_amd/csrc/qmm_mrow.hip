@@ -125,8 +125,9 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&xs[mr_at(r, rs, 8 * gr + c)]);
+          // each pair of the dword as a bf16 dot against (1, 1)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) sum[k] = (sum[k] + bf16_lo(v[k])) + bf16_hi(v[k]);
+          for (int k = 0; k < 4; ++k) sum[k] = dot2_bf16(v[k], 0x3F803F80u, sum[k]);
         }
       }
       xsum[q] = (sum[0] + sum[1]) + (sum[2] + sum[3]);
