@@ -94,7 +94,7 @@ size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
  *   2 <= t <= 64 rows on the multi-row kernel (see qmm_gemm: for t <= 16
  *     MXFP4 weights with n >= 5120 or t <= 8, affine weights with
  *     n >= 8192, while the t rows fit the kernel's LDS; for 17 <= t <= 64
- *     n >= 6144, or n >= 2048 with d <= 2048): 0.
+ *     d <= 2048, n >= 6912 with d <= 5120, or n >= 10240): 0.
  *   other 2 <= t <= 64 rows: one fp32 [t][n] plane per 512-code slab of d,
  *     ceil(d/512)·t·n·4 bytes (0.66 MB for t = 4, n = 4096, d = 5120).
  *   t > 64, affine weights: the activations converted to fp16 (t·d·2 bytes),
@@ -180,7 +180,7 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
  *     affine weights; at d = 5120 affine t <= 14, MXFP4 t <= 15): every
  *     weight read once for all rows, no workspace, one kernel.  Affine codes enter bf16 MFMAs as the exact
  *     values 128 + q and each group's scale and bias follow in fp32.
- *   17 <= t <= 64 with n >= 6144, or n >= 2048 and d <= 2048: the same
+ *   17 <= t <= 64 with d <= 2048, n >= 6912 and d <= 5120, or n >= 10240: the same
  *     kernel with the rows streamed through LDS one 512-code slab at a
  *     time (two buffers of 16·ceil(t/16) rows, at most 132 KiB): every
  *     weight read once for all rows, no workspace, one kernel.

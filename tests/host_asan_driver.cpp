@@ -140,12 +140,15 @@ int main() {
   EXPECT(strstr(qmm_last_error(), "64 MiB") != nullptr);
   EXPECT(qmm_gemm_noalloc(A, P(), 8, 13824, 5120, B(), B(), nullptr) == QMM_OK && g_called == "mrow");
   EXPECT(qmm_gemm_noalloc(A, P(), 8, 4096, 5120, B(), B(), nullptr) == QMM_OK && g_called == "skinny");
-  // 17 <= t <= 64: streamed multi-row rows from 6144 columns (or 2048 where
-  // d <= 2048), the few-row kernel below
+  // 17 <= t <= 64: streamed multi-row rows wherever d <= 2048, from 6912
+  // columns while d <= 5120 and from 10240 beyond; the few-row kernel below
   EXPECT(qmm_gemm_noalloc(A, P(), 40, 13824, 5120, B(), B(), nullptr) == QMM_OK && g_called == "mrow");
-  EXPECT(qmm_gemm_noalloc(M, P(), 40, 2048, 2048, B(), B(), nullptr) == QMM_OK && g_called == "mrow");
-  EXPECT(qmm_gemm_noalloc(M, P(), 40, 2047, 2048, B(), B(), nullptr) == QMM_OK && g_called == "skinny");
-  EXPECT(qmm_gemm_noalloc(A, P(), 40, 6143, 5120, B(), B(), nullptr) == QMM_OK && g_called == "skinny");
+  EXPECT(qmm_gemm_noalloc(M, P(), 40, 300, 2048, B(), B(), nullptr) == QMM_OK && g_called == "mrow");
+  EXPECT(qmm_gemm_noalloc(A, P(), 40, 6912, 5120, B(), B(), nullptr) == QMM_OK && g_called == "mrow");
+  EXPECT(qmm_gemm_noalloc(M, P(), 40, 10240, 8192, B(), B(), nullptr) == QMM_OK && g_called == "mrow");
+  EXPECT(qmm_gemm_noalloc(M, P(), 40, 2047, 2560, B(), B(), nullptr) == QMM_OK && g_called == "skinny");
+  EXPECT(qmm_gemm_noalloc(A, P(), 40, 6911, 5120, B(), B(), nullptr) == QMM_OK && g_called == "skinny");
+  EXPECT(qmm_gemm_noalloc(M, P(), 40, 8192, 8192, B(), B(), nullptr) == QMM_OK && g_called == "skinny");
   EXPECT(g_ws == g_scratch);
   g_fail = 1;   // the scratch lookup fails: a HIP status, with the HIP text
   EXPECT(qmm_gemm_noalloc(A, P(), 8, 4096, 5120, B(), B(), nullptr) == QMM_E_HIP);

@@ -61,24 +61,26 @@ def test_packed_bytes_rejects_bad_shapes():
 
 def test_workspace_contract():
     # the multi-row kernel (2 <= t <= 16, rows within its LDS; MXFP4 from 5120
-    # columns or up to 8 rows, affine from 8192 columns; 17 <= t <= 64 from
-    # 6144 columns, or from 2048 where d <= 2048) takes none
+    # columns or up to 8 rows, affine from 8192 columns; 17 <= t <= 64 where
+    # d <= 2048, from 6912 columns while d <= 5120, from 10240 beyond) takes none
     assert qmm.qmm_workspace_bytes(A, 2, 13824, 5120) == 0
     assert qmm.qmm_workspace_bytes(A, 14, 13824, 5120) == 0
     assert qmm.qmm_workspace_bytes(M, 8, 1024, 5120) == 0
     assert qmm.qmm_workspace_bytes(M, 15, 5120, 5120) == 0
     assert qmm.qmm_workspace_bytes(A, 17, 13824, 5120) == 0
-    assert qmm.qmm_workspace_bytes(M, 64, 6144, 8192) == 0
-    assert qmm.qmm_workspace_bytes(A, 40, 2048, 2048) == 0
+    assert qmm.qmm_workspace_bytes(M, 64, 10240, 8192) == 0
+    assert qmm.qmm_workspace_bytes(A, 40, 6912, 5120) == 0
+    assert qmm.qmm_workspace_bytes(A, 40, 300, 2048) == 0
     # split-K partials of qmm_gemm for the other 2 <= t <= 64: one fp32 [t][n]
     # plane per 512-code slab of d; nothing for other t or invalid shapes
     assert qmm.qmm_workspace_bytes(A, 2, 4096, 5120) == 10 * 2 * 4096 * 4
     assert qmm.qmm_workspace_bytes(A, 15, 13824, 5120) == 10 * 15 * 13824 * 4   # 15 rows exceed its LDS
     assert qmm.qmm_workspace_bytes(M, 12, 1024, 5120) == 10 * 12 * 1024 * 4
     assert qmm.qmm_workspace_bytes(A, 17, 4096, 5120) == 10 * 17 * 4096 * 4
-    assert qmm.qmm_workspace_bytes(M, 64, 6143, 2560) == 5 * 64 * 6143 * 4
-    assert qmm.qmm_workspace_bytes(A, 40, 2047, 2048) == 4 * 40 * 2047 * 4
-    assert qmm.qmm_workspace_bytes(M, 64, 300, 1088) == 3 * 64 * 300 * 4
+    assert qmm.qmm_workspace_bytes(M, 64, 6911, 2560) == 5 * 64 * 6911 * 4
+    assert qmm.qmm_workspace_bytes(A, 40, 6144, 4096) == 8 * 40 * 6144 * 4
+    assert qmm.qmm_workspace_bytes(M, 40, 8192, 8192) == 16 * 40 * 8192 * 4
+    assert qmm.qmm_workspace_bytes(M, 64, 300, 2560) == 5 * 64 * 300 * 4
     for t in (1, 2048, 300):
         assert qmm.qmm_workspace_bytes(M, t, 13824, 5120) == 0
     # affine weights through the tile kernel (t > 64): the activations as fp16,

@@ -879,7 +879,7 @@ def auto_picks_multi_row(fmt, t, n, d):
     if not kernel_takes(qmm.QMM_KERNEL_MULTI_ROW, fmt, t, d):
         return False
     if t > 16:
-        return n >= 6144 or (d <= 2048 and n >= 2048)
+        return d <= 2048 or (n >= 6912 and d <= 5120) or n >= 10240
     return n >= 5120 or t <= 8 if fmt == M else n >= 8192
 
 
