@@ -90,9 +90,10 @@ bool forces_tile(int k) { return k == QMM_KERNEL_TILE || k == QMM_KERNEL_TILE_UN
 // forced, or by default where it was measured faster than the few-row
 // split-K kernel.  Each of its workgroups stages every activation row, so
 // narrow matrices (few columns per workgroup) favour the split-K kernel.
-// Rows held in LDS (t <= 16): MXFP4 weights from 5120 columns, or for up to
-// 8 rows; affine weights, whose per-group scale and bias cost more per code,
-// from 8192.  Rows streamed (17 <= t <= 64): wherever d <= 2048 (the
+// Rows held in LDS (t <= 16): wherever d <= 3072 (a short reduction leaves
+// the split-K kernel little to share out beside its second launch), else
+// MXFP4 weights from 5120 columns, or for up to 8 rows, and affine weights,
+// whose per-group scale and bias cost more per code, from 8192.  Rows streamed (17 <= t <= 64): wherever d <= 2048 (the
 // split-K kernel then has few slabs to share out), else from 6912 columns
 // while d <= 5120 and from 10240 beyond (below those the split-K grid fits
 // about one round of workgroups and wins).
@@ -101,6 +102,7 @@ bool uses_mrow(int k, int f, int64_t t, int64_t n, int64_t d, const qmm::Layout&
   // (the grouped-matmul setting does not concern qmm_gemm: as under auto)
   if ((k != QMM_KERNEL_AUTO && k != QMM_KERNEL_GROUPED_MATMUL) || !qmm::mrow_fits(f, t, n, d, l)) return false;
   if (t > qmm::kMrowMaxT) return d <= 2048 || (n >= 6912 && d <= 5120) || n >= 10240;
+  if (d <= 3072) return true;
   return f == QMM_MXFP4_G32 ? (n >= 5120 || t <= 8) : n >= 8192;
 }
 

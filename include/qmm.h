@@ -92,8 +92,8 @@ size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
  * byte counts that fixed the NULL-scale crash of "Colibri Kimi K3 Metal
  * 后端实现全解析", Phase 10 (fmt_scale_bytes).
  *   2 <= t <= 64 rows on the multi-row kernel (see qmm_gemm: for t <= 16
- *     MXFP4 weights with n >= 5120 or t <= 8, affine weights with
- *     n >= 8192, while the t rows fit the kernel's LDS; for 17 <= t <= 64
+ *     d <= 3072, MXFP4 weights with n >= 5120 or t <= 8, or affine weights
+ *     with n >= 8192, while the t rows fit the kernel's LDS; for 17 <= t <= 64
  *     d <= 2048, n >= 6912 with d <= 5120, or n >= 10240): 0.
  *   other 2 <= t <= 64 rows: one fp32 [t][n] plane per 512-code slab of d,
  *     ceil(d/512)·t·n·4 bytes (0.66 MB for t = 4, n = 4096, d = 5120).
@@ -173,8 +173,8 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
  *   for affine weights where that is not 0 (see there), optional for MXFP4.
  * t = 1 runs the GEMV kernel.  Otherwise MFMA with fp32 accumulation, every
  * output rounded once to bf16:
- *   2 <= t <= 16, multi-row kernel (MXFP4 weights with n >= 5120 or t <= 8,
- *     affine weights with n >= 8192, while its LDS fits 160 KiB: the t rows
+ *   2 <= t <= 16, multi-row kernel (d <= 3072, MXFP4 weights with n >= 5120
+ *     or t <= 8, or affine weights with n >= 8192, while its LDS fits 160 KiB: the t rows
  *     padded to whole 512-code slabs, t·ceil(d/512) KiB (one row more for
  *     affine weights with t <= 8), plus 6 KiB, plus ceil(d/512)/2 KiB for
  *     affine weights; at d = 5120 affine t <= 14, MXFP4 t <= 15): every

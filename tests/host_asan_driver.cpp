@@ -130,8 +130,10 @@ int main() {
   EXPECT(qmm_gemm(A, P(), 2048, 13824, 5120, B(), B(), nullptr, 0, nullptr) == QMM_E_WORKSPACE);
   EXPECT(qmm_gemm(A, P(), 2048, 13824, 5120, B(), B(), P(), need2k, nullptr) == QMM_OK && g_called == "gemm_ws");
   EXPECT(g_ws == P() && g_ws_bytes == need2k);
-  EXPECT(qmm_gemm(A, P(), 3, 16, 64, B(), B(), P(), qmm_workspace_bytes(A, 3, 16, 64), nullptr) == QMM_OK &&
+  EXPECT(qmm_gemm(A, P(), 3, 16, 5120, B(), B(), P(), qmm_workspace_bytes(A, 3, 16, 5120), nullptr) == QMM_OK &&
          g_called == "skinny");
+  // short reductions (d <= 3072) take the multi-row kernel at any width
+  EXPECT(qmm_gemm(A, P(), 3, 16, 3072, B(), B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow");
 
   // the allocation-free GEMM: the static scratch replaces the workspace; too
   // large a shape is refused before the scratch is looked up

@@ -60,8 +60,8 @@ def test_packed_bytes_rejects_bad_shapes():
 
 
 def test_workspace_contract():
-    # the multi-row kernel (2 <= t <= 16, rows within its LDS; MXFP4 from 5120
-    # columns or up to 8 rows, affine from 8192 columns; 17 <= t <= 64 where
+    # the multi-row kernel (2 <= t <= 16, rows within its LDS; any n where
+    # d <= 3072, else MXFP4 from 5120 columns or up to 8 rows, affine from 8192; 17 <= t <= 64 where
     # d <= 2048, from 6912 columns while d <= 5120, from 10240 beyond) takes none
     assert qmm.qmm_workspace_bytes(A, 2, 13824, 5120) == 0
     assert qmm.qmm_workspace_bytes(A, 14, 13824, 5120) == 0
@@ -71,11 +71,14 @@ def test_workspace_contract():
     assert qmm.qmm_workspace_bytes(M, 64, 10240, 8192) == 0
     assert qmm.qmm_workspace_bytes(A, 40, 6912, 5120) == 0
     assert qmm.qmm_workspace_bytes(A, 40, 300, 2048) == 0
+    assert qmm.qmm_workspace_bytes(A, 4, 16, 64) == 0
+    assert qmm.qmm_workspace_bytes(A, 16, 300, 3072) == 0
     # split-K partials of qmm_gemm for the other 2 <= t <= 64: one fp32 [t][n]
     # plane per 512-code slab of d; nothing for other t or invalid shapes
     assert qmm.qmm_workspace_bytes(A, 2, 4096, 5120) == 10 * 2 * 4096 * 4
     assert qmm.qmm_workspace_bytes(A, 15, 13824, 5120) == 10 * 15 * 13824 * 4   # 15 rows exceed its LDS
     assert qmm.qmm_workspace_bytes(M, 12, 1024, 5120) == 10 * 12 * 1024 * 4
+    assert qmm.qmm_workspace_bytes(A, 16, 300, 3584) == 7 * 16 * 300 * 4
     assert qmm.qmm_workspace_bytes(A, 17, 4096, 5120) == 10 * 17 * 4096 * 4
     assert qmm.qmm_workspace_bytes(M, 64, 6911, 2560) == 5 * 64 * 6911 * 4
     assert qmm.qmm_workspace_bytes(A, 40, 6144, 4096) == 8 * 40 * 6144 * 4
@@ -99,11 +102,11 @@ def test_workspace_contract():
     # optional, but one that is passed must be large enough and 16-byte aligned
     # (host validation: nothing is launched)
     lib = qmm.load()
-    need = qmm.qmm_workspace_bytes(A, 4, 16, 64)
-    assert need == 256
-    assert lib.qmm_gemm(A, P, 4, 16, 64, P, P, P, need - 1, None) == E_WS
+    need = qmm.qmm_workspace_bytes(A, 4, 16, 5120)
+    assert need == 10 * 4 * 16 * 4
+    assert lib.qmm_gemm(A, P, 4, 16, 5120, P, P, P, need - 1, None) == E_WS
     assert "workspace" in qmm.qmm_last_error()
-    assert lib.qmm_gemm(A, P, 4, 16, 64, P, P, P + 8, need, None) == E_ALIGN
+    assert lib.qmm_gemm(A, P, 4, 16, 5120, P, P, P + 8, need, None) == E_ALIGN
     assert lib.qmm_gemv(A, P, 16, 64, P + 1, P, P, 1, None) == E_ALIGN   # gemv ignores ws, checks x
     # affine weights with t >= 2 cannot do without it
     assert lib.qmm_gemm(A, P, 2048, 16, 64, P, P, None, 0, None) == E_WS
@@ -196,7 +199,7 @@ if {want} < 0:
     assert "QMM_FORCE_KERNEL" in qmm.qmm_last_error()
     qmm.qmm_set_kernel(qmm.QMM_KERNEL_AUTO)
     assert qmm.qmm_get_kernel() == 0
-    assert qmm.qmm_workspace_bytes(1, 4, 16, 64) == 256
+    assert qmm.qmm_workspace_bytes(1, 4, 16, 5120) == 2560
 """
     env = dict(os.environ, QMM_FORCE_KERNEL=value)
     r = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True, text=True, timeout=120)

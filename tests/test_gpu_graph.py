@@ -52,7 +52,7 @@ def test_graph_replay_matches_eager():
 
     # weights: affine decode matrix and prefill matrix, MXFP4 expert stacks
     nd, dd = 1000, 1024
-    tg, ng, dg = 70, 300, 1024
+    tg, ng, dg = 70, 300, 3584
     ne, k, t, dm, ni = 12, 4, 40, 256, 96
     wd = synth.affine_weights(901, nd, dd)
     wg = synth.affine_weights(902, ng, dg)

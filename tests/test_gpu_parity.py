@@ -880,6 +880,8 @@ def auto_picks_multi_row(fmt, t, n, d):
         return False
     if t > 16:
         return d <= 2048 or (n >= 6912 and d <= 5120) or n >= 10240
+    if d <= 3072:
+        return True
     return n >= 5120 or t <= 8 if fmt == M else n >= 8192
 
 

@@ -76,7 +76,7 @@ def both(fmt, p, t, n, d, x):
 # matrices of under 6144 columns, and narrow affine matrices below that), the tile kernel split along K (t > 64
 # with few tiles, d a multiple of 512), and the affine tile kernel unsplit
 # (its fp16 activations in the scratch)
-CASES = [(A, 4096, 5120, 40, 20), (M, 1000, 3584, 64, 17), (A, 4096, 2048, 12, 3),
+CASES = [(A, 4096, 5120, 40, 20), (M, 1000, 3584, 64, 17), (A, 4096, 3584, 12, 3),
          (A, 1000, 2048, 200, 70), (M, 700, 3072, 97, 66), (A, 4352, 1024, 2048, 300)]
 
 
