@@ -1002,11 +1002,16 @@ int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream) 
     const int tiles_m = (a.t + wm - 1) / wm;
     const int tiles = tiles_m * tiles_n;
     // split along K while the tiles cannot fill the chip (few rows): as many
-    // splits as fit the CUs, at most kTileSplits, each at least 8 steps
+    // splits as fit the CUs, each at least 8 steps, and no more than the
+    // planes the workspace layout reserves for the shape (whatever the size of
+    // the buffer passed, so the split, and with it every output bit, depends
+    // on the shape only); none if the buffer holds fewer
     int splits = 1;
     if (fast && planes && a.t > kSkinnyMaxT) {
-      splits = int(std::min<int64_t>({int64_t(kTileSplits), cus / tiles, int64_t(nk / 8)}));
-      if (splits < 2 || size_t(splits) * size_t(a.t) * size_t(a.n) * 4 > planes_bytes) splits = 1;
+      const size_t plane = size_t(a.t) * size_t(a.n) * 4;
+      const int64_t reserved = (tw.total - tw.planes) / int64_t(plane);
+      splits = int(std::min<int64_t>({reserved, cus / tiles, int64_t(nk / 8)}));
+      if (splits < 2 || size_t(splits) * plane > planes_bytes) splits = 1;
     }
     if (splits == 1) {
       if (pe.start || pe.stop)

@@ -101,7 +101,7 @@ size_t qmm_packed_bytes(qmm_format f, int64_t n, int64_t d);
  *     one int32 exponent per row and per weight column, each rounded up to
  *     256 bytes (21.0 MB for t = 2048, n = 13824, d = 5120), plus, while the
  *     tile kernel has few tiles (128-row tiles over at most 128 workgroups)
- *     and d is a multiple of 512, up to four K-split planes of t·n·4 bytes.
+ *     and d is a multiple of 512, up to eight K-split planes of t·n·4 bytes.
  *   t > 64, MXFP4 weights: those K-split planes, else 0.
  * Affine weights REQUIRE this workspace where it is not 0 (QMM_E_WORKSPACE
  * without one).  For MXFP4 it is optional: ws = NULL runs the tile kernel,
@@ -195,7 +195,7 @@ qmm_status qmm_gemv_int8(qmm_format f, const void* packed, int64_t n, int64_t d,
  *     (relative error <= 2^-11 wherever the scaled weight is a normal fp16:
  *     every weight within 2^-27 of its column's largest), runs fp16 MFMAs
  *     and removes both powers of two exactly.  With few tiles the tile kernel
- *     is split along d into up to four fp32 planes summed in order.
+ *     is split along d into up to eight fp32 planes summed in order.
  *   MXFP4: the weights are bf16 MFMA operands, exact for E8M0 in [2, 252]
  *     (at 253 and 254 the largest codes reach 2^128: not representable).
  * Profiling events armed by qmm_profile_next bracket every kernel of the

@@ -92,9 +92,12 @@ def test_workspace_contract():
     up = lambda v: -(-v // 256) * 256
     assert qmm.qmm_workspace_bytes(A, 2048, 13824, 5120) == 2048 * 5120 * 2 + 2048 * 4 + 13824 * 4
     assert qmm.qmm_workspace_bytes(A, 300, 13824, 5120) == 300 * 5120 * 2 + up(300 * 4) + 13824 * 4
-    # the tile kernel split along K (up to 4 planes) while 128-row tiles would
+    # the tile kernel split along K (up to 8 planes) while 128-row tiles would
     # cover at most half of a 256-CU chip; d a multiple of 512 only
-    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5120) == up(65 * 5120 * 2) + up(65 * 4) + 13824 * 4 + 4 * 65 * 13824 * 4
+    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5120) == up(65 * 5120 * 2) + up(65 * 4) + 13824 * 4 + 8 * 65 * 13824 * 4
+    assert qmm.qmm_workspace_bytes(M, 128, 8192, 5120) == 8 * 128 * 8192 * 4
+    # four planes where eight (and the other regions) would pass the 64 MiB of
+    # the allocation-free scratch
     assert qmm.qmm_workspace_bytes(M, 256, 13824, 5120) == 4 * 256 * 13824 * 4
     assert qmm.qmm_workspace_bytes(M, 65, 13824, 5056) == 0
     assert qmm.qmm_workspace_bytes(A, 65, 13824, 5056) == up(65 * 5056 * 2) + up(65 * 4) + 13824 * 4
@@ -144,7 +147,7 @@ def test_kernel_override_sizes_and_refusals(kernel_auto_after):
     assert qmm.qmm_get_kernel() == qmm.QMM_KERNEL_TILE
     assert qmm.qmm_workspace_bytes(A, 4, 13824, 5120) == tile_aff(4)       # no split for t <= 64
     assert qmm.qmm_workspace_bytes(A, 1, 13824, 5120) == tile_aff(1)       # t = 1 on the tile kernel too
-    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5120) == tile_aff(65) + 4 * 65 * 13824 * 4
+    assert qmm.qmm_workspace_bytes(A, 65, 13824, 5120) == tile_aff(65) + 8 * 65 * 13824 * 4
     assert qmm.qmm_workspace_bytes(M, 4, 13824, 5120) == 0
     assert lib.qmm_gemm(A, P, 1, 16, 64, P, P, None, 0, None) == E_WS     # affine tile needs one at t = 1
     qmm.qmm_set_kernel(qmm.QMM_KERNEL_TILE_UNSPLIT)
