@@ -664,6 +664,42 @@ def test_gemm_split_k_mxfp4(t, n, d, elo, ecount):
     assert_parity(y, yr, ar, f"gemm split-k mxfp4 {t}x{n}x{d}")
 
 
+@pytest.mark.parametrize("fmt,t,n,d", [(A, 65, 4096, 5120), (M, 192, 12288, 5120)])
+def test_tile_split_depends_on_shape_only(fmt, t, n, d):
+    """The tile GEMM splits along K into the planes the workspace layout
+    reserves for the shape (eight; four where eight and the other regions
+    would pass the 64 MiB of the allocation-free scratch), whatever the size
+    of the buffer passed: the workspace asked for, a larger one and the
+    allocation-free call give the same bits, and they meet the oracle."""
+    say("tile split by shape", fmt, t, n, d)
+    x = synth.activations(7300 + t, synth.S_X, t, d)
+    if fmt == A:
+        w = synth.affine_weights(7400 + n, n, d)
+        p = pack_affine(w)
+        yr, ar = oracle.gemm_affine(x, w.codes, w.scale, w.bias)
+    else:
+        w = rand_mxfp4(7400 + n, n, d)
+        p = pack_mxfp4(w)
+        yr, ar = oracle.gemm_mxfp4(x, w.codes, w.e8m0)
+    need = qmm.qmm_workspace_bytes(fmt, t, n, d)
+    base = (-(-t * d * 2 // 256) * 256 + -(-t * 4 // 256) * 256 + -(-n * 4 // 256) * 256) if fmt == A else 0
+    planes = (need - base) // (t * n * 4)
+    assert planes == (8 if base + 8 * t * n * 4 <= 64 << 20 else 4), planes
+    outs = []
+    for extra in (0, 32 << 20):
+        ws = guarded(((need + extra) // 4,), float("nan"), torch.float32)
+        y = nan_out(t, n)
+        qmm.qmm_gemm(fmt, p, t, n, d, dev(x), y, ws)
+        torch.cuda.synchronize()
+        outs.append(host_u16(y))
+    y = nan_out(t, n)
+    qmm.qmm_gemm_noalloc(fmt, p, t, n, d, dev(x), y)
+    torch.cuda.synchronize()
+    outs.append(host_u16(y))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    assert_parity(outs[0], yr, ar, f"tile split by shape fmt={fmt} {t}x{n}x{d}")
+
+
 def run_gemm_ws(fmt, packed, n, d, x_bits):
     """qmm_gemm given the workspace qmm_workspace_bytes asks for (NaN-filled)."""
     t = x_bits.shape[0]
