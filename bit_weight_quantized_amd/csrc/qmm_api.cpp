@@ -414,6 +414,27 @@ qmm_status grouped(const char* name, bool swiglu, qmm_format f, const void* pack
     a.m_total = m_total;
     a.y = y;
     err = qmm::launch_gemv(a, stream);
+  } else if (!swiglu && kf != QMM_KERNEL_GROUPED_MATMUL &&
+             qmm::mrow_grouped_fits(f, max_seg_rows, n, d, t_x, l)) {
+    // a few rows per segment: the multi-row kernel reads each expert's
+    // weights once for all of them
+    qmm::MrowGroupedArgs a{};
+    a.f = f;
+    a.stack = static_cast<const uint8_t*>(packed_stack);
+    a.grp.expert_stride = expert_stride_bytes;
+    a.grp.row_index = row_index;
+    a.grp.seg_expert = seg_expert;
+    a.grp.seg_offsets = seg_offsets;
+    a.grp.n_experts = n_experts;
+    a.grp.m_total = m_total;
+    a.grp.t_x = int(t_x);
+    a.n_seg = n_seg;
+    a.t = max_seg_rows;
+    a.n = int(n);
+    a.d = int(d);
+    a.x = x;
+    a.y = y;
+    err = qmm::launch_mrow_grouped(a, stream);
   } else {
     qmm::GemmArgs a{};
     a.f = f;

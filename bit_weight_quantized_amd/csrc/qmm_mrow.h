@@ -82,4 +82,39 @@ inline bool mrow_fits(int f, int64_t t, int64_t n, int64_t d, const Layout& l) {
 // Y = X·Ŵᵀ for a shape mrow_fits accepts; no workspace.
 int launch_mrow(const GemmArgs& a, void* stream);
 
+// Routed experts through the in-LDS kernel: segment s's rows (gathered from
+// x through row_index, or in order when it is NULL) against expert
+// seg_expert[s], at most `t` rows per pass of the segment (the LDS is sized
+// for t; a longer segment takes several passes).  Kernel-side view:
+struct MrowGroups {
+  int64_t expert_stride;        // bytes between expert blobs
+  const int32_t* row_index;     // NULL: grouped row r reads x row r
+  const int32_t* seg_expert;
+  const int32_t* seg_offsets;
+  int n_experts, m_total, t_x;
+};
+struct MrowGroupedArgs {
+  int f;
+  const uint8_t* stack;         // expert 0's blob
+  MrowGroups grp;
+  int n_seg, t, n, d;
+  const uint16_t* x;
+  uint16_t* y;
+};
+// the grouped launch's LDS: the dense one plus the chunk's x-row table
+inline size_t mrow_grouped_lds_bytes(int f, int64_t t, int64_t d) {
+  return mrow_lds_bytes(f, t, d) + size_t(kMrowMaxT) * 4;
+}
+// 2 <= t <= kMrowGroupedMaxT rows per pass within the LDS, and 32-bit
+// offsets over one expert's codes and metadata and over x.  Up to 8 rows
+// per segment the grouped form measured faster than the grouped matmul
+// kernel on the decode experts (5-37%), at 12-16 rows not always.
+constexpr int kMrowGroupedMaxT = 8;
+inline bool mrow_grouped_fits(int f, int64_t t, int64_t n, int64_t d, int64_t t_x, const Layout& l) {
+  return t >= 2 && t <= kMrowGroupedMaxT && mrow_grouped_lds_bytes(f, t, d) <= kMrowMaxLds &&
+         n * (d / 2) < (int64_t(1) << 31) && l.meta_bytes < (int64_t(1) << 31) &&
+         t_x * d * 2 < (int64_t(1) << 31);
+}
+int launch_mrow_grouped(const MrowGroupedArgs& a, void* stream);
+
 }  // namespace qmm

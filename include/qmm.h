@@ -230,12 +230,16 @@ qmm_status qmm_gemm_noalloc(qmm_format f, const void* packed, int64_t t, int64_t
  *   row_index           int32[m_total]: grouped row r reads x row row_index[r];
  *                       or NULL: row r reads x row r (x already in grouped
  *                       order, e.g. the activated rows of the expert FFN;
- *                       this always takes the matmul kernel)
+ *                       never the decode GEMV path)
  *   seg_expert          int32[n_seg]: expert of segment s
  *   seg_offsets         int32[n_seg + 1]: segment s owns grouped rows
  *                       [seg_offsets[s], seg_offsets[s+1])
  *   max_seg_rows        host upper bound on segment sizes; it selects the
- *                       kernel (1 = decode GEMV path), never memory bounds
+ *                       kernel, never memory bounds: 1 = the decode GEMV
+ *                       path; 2..8 = the multi-row kernel (each expert's
+ *                       weights read once per pass of up to max_seg_rows
+ *                       rows; a longer segment takes several passes);
+ *                       more = the matmul kernel
  *   y                   bf16[m_total][n]: row r = x[row_index[r]]·Ŵ_eᵀ
  * row_index, seg_expert, seg_offsets are device arrays; n_seg, m_total,
  * max_seg_rows, t_x, n_experts are host scalars.  The kernels clamp segment

@@ -12,6 +12,7 @@
 
 #include "../bit_weight_quantized_amd/csrc/qmm_deferred.h"
 #include "../bit_weight_quantized_amd/csrc/qmm_internal.h"
+#include "../bit_weight_quantized_amd/csrc/qmm_mrow.h"
 #include "../bit_weight_quantized_amd/csrc/qmm_skinny.h"
 
 // ---- stubs -----------------------------------------------------------------
@@ -49,6 +50,7 @@ int read_header(const void*, PackedHeader* h, void*) {
 int launch_route(const RouteArgs&, void*) { return reach("route"); }
 int launch_skinny(const GemmArgs&, float* ws, void*) { g_ws = ws; return reach("skinny"); }
 int launch_mrow(const GemmArgs&, void*) { return reach("mrow"); }
+int launch_mrow_grouped(const MrowGroupedArgs&, void*) { return reach("mrow_grouped"); }
 int launch_combine(const CombineArgs&, void*) { return reach("combine"); }
 int launch_gemm_ws(const GemmArgs&, float* ws, size_t bytes, void*) {
   g_ws = ws;
@@ -195,7 +197,13 @@ int main() {
   g_called = "none";
   EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 0, 0, 1, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "none");
   EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 1, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "gemv");
+  // 2..8 rows per segment: the multi-row kernel; more, or forced, the matmul kernel
+  EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 4, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow_grouped");
+  EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, nullptr, I(), I(), 1, 4, 8, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow_grouped");
+  EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 9, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "grouped_gemm");
+  EXPECT(qmm_set_kernel(QMM_KERNEL_GROUPED_MATMUL) == QMM_OK);
   EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 4, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "grouped_gemm");
+  EXPECT(qmm_set_kernel(QMM_KERNEL_AUTO) == QMM_OK);
   EXPECT(qmm_grouped_gemm_swiglu(A, P(), blob, 2, 15, 64, B(), 4, I(), I(), I(), 1, 4, 4, B(), nullptr, 0, nullptr) == QMM_E_SHAPE);
   EXPECT(qmm_grouped_gemm_swiglu(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 1, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "grouped_gemm");
 

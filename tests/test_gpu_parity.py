@@ -1173,6 +1173,82 @@ def test_grouped_forced_matmul_on_one_row_segments(fmt, kernel_auto_after):
         assert np.array_equal(y, want), f"kernel setting {k}"
 
 
+def run_grouped_order(fmt, stk, stride, n_exp, n, d, x_bits, seg_expert, seg_offsets, max_rows):
+    """The grouped call with row_index NULL: grouped row r reads x row r."""
+    m_total = int(seg_offsets[-1])
+    y = nan_out(m_total, n)
+    qmm.qmm_grouped_gemm(fmt, stk, stride, n_exp, n, d, dev(x_bits), x_bits.shape[0], None,
+                         dev(np.asarray(seg_expert, np.int32)), dev(np.asarray(seg_offsets, np.int32)),
+                         len(seg_expert), m_total, max_rows, y)
+    torch.cuda.synchronize()
+    return host_u16(y)
+
+
+# a bound of 2 .. 8 rows per segment takes the multi-row kernel (one
+# workgroup per 128-column block and segment, each segment's rows gathered
+# into LDS, a longer segment in several passes); shapes:
+# one narrow slab and a narrow last slab, n not a multiple of 64, affine with
+# 8 rows or fewer (two groups per MFMA) and with more, the decode experts
+GROUPED_MR_SHAPES = [(A, 300, 1024), (A, 257, 576), (M, 300, 2080), (M, 6144, 3584), (A, 129, 64), (M, 97, 32)]
+
+
+@pytest.mark.parametrize("fmt,n,d", GROUPED_MR_SHAPES)
+def test_grouped_multi_row(fmt, n, d, kernel_auto_after):
+    """Segments of 0 .. 16 rows through the multi-row kernel (bounds of 2 to
+    8 rows per pass) against the oracle: a segment longer than the bound
+    takes several passes of that many rows; also with the rows in order
+    (row_index NULL), and the matmul kernel forced on the same table."""
+    say("grouped multi-row", fmt, n, d)
+    n_exp, t = 6, 48
+    ws = [synth.affine_weights(960 + e, n, d) if fmt == A else rand_mxfp4(960 + e, n, d) for e in range(n_exp)]
+    stk, size = stack(fmt, ws)
+    x = synth.activations(961, synth.S_X, t, d)
+    sizes = [0, 1, 3, 16, 5, 0, 2, 9]
+    seg_expert = [4, 0, 2, 5, 3, 1, 2, 0]
+    seg_offsets = np.concatenate([[0], np.cumsum(sizes)])
+    rng = np.random.default_rng(12)
+    row_index = np.concatenate([np.sort(rng.choice(t, sz, replace=False)) for sz in sizes]).astype(np.int32)
+    deq = (lambda e: oracle.dequant_affine(ws[e].codes, ws[e].scale, ws[e].bias)) if fmt == A else \
+          (lambda e: oracle.dequant_mxfp4(ws[e].codes, ws[e].e8m0))
+    yr, ar = oracle.grouped(x, row_index, seg_expert, seg_offsets, deq)
+    for max_rows in (8, 4, 2):
+        y = run_grouped(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, max_rows)
+        assert_parity(y, yr, ar, f"grouped multi-row fmt={fmt} {n}x{d} max_rows={max_rows}")
+    m_total = int(seg_offsets[-1])
+    yo = run_grouped_order(fmt, stk, size, n_exp, n, d, x[:m_total], seg_expert, seg_offsets, 8)
+    yro, aro = oracle.grouped(x[:m_total], np.arange(m_total), seg_expert, seg_offsets, deq)
+    assert_parity(yo, yro, aro, f"grouped multi-row rows in order fmt={fmt} {n}x{d}")
+    qmm.qmm_set_kernel(qmm.QMM_KERNEL_GROUPED_MATMUL)
+    y = run_grouped(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, 16)
+    assert_parity(y, yr, ar, f"grouped matmul forced fmt={fmt} {n}x{d}")
+
+
+@pytest.mark.parametrize("fmt", [A, M])
+def test_grouped_multi_row_integer_exact(fmt, kernel_auto_after):
+    """Integer weights and activations: the multi-row kernel (true and
+    understated bound) and the matmul kernel return the oracle's exact sums
+    rounded to bf16, bit for bit."""
+    say("grouped multi-row integer exact", fmt)
+    n, d, n_exp, t = 200, 1536, 4, 30
+    ws = [integer_affine(970 + e, n, d) if fmt == A else rand_mxfp4(970 + e, n, d, 127, 1) for e in range(n_exp)]
+    stk, size = stack(fmt, ws)
+    rng = np.random.default_rng(33)
+    x = synth.bf16_bits(rng.integers(-3, 4, size=(t, d)).astype(float))
+    sizes = [7, 0, 12, 3]
+    seg_expert = [3, 1, 0, 2]
+    seg_offsets = np.concatenate([[0], np.cumsum(sizes)])
+    row_index = rng.integers(0, t, int(seg_offsets[-1])).astype(np.int32)
+    deq = (lambda e: oracle.dequant_affine(ws[e].codes, ws[e].scale, ws[e].bias)) if fmt == A else \
+          (lambda e: oracle.dequant_mxfp4(ws[e].codes, ws[e].e8m0))
+    yr, _ = oracle.grouped(x, row_index, seg_expert, seg_offsets, deq)
+    assert np.all(np.abs(yr) < 2 ** 24)
+    want = oracle.f64_to_bf16_bits(yr)
+    for k, max_rows in ((qmm.QMM_KERNEL_AUTO, 8), (qmm.QMM_KERNEL_AUTO, 5), (qmm.QMM_KERNEL_GROUPED_MATMUL, 12)):
+        qmm.qmm_set_kernel(k)
+        y = run_grouped(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, max_rows)
+        assert np.array_equal(y, want), f"kernel setting {k}, max_rows {max_rows}"
+
+
 # ---------------------------------------------------------------------------
 # expert FFN: gate_up with the SwiGLU activation, down on the activated rows,
 # weighted combine back to the tokens
