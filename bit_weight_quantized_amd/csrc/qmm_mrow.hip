@@ -22,6 +22,11 @@
 // kept apart by regrouping the loaded words across lanes (v_permlane32_swap)
 // so that every MFMA sees one group.  MXFP4 weights convert exactly to bf16
 // with their E8M0 scale.  No weight is rounded.
+//
+// Grouped form (routed experts, a few rows per segment): the same kernel with
+// blockIdx.y a segment of the routing tables, its expert's weights, and its
+// rows gathered through row_index; a segment longer than the launch's T rows
+// takes several passes, each re-reading the expert.
 #include <hip/hip_runtime.h>
 
 #include "qmm_device.h"
