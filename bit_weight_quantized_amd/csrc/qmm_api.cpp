@@ -436,6 +436,40 @@ qmm_status grouped(const char* name, bool swiglu, qmm_format f, const void* pack
     a.y = y;
     err = qmm::launch_mrow_grouped(a, stream);
   } else {
+    // longer segments: the matmul kernel; without the activation, the short
+    // ones among them (up to the multi-row kernel's bound, found on the
+    // device) go to the multi-row kernel first
+    const bool split = !swiglu && kf != QMM_KERNEL_GROUPED_MATMUL &&
+                       qmm::mrow_grouped_fits(f, qmm::kMrowGroupedMaxT, n, d, t_x, l);
+    if (split) {
+      // armed profiling events: the start with the first launch, the stop
+      // with the second
+      const qmm::ProfileEvents pe = qmm::take_profile_events();
+      g_profile = {pe.start, nullptr};
+      qmm::MrowGroupedArgs a{};
+      a.f = f;
+      a.stack = static_cast<const uint8_t*>(packed_stack);
+      a.grp.expert_stride = expert_stride_bytes;
+      a.grp.row_index = row_index;
+      a.grp.seg_expert = seg_expert;
+      a.grp.seg_offsets = seg_offsets;
+      a.grp.n_experts = n_experts;
+      a.grp.m_total = m_total;
+      a.grp.t_x = int(t_x);
+      a.grp.max_rows = qmm::kMrowGroupedMaxT;
+      a.n_seg = n_seg;
+      a.t = qmm::kMrowGroupedMaxT;
+      a.n = int(n);
+      a.d = int(d);
+      a.x = x;
+      a.y = y;
+      err = qmm::launch_mrow_grouped(a, stream);
+      g_profile = {nullptr, pe.stop};
+      if (err) {
+        g_profile = {nullptr, nullptr};
+        return hip_fail(err, name);
+      }
+    }
     qmm::GemmArgs a{};
     a.f = f;
     a.packed = static_cast<const uint8_t*>(packed_stack);
@@ -453,7 +487,7 @@ qmm_status grouped(const char* name, bool swiglu, qmm_format f, const void* pack
     a.max_seg_rows = max_seg_rows;
     a.y = y;
     a.swiglu = swiglu;
-    err = qmm::launch_grouped_gemm(a, stream);
+    err = qmm::launch_grouped_gemm_long(a, split ? qmm::kMrowGroupedMaxT : 0, stream);
   }
   if (err) return hip_fail(err, name);
   return QMM_OK;

@@ -40,6 +40,7 @@
 #include "qmm_internal.h"
 #include "qmm_launch.h"
 #include "qmm_lds_copy.h"
+#include "qmm_mrow.h"
 #include "qmm_skinny.h"
 
 namespace qmm {
@@ -650,7 +651,7 @@ __global__ __launch_bounds__(256, FMT == QMM_AFFINE4_G64 ? 1 : 2) void grouped_g
     const uint8_t* __restrict__ base, int64_t expert_stride, int n_experts, int64_t codes_off,
     int64_t meta_off, int n, int d, const uint16_t* __restrict__ x, int64_t t_x,
     const int32_t* __restrict__ row_index, const int32_t* __restrict__ seg_expert,
-    const int32_t* __restrict__ seg_offsets, int m_total, uint16_t* __restrict__ y) {
+    const int32_t* __restrict__ seg_offsets, int m_total, uint16_t* __restrict__ y, int skip_rows) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][kGBM * kGXs];
   __shared__ int32_t src_row[kGBM];
   // affine: each staged row's activation sum per 64-code group of the K step,
@@ -673,7 +674,7 @@ __global__ __launch_bounds__(256, FMT == QMM_AFFINE4_G64 ? 1 : 2) void grouped_g
 
   const int r_begin = min(max(seg_offsets[s], 0), m_total);
   const int r_end = min(max(seg_offsets[s + 1], r_begin), m_total);
-  if (r_begin >= r_end) return;
+  if (r_end - r_begin <= max(skip_rows, 0)) return;   // no rows, or left to the multi-row kernel
   const int e = seg_expert[s];
   const bool bad_expert = e < 0 || e >= n_experts;
   const uint8_t* blob = base + (bad_expert ? 0 : int64_t(e) * expert_stride);
@@ -1070,7 +1071,9 @@ int launch_gemm_ws(const GemmArgs& a, float* ws, size_t ws_bytes, void* stream) 
   return int(hipGetLastError());
 }
 
-int launch_grouped_gemm(const GemmArgs& a, void* stream) {
+int launch_grouped_gemm(const GemmArgs& a, void* stream) { return launch_grouped_gemm_long(a, 0, stream); }
+
+int launch_grouped_gemm_long(const GemmArgs& a, int skip_rows, void* stream) {
   Layout l;
   if (!layout_of(a.f, a.n, a.d, &l)) return int(hipErrorInvalidValue);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1080,7 +1083,7 @@ int launch_grouped_gemm(const GemmArgs& a, void* stream) {
   auto go = [&](auto kernel) {
     launch_kernel(kernel, grid, dim3(256), s, a.packed, a.expert_stride, a.n_experts, l.codes_offset,
                   l.meta_offset, a.n, a.d, a.x, a.t_x, a.row_index, a.seg_expert, a.seg_offsets,
-                  a.m_total, a.y);
+                  a.m_total, a.y, skip_rows);
   };
   if (a.f == QMM_AFFINE4_G64)
     a.swiglu ? go(grouped_gemm_kernel<QMM_AFFINE4_G64, true>) : go(grouped_gemm_kernel<QMM_AFFINE4_G64, false>);

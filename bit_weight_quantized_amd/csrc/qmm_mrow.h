@@ -92,6 +92,7 @@ struct MrowGroups {
   const int32_t* seg_expert;
   const int32_t* seg_offsets;
   int n_experts, m_total, t_x;
+  int max_rows;                 // > 0: segments of more rows are left to another launch
 };
 struct MrowGroupedArgs {
   int f;
@@ -116,5 +117,13 @@ inline bool mrow_grouped_fits(int f, int64_t t, int64_t n, int64_t d, int64_t t_
          t_x * d * 2 < (int64_t(1) << 31);
 }
 int launch_mrow_grouped(const MrowGroupedArgs& a, void* stream);
+
+// A routed call whose segments are mostly long but many short (prefill
+// routing: 1 to ~60 rows per expert) splits on the device: segments of at
+// most kMrowGroupedMaxT rows take the grouped multi-row kernel (max_rows),
+// the others the grouped matmul kernel (skip_rows), each workgroup reading
+// its segment's row count from the same tables; the two launches write
+// disjoint rows of y.
+int launch_grouped_gemm_long(const GemmArgs& a, int skip_rows, void* stream);
 
 }  // namespace qmm

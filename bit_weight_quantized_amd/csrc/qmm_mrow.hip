@@ -78,14 +78,15 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
   const bool active = 16 * cw < c1 - c0;
   // grouped (routed experts): the workgroup's segment blockIdx.y, its rows
   // [r_begin, r_end) taken t at a time, its expert's weights; a segment with
-  // no rows returns before any barrier, the whole workgroup alike
+  // no rows, or more than grp.max_rows when that is set, returns before any
+  // barrier, the whole workgroup alike
   int r_begin = 0, r_end = t;
   bool bad_expert = false;
   if constexpr (GRP) {
     const int sg = blockIdx.y;
     r_begin = min(max(grp.seg_offsets[sg], 0), grp.m_total);
     r_end = min(max(grp.seg_offsets[sg + 1], r_begin), grp.m_total);
-    if (r_begin >= r_end) return;
+    if (r_begin >= r_end || (grp.max_rows > 0 && r_end - r_begin > grp.max_rows)) return;
     const int e = grp.seg_expert[sg];
     bad_expert = e < 0 || e >= grp.n_experts;
     const int64_t eo = bad_expert ? 0 : int64_t(e) * grp.expert_stride;

@@ -239,7 +239,12 @@ qmm_status qmm_gemm_noalloc(qmm_format f, const void* packed, int64_t t, int64_t
  *                       path; 2..8 = the multi-row kernel (each expert's
  *                       weights read once per pass of up to max_seg_rows
  *                       rows; a longer segment takes several passes);
- *                       more = the matmul kernel
+ *                       more = two launches that split the segments on
+ *                       the device: those of at most 8 rows to the
+ *                       multi-row kernel, the longer ones to the matmul
+ *                       kernel (which takes all of them when forced with
+ *                       QMM_KERNEL_GROUPED_MATMUL, or where the multi-row
+ *                       kernel's LDS or offsets do not fit the shape)
  *   y                   bf16[m_total][n]: row r = x[row_index[r]]·Ŵ_eᵀ
  * row_index, seg_expert, seg_offsets are device arrays; n_seg, m_total,
  * max_seg_rows, t_x, n_experts are host scalars.  The kernels clamp segment

@@ -64,6 +64,12 @@ int noalloc_scratch(void*, void** out) {
 }
 int launch_stream_read(const void*, size_t, uint32_t*, void*) { return reach("stream_read"); }
 int launch_grouped_gemm(const GemmArgs&, void*) { return reach("grouped_gemm"); }
+// the matmul kernel over the segments longer than skip_rows: after the
+// multi-row kernel took the short ones (a split call), or alone
+int launch_grouped_gemm_long(const GemmArgs&, int skip_rows, void*) {
+  if (skip_rows == 0) return reach("grouped_gemm");
+  return reach(skip_rows == kMrowGroupedMaxT && g_called == "mrow_grouped" ? "split" : "bad_split");
+}
 }  // namespace qmm
 
 // ---- checks ----------------------------------------------------------------
@@ -200,8 +206,12 @@ int main() {
   // 2..8 rows per segment: the multi-row kernel; more, or forced, the matmul kernel
   EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 4, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow_grouped");
   EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, nullptr, I(), I(), 1, 4, 8, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow_grouped");
-  EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 9, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "grouped_gemm");
+  // more than 8: segments of up to 8 rows to the multi-row kernel, the rest
+  // to the matmul kernel (found on the device)
+  g_called = "none";
+  EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 9, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "split");
   EXPECT(qmm_set_kernel(QMM_KERNEL_GROUPED_MATMUL) == QMM_OK);
+  EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 9, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "grouped_gemm");
   EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 4, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "grouped_gemm");
   EXPECT(qmm_set_kernel(QMM_KERNEL_AUTO) == QMM_OK);
   EXPECT(qmm_grouped_gemm_swiglu(A, P(), blob, 2, 15, 64, B(), 4, I(), I(), I(), 1, 4, 4, B(), nullptr, 0, nullptr) == QMM_E_SHAPE);

@@ -1211,13 +1211,16 @@ def test_grouped_multi_row(fmt, n, d, kernel_auto_after):
     deq = (lambda e: oracle.dequant_affine(ws[e].codes, ws[e].scale, ws[e].bias)) if fmt == A else \
           (lambda e: oracle.dequant_mxfp4(ws[e].codes, ws[e].e8m0))
     yr, ar = oracle.grouped(x, row_index, seg_expert, seg_offsets, deq)
-    for max_rows in (8, 4, 2):
+    # a bound above 8 splits the call: segments of up to 8 rows to the
+    # multi-row kernel, 9 and 16 to the matmul kernel
+    for max_rows in (8, 4, 2, 16):
         y = run_grouped(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, max_rows)
         assert_parity(y, yr, ar, f"grouped multi-row fmt={fmt} {n}x{d} max_rows={max_rows}")
     m_total = int(seg_offsets[-1])
-    yo = run_grouped_order(fmt, stk, size, n_exp, n, d, x[:m_total], seg_expert, seg_offsets, 8)
     yro, aro = oracle.grouped(x[:m_total], np.arange(m_total), seg_expert, seg_offsets, deq)
-    assert_parity(yo, yro, aro, f"grouped multi-row rows in order fmt={fmt} {n}x{d}")
+    for max_rows in (8, 16):
+        yo = run_grouped_order(fmt, stk, size, n_exp, n, d, x[:m_total], seg_expert, seg_offsets, max_rows)
+        assert_parity(yo, yro, aro, f"grouped multi-row rows in order fmt={fmt} {n}x{d} max_rows={max_rows}")
     qmm.qmm_set_kernel(qmm.QMM_KERNEL_GROUPED_MATMUL)
     y = run_grouped(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, 16)
     assert_parity(y, yr, ar, f"grouped matmul forced fmt={fmt} {n}x{d}")
@@ -1226,8 +1229,9 @@ def test_grouped_multi_row(fmt, n, d, kernel_auto_after):
 @pytest.mark.parametrize("fmt", [A, M])
 def test_grouped_multi_row_integer_exact(fmt, kernel_auto_after):
     """Integer weights and activations: the multi-row kernel (true and
-    understated bound) and the matmul kernel return the oracle's exact sums
-    rounded to bf16, bit for bit."""
+    understated bound), the split call (the 12-row segment to the matmul
+    kernel, the others to the multi-row kernel) and the matmul kernel alone
+    return the oracle's exact sums rounded to bf16, bit for bit."""
     say("grouped multi-row integer exact", fmt)
     n, d, n_exp, t = 200, 1536, 4, 30
     ws = [integer_affine(970 + e, n, d) if fmt == A else rand_mxfp4(970 + e, n, d, 127, 1) for e in range(n_exp)]
@@ -1243,7 +1247,8 @@ def test_grouped_multi_row_integer_exact(fmt, kernel_auto_after):
     yr, _ = oracle.grouped(x, row_index, seg_expert, seg_offsets, deq)
     assert np.all(np.abs(yr) < 2 ** 24)
     want = oracle.f64_to_bf16_bits(yr)
-    for k, max_rows in ((qmm.QMM_KERNEL_AUTO, 8), (qmm.QMM_KERNEL_AUTO, 5), (qmm.QMM_KERNEL_GROUPED_MATMUL, 12)):
+    for k, max_rows in ((qmm.QMM_KERNEL_AUTO, 8), (qmm.QMM_KERNEL_AUTO, 5), (qmm.QMM_KERNEL_AUTO, 12),
+                        (qmm.QMM_KERNEL_GROUPED_MATMUL, 12)):
         qmm.qmm_set_kernel(k)
         y = run_grouped(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, max_rows)
         assert np.array_equal(y, want), f"kernel setting {k}, max_rows {max_rows}"
