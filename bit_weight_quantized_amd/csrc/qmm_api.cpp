@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -414,10 +415,10 @@ qmm_status grouped(const char* name, bool swiglu, qmm_format f, const void* pack
     a.m_total = m_total;
     a.y = y;
     err = qmm::launch_gemv(a, stream);
-  } else if (!swiglu && kf != QMM_KERNEL_GROUPED_MATMUL &&
-             qmm::mrow_grouped_fits(f, max_seg_rows, n, d, t_x, l)) {
+  } else if (kf != QMM_KERNEL_GROUPED_MATMUL && max_seg_rows <= qmm::kMrowGroupedMaxT &&
+             qmm::mrow_grouped_fits(f, swiglu ? std::max(max_seg_rows, 2) : max_seg_rows, n, d, t_x, l)) {
     // a few rows per segment: the multi-row kernel reads each expert's
-    // weights once for all of them
+    // weights once for all of them (with the activation: also one row)
     qmm::MrowGroupedArgs a{};
     a.f = f;
     a.stack = static_cast<const uint8_t*>(packed_stack);
@@ -429,17 +430,18 @@ qmm_status grouped(const char* name, bool swiglu, qmm_format f, const void* pack
     a.grp.m_total = m_total;
     a.grp.t_x = int(t_x);
     a.n_seg = n_seg;
-    a.t = max_seg_rows;
+    a.t = swiglu ? std::max(max_seg_rows, 2) : max_seg_rows;
     a.n = int(n);
     a.d = int(d);
     a.x = x;
     a.y = y;
+    a.glu = swiglu;
     err = qmm::launch_mrow_grouped(a, stream);
   } else {
-    // longer segments: the matmul kernel; without the activation, the short
-    // ones among them (up to the multi-row kernel's bound, found on the
-    // device) go to the multi-row kernel first
-    const bool split = !swiglu && kf != QMM_KERNEL_GROUPED_MATMUL &&
+    // longer segments: the matmul kernel; the short ones among them (up to
+    // the multi-row kernel's bound, found on the device) go to the multi-row
+    // kernel first
+    const bool split = kf != QMM_KERNEL_GROUPED_MATMUL && max_seg_rows > qmm::kMrowGroupedMaxT &&
                        qmm::mrow_grouped_fits(f, qmm::kMrowGroupedMaxT, n, d, t_x, l);
     if (split) {
       // armed profiling events: the start with the first launch, the stop
@@ -463,6 +465,7 @@ qmm_status grouped(const char* name, bool swiglu, qmm_format f, const void* pack
       a.d = int(d);
       a.x = x;
       a.y = y;
+      a.glu = swiglu;
       err = qmm::launch_mrow_grouped(a, stream);
       g_profile = {nullptr, pe.stop};
       if (err) {

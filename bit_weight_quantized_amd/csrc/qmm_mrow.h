@@ -100,7 +100,8 @@ struct MrowGroupedArgs {
   MrowGroups grp;
   int n_seg, t, n, d;
   const uint16_t* x;
-  uint16_t* y;
+  uint16_t* y;                  // [m_total][n], or [m_total][n/2] with glu
+  bool glu;                     // y = silu(gate)·up of a gate_up stack (n even)
 };
 // the grouped launch's LDS: the dense one plus the chunk's x-row table
 inline size_t mrow_grouped_lds_bytes(int f, int64_t t, int64_t d) {

@@ -44,7 +44,7 @@ constexpr int kMrRing = 2;               // slabs in flight per lane
 // element offset of 16-byte piece c of row r (row stride rs elements)
 __device__ __forceinline__ int mr_at(int r, int rs, int c) { return r * rs + ((c ^ (r & 15)) << 3); }
 
-template <int FMT, int KQ, bool G2, bool GRP>
+template <int FMT, int KQ, bool G2, bool GRP, bool GLU = false>
 __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ meta,
                                                    uint32_t codes_bytes, uint32_t meta_bytes, int t,
@@ -53,6 +53,7 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
                                                    uint16_t* __restrict__ y, MrowGroups grp) {
   constexpr bool AFF = FMT == QMM_AFFINE4_G64;
   static_assert(!G2 || AFF, "two groups per MFMA: affine weights only");
+  static_assert(!GLU || (GRP && KQ == 1), "the activation: grouped, one wave per column block");
   constexpr int MP = AFF ? 2 : 1;   // 16-byte metadata pieces of one column per slab
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
   const Slabs L{n, d, FMT};
@@ -71,11 +72,16 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
   const int col_l = lane & 15, g = lane >> 4;
   // the workgroup's columns [c0, c1), at most 16·ncw: wave cw takes c0 + 16cw ..
   // c0 + 16cw + 15; a lane past c1 re-reads column c1 - 1 and stores nothing,
-  // a wave wholly past it loads nothing
-  const int c0 = blockIdx.x * cpw, c1 = min(c0 + cpw, n);
-  const int col = c0 + 16 * cw + col_l;
-  const int lcol = min(col, c1 - 1);
-  const bool active = 16 * cw < c1 - c0;
+  // a wave wholly past it loads nothing.  GLU (a gate_up stack: rows [0, n/2)
+  // the gate, [n/2, n) the up projection; eight waves): output columns
+  // [c0, c1) of n/2, at most 64, waves 0-3 on their gate rows and waves 4-7 on
+  // the same columns' up rows
+  const int nout = GLU ? n / 2 : n;
+  const int cwo = GLU ? cw & 3 : cw;   // the wave's column block among the outputs
+  const int c0 = blockIdx.x * cpw, c1 = min(c0 + cpw, nout);
+  const int col = c0 + 16 * cwo + col_l;
+  const int lcol = (GLU ? (cw >> 2) * nout : 0) + min(col, c1 - 1);   // packed row the lane reads
+  const bool active = 16 * cwo < c1 - c0;
   // grouped (routed experts): the workgroup's segment blockIdx.y, its rows
   // [r_begin, r_end) taken t at a time, its expert's weights; a segment with
   // no rows, or more than grp.max_rows when that is set, returns before any
@@ -310,7 +316,25 @@ __global__ __launch_bounds__(64 * kMrowMaxWaves) void mrow_kernel(const uint8_t*
         for (int k = 1; k < KQ; ++k) acc += red[((k - 1) * ncw + cw) * 64 + lane];
       }
     }
-    if (kq == 0 && col < c1 && (!G2 || g < 2)) {
+    if constexpr (GLU) {
+      // the up waves hand their sums to the gate waves of the same columns
+      // (through the partial-sum area, unused with one wave per column block),
+      // which store h = silu(gate)·up, rounded once
+      if (cw >= 4) red[(cw - 4) * 64 + lane] = acc;
+      __syncthreads();
+      if (cw < 4 && col < c1 && (!G2 || g < 2)) {
+        const f32x4_t u = red[cw * 64 + lane];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 4 * (G2 ? g & 1 : g) + r;
+          if (row < tr) {
+            const float gv = acc[r];
+            const float h = gv / (1.0f + expf(-gv)) * u[r];
+            y[int64_t(mb + row) * nout + col] = f32_to_bf16(src_rows[row] < 0 ? __builtin_nanf("") : h);
+          }
+        }
+      }
+    } else if (kq == 0 && col < c1 && (!G2 || g < 2)) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * (G2 ? g & 1 : g) + r;
@@ -609,8 +633,10 @@ int launch_mrow_grouped(const MrowGroupedArgs& a, void* stream) {
   if (!mrow_grouped_fits(a.f, a.t, a.n, a.d, a.grp.t_x, l) || a.n_seg < 1 || a.n_seg > 65535)
     return int(hipErrorInvalidValue);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  constexpr int ncw = kMrowMaxWaves, cpw = 16 * ncw;
-  const dim3 grid(unsigned((a.n + cpw - 1) / cpw), unsigned(a.n_seg)), block(unsigned(64 * ncw));
+  constexpr int ncw = kMrowMaxWaves;
+  const int cpw = a.glu ? 16 * ncw / 2 : 16 * ncw;   // output columns per workgroup
+  const int nout = a.glu ? a.n / 2 : a.n;
+  const dim3 grid(unsigned((nout + cpw - 1) / cpw), unsigned(a.n_seg)), block(unsigned(64 * ncw));
   const size_t lds = mrow_grouped_lds_bytes(a.f, a.t, a.d);
   const uint8_t* codes = a.stack + l.codes_offset;
   const uint8_t* meta = a.stack + l.meta_offset;
@@ -619,12 +645,13 @@ int launch_mrow_grouped(const MrowGroupedArgs& a, void* stream) {
     launch_kernel_lds(kern, grid, block, lds, s, codes, meta, cb, mb, a.t, a.n, a.d, cpw, ncw, a.x, a.y, a.grp);
   };
   constexpr int AF = QMM_AFFINE4_G64, MX = QMM_MXFP4_G32;
+  if (a.glu && (a.n % 2 != 0)) return int(hipErrorInvalidValue);
   if (a.f == AF && a.t <= kMrowG2MaxT)
-    go(mrow_kernel<AF, 1, true, true>);
+    a.glu ? go(mrow_kernel<AF, 1, true, true, true>) : go(mrow_kernel<AF, 1, true, true>);
   else if (a.f == AF)
-    go(mrow_kernel<AF, 1, false, true>);
+    a.glu ? go(mrow_kernel<AF, 1, false, true, true>) : go(mrow_kernel<AF, 1, false, true>);
   else
-    go(mrow_kernel<MX, 1, false, true>);
+    a.glu ? go(mrow_kernel<MX, 1, false, true, true>) : go(mrow_kernel<MX, 1, false, true>);
   return int(hipGetLastError());
 }
 

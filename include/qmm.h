@@ -266,8 +266,10 @@ qmm_status qmm_grouped_gemm(qmm_format f, const void* packed_stack, int64_t expe
  *   h   bf16[m_total][n/2]: h[r][j] = silu(g)·u, g = (x_r·Ŵ_eᵀ)[j],
  *       u = (x_r·Ŵ_eᵀ)[n/2 + j], silu(v) = v / (1 + e^-v); g and u are the
  *       fp32 accumulations (never rounded), h is rounded once to bf16.
- * n must be even (QMM_E_SHAPE).  Always the matmul kernel, whatever
- * max_seg_rows says.  Error rows are NaN as for qmm_grouped_gemm. */
+ * n must be even (QMM_E_SHAPE).  max_seg_rows selects the kernels as for
+ * qmm_grouped_gemm, except that a bound of 1 takes the multi-row kernel too
+ * (there is no GEMV form with the activation).  Error rows are NaN as for
+ * qmm_grouped_gemm. */
 qmm_status qmm_grouped_gemm_swiglu(qmm_format f, const void* packed_stack,
                                    int64_t expert_stride_bytes, int32_t n_experts, int64_t n,
                                    int64_t d, const qmm_bf16* x, int64_t t_x,

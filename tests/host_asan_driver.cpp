@@ -215,7 +215,15 @@ int main() {
   EXPECT(qmm_grouped_gemm(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 4, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "grouped_gemm");
   EXPECT(qmm_set_kernel(QMM_KERNEL_AUTO) == QMM_OK);
   EXPECT(qmm_grouped_gemm_swiglu(A, P(), blob, 2, 15, 64, B(), 4, I(), I(), I(), 1, 4, 4, B(), nullptr, 0, nullptr) == QMM_E_SHAPE);
-  EXPECT(qmm_grouped_gemm_swiglu(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 1, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "grouped_gemm");
+  // with the activation: the multi-row kernel up to 8 rows (one included),
+  // the split above, the matmul kernel when forced
+  EXPECT(qmm_grouped_gemm_swiglu(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 1, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow_grouped");
+  EXPECT(qmm_grouped_gemm_swiglu(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 8, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "mrow_grouped");
+  g_called = "none";
+  EXPECT(qmm_grouped_gemm_swiglu(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 9, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "split");
+  EXPECT(qmm_set_kernel(QMM_KERNEL_GROUPED_MATMUL) == QMM_OK);
+  EXPECT(qmm_grouped_gemm_swiglu(A, P(), blob, 2, 16, 64, B(), 4, I(), I(), I(), 1, 4, 4, B(), nullptr, 0, nullptr) == QMM_OK && g_called == "grouped_gemm");
+  EXPECT(qmm_set_kernel(QMM_KERNEL_AUTO) == QMM_OK);
 
   // router, combine, int8 GEMV, stream read
   EXPECT(qmm_route(nullptr, 4, 64, B(), 8, nullptr, 2, static_cast<float*>(P()), I(), I(), I(), I(), nullptr) == QMM_E_ARG);

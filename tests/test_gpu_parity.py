@@ -1283,25 +1283,31 @@ def assert_swiglu(h_bits, y_ref, a_ref, n_inter, what):
 
 
 @pytest.mark.parametrize("fmt,d", [(A, 256), (M, 256), (A, 576), (M, 1056)])
-def test_grouped_swiglu_small(fmt, d):
+def test_grouped_swiglu_small(fmt, d, kernel_auto_after):
     """gate_up stacks of 600 rows (300 gate, 300 up: the last 128-column tile
-    is partial), segments of 0 .. 130 rows, narrow last slabs."""
+    is partial), segments of 0 .. 130 rows, narrow last slabs; the true bound
+    splits the segments (up to 8 rows to the multi-row kernel, the rest to
+    the matmul kernel), bounds of 8 and 1 take the multi-row kernel alone (a
+    longer segment in passes of 8 or 2 rows), and the matmul kernel forced
+    takes them all."""
     say("grouped swiglu small", fmt, d)
     n, n_exp, t = 600, 5, 140
     ws = [synth.affine_weights(960 + e, n, d) if fmt == A else rand_mxfp4(960 + e, n, d) for e in range(n_exp)]
     stk, size = stack(fmt, ws)
     x = synth.activations(961, synth.S_X, t, d)
-    sizes = [0, 1, 17, 64, 65, 130]
-    seg_expert = [4, 0, 2, 1, 3, 2]
+    sizes = [0, 1, 17, 64, 5, 65, 130, 8]
+    seg_expert = [4, 0, 2, 1, 0, 3, 2, 4]
     seg_offsets = np.concatenate([[0], np.cumsum(sizes)])
     rng = np.random.default_rng(9)
     row_index = np.concatenate([np.sort(rng.choice(t, s, replace=False)) for s in sizes]).astype(np.int32)
     deq = (lambda e: oracle.dequant_affine(ws[e].codes, ws[e].scale, ws[e].bias)) if fmt == A else \
           (lambda e: oracle.dequant_mxfp4(ws[e].codes, ws[e].e8m0))
     yr, ar = oracle.grouped(x, row_index, seg_expert, seg_offsets, deq)
-    for max_rows in (max(sizes), 1):      # one kernel whatever the bound says
+    for k, max_rows in ((qmm.QMM_KERNEL_AUTO, max(sizes)), (qmm.QMM_KERNEL_AUTO, 8), (qmm.QMM_KERNEL_AUTO, 1),
+                        (qmm.QMM_KERNEL_GROUPED_MATMUL, max(sizes))):
+        qmm.qmm_set_kernel(k)
         h = run_grouped_swiglu(fmt, stk, size, n_exp, n, d, x, seg_expert, seg_offsets, row_index, max_rows)
-        assert_swiglu(h, yr, ar, n // 2, f"swiglu fmt={fmt} d={d} max_rows={max_rows}")
+        assert_swiglu(h, yr, ar, n // 2, f"swiglu fmt={fmt} d={d} kernel={k} max_rows={max_rows}")
 
 
 def test_grouped_rows_in_order():
