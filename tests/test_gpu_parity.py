@@ -1415,6 +1415,25 @@ def test_grouped_invalid_entries_give_nan():
         yf = oracle.bf16_to_f64(y)
         assert np.all(np.isnan(yf[2:4])) and np.all(np.isnan(yf[5]))
         assert np.all(np.isfinite(yf[0:2])) and np.all(np.isfinite(yf[4]))
+    # a bound of 16 splits the segments (10 and 9 rows to the matmul kernel,
+    # 3 and 2 to the multi-row kernel), with and without the activation:
+    # each kernel marks its own segments' bad rows
+    seg_expert = [0, 7, 1, -1]
+    seg_offsets = [0, 10, 19, 22, 24]
+    row_index = [0, 1, 2, 3, 99, 5, 6, 7, 1, 2] + [0] * 9 + [3, 100, 5] + [1, 2]
+    bad = np.zeros(24, bool)
+    bad[[4, 20, 22, 23]] = True
+    bad[10:19] = True
+    # (outputs start at zero, so a NaN row is one a kernel wrote)
+    for glu in (False, True):
+        call = qmm.qmm_grouped_gemm_swiglu if glu else qmm.qmm_grouped_gemm
+        y = torch.zeros(24, n // 2 if glu else n, dtype=torch.int16, device="cuda")
+        call(M, stk, size, n_exp, n, d, dev(x), t, dev(np.asarray(row_index, np.int32)),
+             dev(np.asarray(seg_expert, np.int32)), dev(np.asarray(seg_offsets, np.int32)), 4, 24, 16, y)
+        torch.cuda.synchronize()
+        yf = oracle.bf16_to_f64(host_u16(y))
+        assert np.all(np.isnan(yf[bad])) and np.all(np.isfinite(yf[~bad])), f"glu={glu}"
+        assert np.count_nonzero(yf[~bad]) > 0.9 * yf[~bad].size, f"glu={glu}: good rows written"
 
 
 def make_expert_stack(which, n_exp):
