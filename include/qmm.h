@@ -220,9 +220,11 @@ qmm_status qmm_gemm(qmm_format f, const void* packed, int64_t t, int64_t n, int6
 qmm_status qmm_gemm_noalloc(qmm_format f, const void* packed, int64_t t, int64_t n, int64_t d,
                             const qmm_bf16* x, qmm_bf16* y, void* stream);
 
-/* Routed-expert grouped matmul (all experts in one launch): the per-expert
- * GEMM of the MoE block of "Colibri Kimi K3 Metal 后端实现全解析", Phase 6, whose
- * experts all run in one submission so the launch cost is paid once.
+/* Routed-expert grouped matmul (all experts in one launch, or two when the
+ * row bound splits the segments between two kernels, see max_seg_rows): the
+ * per-expert GEMM of the MoE block of "Colibri Kimi K3 Metal 后端实现全解析",
+ * Phase 6, whose experts all run in one submission so the launch cost is
+ * paid once per kernel, not per expert.
  *   packed_stack        n_experts blobs of qmm_packed_bytes(f, n, d) bytes,
  *                       blob e at packed_stack + e·expert_stride_bytes
  *                       (stride a multiple of 256, >= the blob size)
